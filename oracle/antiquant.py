@@ -1,0 +1,92 @@
+"""Literal fp64 oracle of the weight-anti-quant matmul.
+
+Test infrastructure only (see the package docstring).
+
+    output = x1 @ ((x2 + antiquantOffset) * antiquantScale) + bias + x3
+
+[guide] "计算公式" (formula) and [npu_mm] "计算公式"; the AllReduce is the identity at
+one rank.  Parameter granularity follows [guide] "关键属性的源码级说明" (attribute
+notes: per-tensor (1), per-channel (n) or (1,n), per-group (ceil(k/g), n)) and
+"约束说明 / 形状与范围约束" (shape constraints).  Per-group parameters are expanded
+along k by repeating each row g times, as the guide's description of its golden
+reference script states ("仓库中的验证与配套资源 / Golden 验证脚本").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .storage import decode, unpack_int4
+
+
+def resolve_mode(scale_shape, group_size: int, n: int) -> str:
+    """Quantisation mode from the scale's shape and the group size.
+
+    [guide] attribute notes: group size 0 means "not per-group"; a non-zero group size
+    selects per-group.  Otherwise a one-element scale is per-tensor and an (n) / (1, n)
+    scale is per-channel."""
+    numel = int(np.prod(scale_shape))
+    if group_size != 0:
+        return "group"
+    if numel == 1 and tuple(scale_shape) == (1,):
+        return "tensor"
+    if tuple(scale_shape) in ((n,), (1, n)):
+        return "channel"
+    raise ValueError(f"scale shape {scale_shape} fits no mode for n={n}, g={group_size}")
+
+
+def expand_params(p: np.ndarray, mode: str, k: int, n: int, group_size: int) -> np.ndarray:
+    """Broadcast a decoded scale or offset to a full (k, n) matrix.
+
+    per-tensor: every entry is the scalar; per-channel: the row vector repeated down k;
+    per-group: row i of the result is parameter row floor(i / g), i.e. each parameter
+    row repeated g times along k and cut to k rows (a partial last group keeps the last
+    parameter row)."""
+    if mode == "tensor":
+        return np.full((k, n), p.reshape(-1)[0], dtype=np.float64)
+    if mode == "channel":
+        return np.broadcast_to(p.reshape(1, n), (k, n)).astype(np.float64)
+    if mode == "group":
+        groups = -(-k // group_size)
+        assert p.shape == (groups, n), (p.shape, groups, n)
+        return np.repeat(p, group_size, axis=0)[:k]
+    raise ValueError(mode)
+
+
+def ref_antiquant(x1, x2, scale, offset=None, bias=None, x3=None, group_size: int = 0, *,
+                  act: str, weight: str, n: int | None = None) -> np.ndarray:
+    """fp64 result of the anti-quant matmul, unrounded, in the output's shape.
+
+    Inputs are stored arrays: x1/scale/offset/bias/x3 in ``act`` ("fp16" -> float16,
+    "bf16" -> uint16 bit patterns); x2 int8 (k, n) or packed int4 uint8 (k, n/2).
+    None means an absent optional input: offset 0, bias 0, x3 0 ([guide] shape
+    constraints: those inputs may be empty)."""
+    x1f = decode(x1, act)
+    lead = x1f.shape[:-1]
+    k = x1f.shape[-1]
+    m = int(np.prod(lead))
+    a = x1f.reshape(m, k)
+    if weight == "int4":
+        codes = unpack_int4(x2).astype(np.float64)
+    else:
+        assert x2.dtype == np.int8
+        codes = x2.astype(np.float64)
+    assert codes.shape[0] == k
+    n_ = codes.shape[1]
+    if n is not None:
+        assert n == n_
+    n = n_
+
+    y = np.zeros((m, n), dtype=np.float64)
+    if k > 0:
+        mode = resolve_mode(scale.shape, group_size, n)
+        s_full = expand_params(decode(scale, act), mode, k, n, group_size)
+        o_full = (np.zeros((k, n)) if offset is None
+                  else expand_params(decode(offset, act), mode, k, n, group_size))
+        w = (codes + o_full) * s_full          # add first, then multiply
+        y = a @ w
+    # k == 0: the product is empty and the output is bias + x3 ([guide] "空 tensor 支持度").
+    if bias is not None:
+        y = y + decode(bias, act).reshape(1, n)
+    if x3 is not None:
+        y = y + decode(x3, act).reshape(m, n)
+    return y.reshape(lead + (n,))
