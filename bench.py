@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-anti-quant matmul (and its W8A8 sibling) on one MI355X.
+
+A step is one call of the library on one batch of resident synthetic inputs: for the
+anti-quant workloads x1 @ ((x2 + offset) * scale) + bias + x3, for the W8A8 workload
+dequant_scale * pertoken_scale * (x1 @ x2 + bias) + x3.  Inputs are drawn by the seeded
+generators in ``workloads`` and copied to HBM before timing.  Several input sets are
+rotated so that the footprint of consecutive steps exceeds the 256 MB Infinity Cache: the
+timed steps read their operands from HBM, not from a warm cache.
+
+Output: one JSON line (the headline workload), with the roofline of the dominant kernel
+(timed with HIP events on the stream the library launches on) and the CPU oracle's rate
+on the host as a baseline.  ``--all`` prints one line per workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "TFLOP/s and HBM GB/s (% of MI355X peak) for anti-quant GEMM+bias+x3"
+HEADLINE = "perchannel_bf16_int8_4096x4096x4096"
+# MI355X published peaks: dense MFMA bf16/fp16 2.5 PFLOP/s, int8 5.0 POP/s; HBM3E 8 TB/s.
+PEAK = {"bf16": 2500.0, "fp16": 2500.0, "int8": 5000.0}   # TFLOP/s (TOP/s)
+PEAK_HBM = 8000.0                                          # GB/s
+# the kernel that dominates each workload's step, and what bounds it
+DOMINANT = {
+    "tiny_pertensor_fp16_int8_16x256x256": ("aq_smallm_kernel", "hbm"),
+    "perchannel_bf16_int8_4096x4096x4096": ("aq_gemm_kernel", "mfma"),
+    "pergroup128_bf16_int4_4x2048x8192x2048": ("aq_gemm_kernel", "mfma"),
+    "smallm_pergroup64_fp16_int8_32x8192x8192": ("aq_smallm_kernel", "hbm"),
+    "w8a8_bf16_8192x4096x8192": ("qm_gemm_kernel", "mfma"),
+}
+CACHE_BYTES = 256 << 20
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_quantized_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case) -> int:
+    total = sum(int(a.nbytes) for a in case.arrays().values())
+    out_elems = int(np.prod(case.out_shape))
+    return total + 2 * out_elems          # fp16 / bf16 output written once
+
+
+def to_dev(a, kind, torch, dev):
+    if a is None:
+        return None
+    if kind == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def make_runner(case, torch, dev, sets):
+    """Device-resident input sets and a closure that runs one step on set i."""
+    import weight_quantized_gemm_amd as W
+    if isinstance(case, workloads.AntiquantCase):
+        act = case.act
+        bufs = []
+        for s in range(sets):
+            # extra sets are copies of the same values at other addresses
+            b = dict(x1=to_dev(case.x1, act, torch, dev), x2=to_dev(case.x2, "raw", torch, dev),
+                     scale=to_dev(case.scale, act, torch, dev), offset=to_dev(case.offset, act, torch, dev),
+                     bias=to_dev(case.bias, act, torch, dev), x3=to_dev(case.x3, act, torch, dev))
+            b["out"] = torch.empty(case.out_shape, dtype=b["x1"].dtype, device=dev)
+            bufs.append(b)
+        int4 = case.weight == "int4"
+        b0 = bufs[0]
+        ws_bytes = W.antiquant_workspace_size(b0["x1"], b0["x2"], b0["scale"], b0["offset"], b0["bias"],
+                                              b0["x3"], case.group_size, x2_int4=int4, out=b0["out"])
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            b = bufs[i % sets]
+            W.antiquant_matmul(b["x1"], b["x2"], b["scale"], b["offset"], b["bias"], b["x3"],
+                               case.group_size, x2_int4=int4, out=b["out"], workspace=ws)
+        return step, bufs
+    bufs = []
+    odt = torch.bfloat16 if case.out == "bf16" else torch.float16
+    for s in range(sets):
+        b = dict(x1=to_dev(case.x1, "raw", torch, dev), x2=to_dev(case.x2, "raw", torch, dev),
+                 dq=to_dev(case.dequant_scale, case.dequant_dtype, torch, dev),
+                 pt=to_dev(case.pertoken_scale, "fp32", torch, dev), bias=to_dev(case.bias, "raw", torch, dev),
+                 x3=to_dev(case.x3, case.out, torch, dev))
+        b["out"] = torch.empty(case.out_shape, dtype=odt, device=dev)
+        bufs.append(b)
+
+    def step(i):
+        b = bufs[i % sets]
+        W.quant_matmul(b["x1"], b["x2"], b["dq"], b["pt"], b["bias"], b["x3"], out=b["out"])
+    return step, bufs
+
+
+def cpu_baseline(case, name):
+    """The oracle as it stands, on the host cores, on the whole workload once."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the visible cores
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    if isinstance(case, workloads.AntiquantCase):
+        oracle.ref_antiquant(case.x1, case.x2, case.scale, case.offset, case.bias, case.x3,
+                             case.group_size, act=case.act, weight=case.weight)
+    else:
+        oracle.ref_w8a8(case.x1, case.x2, case.dequant_scale, case.pertoken_scale, case.bias, case.x3,
+                        dequant_dtype=case.dequant_dtype, out=case.out)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * case.m * case.k * case.n
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"whole workload once ({dt:.2f} s), fp64 NumPy/BLAS",
+            "seconds": round(dt, 3)}
+
+
+def traffic_for(kernel, name):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(name)
+    if not rec or rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def bench_one(name, args, torch, dev):
+    case = workloads.make_workload(name)
+    abytes = algorithmic_bytes(case)
+    sets = max(1, min(8, -(-2 * CACHE_BYTES // max(abytes, 1))))
+    step, bufs = make_runner(case, torch, dev, sets)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(args.warmup + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in evs)          # ms, per launch
+    ev_total = sum(per)
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 2.0 * case.m * case.k * case.n
+    kernel, bound = DOMINANT[name]
+    dtype = "int8" if isinstance(case, workloads.W8A8Case) else case.act
+    avg_launch_s = (ev_total / len(per)) / 1e3
+    if bound == "mfma":
+        achieved = flops / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[dtype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK[dtype], 4)}
+    else:
+        achieved = abytes / avg_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM, 4)}
+    roof["traffic"] = traffic_for(kernel, name)
+    roof["kernel"] = kernel
+    roof["launch_us_median"] = round(per[len(per) // 2] * 1e3, 2)
+    roof["launch_us_avg"] = round(avg_launch_s * 1e6, 2)
+    value = flops / (ms_per_step / 1e3) / 1e12
+    spec = workloads.WORKLOADS[name]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if dtype == "int8" else dtype,
+        "data": "synthetic (seeded generators; inputs resident in HBM, rotated over "
+                f"{sets} sets to defeat the Infinity Cache)",
+        "config": {"workload": name, "m": case.m, "k": case.k, "n": case.n,
+                   "x1_shape": list(case.x1.shape), "seed": spec["seed"],
+                   "algorithmic_bytes": abytes, "flops": flops,
+                   "hbm_gbps": round(abytes / (ms_per_step / 1e3) / 1e9, 1),
+                   "hbm_frac": round(abytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM, 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu_baseline(case, name) if args.cpu else None,
+    }
+    del bufs
+    torch.cuda.empty_cache()
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="one line per workload")
+    ap.add_argument("--no-cpu", dest="cpu", action="store_false", help="skip the CPU oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is "
+              "not part of this library", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import weight_quantized_gemm_amd as W
+    W.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    names = sorted(workloads.WORKLOADS) if args.all else [args.workload]
+    for name in names:
+        print(json.dumps(bench_one(name, args, torch, dev)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

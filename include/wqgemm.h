@@ -1,0 +1,156 @@
+/*
+ * wqgemm -- weight-anti-quant matmul and its W8A8 sibling for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; no framework types cross this boundary.
+ *
+ * Operations (one rank's local result; the pages' AllReduce over ranks is the identity at
+ * world size 1 and is not part of this library):
+ *
+ *   anti-quant:  output = x1 @ ((x2 + antiquant_offset) * antiquant_scale) + bias + x3
+ *     -- "CANN ops-transformer ... aclnnWeightQuantMatmulAllReduce 完全指南" (discosf.com),
+ *        section 计算公式 (formula); torch_npu.npu_mm_all_reduce_base, section 计算公式.
+ *
+ *   W8A8:        output = dequant_scale * pertoken_scale * (x1_int8 @ x2_int8 + bias_int32) + x3
+ *     -- "aclnnQuantMatmulAllReduceV2" (hiascend.com), section Function, formula case 2
+ *        (case 1 is case 2 with no pertoken scale).
+ *
+ * Calling convention (after the pages' two-phase interface, "两段式接口与函数原型" of the
+ * guide and "Function Prototype" of aclnnQuantMatmulAllReduceV2): first ask for the workspace
+ * size, allocate it (device memory, owned by the caller), then launch.  Unlike the pages,
+ * there is no executor object: both calls are stateless and may be repeated with the same
+ * arguments any number of times.
+ *
+ * Ownership: the caller owns every buffer, including the workspace.  The library allocates
+ * and frees no device memory on these calls.  Launches are asynchronous on the caller's
+ * stream and return once enqueued; the caller synchronises.  `output` must not alias an
+ * input.  Calls that share a workspace on overlapping streams race.
+ *
+ * Errors: status codes only (nothing is printed, thrown or aborted).  Checks run in the
+ * pages' order: null pointers, then dtypes, then attributes, then shapes (guide section
+ * 返回值与错误码 (return codes)).  Numeric codes for the two parameter errors are the pages'
+ * (aclnnQuantMatmulAllReduceV2, "Return Value" table).
+ */
+#ifndef WQGEMM_H
+#define WQGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  WQ_I4 is a packed signed 4-bit type: see wq_tensor. */
+typedef enum wq_dtype {
+  WQ_F16 = 1,
+  WQ_BF16 = 2,
+  WQ_F32 = 3,
+  WQ_I8 = 4,
+  WQ_I4 = 5,
+  WQ_I32 = 6
+} wq_dtype;
+
+/*
+ * Tensor descriptor (the role of the pages' aclTensor).
+ *   data    device address of the first element (for an empty tensor it may be NULL).
+ *   dtype   a wq_dtype.
+ *   ndim    1, 2 or 3.
+ *   shape   logical shape; entries past ndim are ignored.
+ *   stride  element strides of the logical shape.  This version accepts row-major
+ *           contiguous tensors only (stride[ndim-1] == 1, stride[i] == stride[i+1]*shape[i+1]);
+ *           anything else is WQ_ERR_PARAM_INVALID.
+ * WQ_I4 weights: logical shape (k, n); storage is k rows of n/2 bytes; each byte holds two
+ * signed two's-complement nibbles along n, bits 0-3 = even column, bits 4-7 = odd column.
+ * Strides of a WQ_I4 tensor are given in logical elements (row stride n).
+ * An optional input is absent when its descriptor pointer is NULL.
+ */
+typedef struct wq_tensor {
+  void* data;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[3];
+  int64_t stride[3];
+} wq_tensor;
+
+#define WQ_OK 0
+#define WQ_ERR_PARAM_NULLPTR 161001 /* a required input/output or its data pointer is NULL */
+#define WQ_ERR_PARAM_INVALID 161002 /* dtype, attribute, shape, layout or workspace rule broken */
+#define WQ_ERR_RUNTIME 561001       /* a HIP runtime or kernel-launch failure (library's own code) */
+
+/*
+ * Workspace size of wq_antiquant_matmul for these arguments, written to *workspace_size.
+ *
+ * Arguments (guide, "aclnnWeightQuantMatmulAllReduceGetWorkspaceSize 参数详解" and
+ * "约束说明 / 形状与范围约束" (shape constraints)):
+ *   x1               required; WQ_F16 or WQ_BF16; (m, k) or (b, s, k); m = b*s in [1, 2^31-1].
+ *   x2               required; WQ_I8 or WQ_I4; (k, n); k in [0, 65535], n in [1, 65535].
+ *                    Alignment (guide, 950 format/alignment rules): int8 needs k and n
+ *                    multiples of 32, int4 multiples of 64 (k = 0 is allowed).
+ *   bias             optional; x1's dtype; (n).
+ *   antiquant_scale  required; x1's dtype.  Per-tensor (1); per-channel (n) or (1, n);
+ *                    per-group (ceil(k / g), n) (guide, attribute notes on
+ *                    IsAntiquantScaleShapeValid).
+ *   antiquant_offset optional; x1's dtype; the scale's shape.  Absent means 0.
+ *   x3               optional; x1's dtype; the output's shape.
+ *   antiquant_group_size  0 = not per-group; otherwise a multiple of 32 in
+ *                    [32, min(k - 1, INT32_MAX)].  Not checked when k == 0.
+ *   output           required; x1's dtype; (m, n) or (b, s, n) following x1.
+ * k == 0 is the empty-K case: output = bias + x3 (absent terms are 0)
+ * (guide, "空 tensor 支持度" (empty tensors)); m == 0 or n == 0 is WQ_ERR_PARAM_INVALID.
+ * Returns WQ_OK, WQ_ERR_PARAM_NULLPTR or WQ_ERR_PARAM_INVALID.  Touches no device.
+ */
+int wq_antiquant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor* x2,
+                                           const wq_tensor* bias, const wq_tensor* antiquant_scale,
+                                           const wq_tensor* antiquant_offset, const wq_tensor* x3,
+                                           int64_t antiquant_group_size, const wq_tensor* output,
+                                           uint64_t* workspace_size);
+
+/*
+ * Enqueue the anti-quant matmul on `stream` (a hipStream_t; NULL = the null stream).
+ * Same arguments as above, plus the caller's device workspace of workspace_size bytes
+ * (at least what the size query returned; NULL allowed when that is 0).
+ * Repeats every check of the size query; a workspace smaller than required is
+ * WQ_ERR_PARAM_INVALID.  Returns WQ_ERR_RUNTIME if a launch fails.
+ */
+int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
+                        const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,
+                        const wq_tensor* x3, int64_t antiquant_group_size, const wq_tensor* output,
+                        void* workspace, uint64_t workspace_size, void* stream);
+
+/*
+ * Workspace size of wq_quant_matmul (the W8A8 sibling).
+ * Arguments (aclnnQuantMatmulAllReduceV2, "Parameters" table and "Constraints"):
+ *   x1              required; WQ_I8; (m, k) or (b, s, k); m in [1, 2^31-1]; k in [1, 65535].
+ *   x2              required; WQ_I8; (k, n); n in [1, 65535]; k and n multiples of 32.
+ *   bias            optional; WQ_I32; (n).  Added to the int32 accumulator before scaling.
+ *   x3              optional; the output's dtype and shape.
+ *   dequant_scale   required; WQ_F32 or WQ_BF16; (1), (n) or (1, n).
+ *   pertoken_scale  optional; WQ_F32; (m) (m = b*s for 3-D x1).  Absent means 1.
+ *   output          required; WQ_F16 or WQ_BF16; (m, n) or (b, s, n) following x1.
+ *   acc_out         optional; WQ_I32; (m, n): receives x1 @ x2 + bias as int32 (two's
+ *                   complement wrap on overflow), for exactness checks.
+ * The pages' INT64/UINT64 packed dequant scale is not supported (WQ_ERR_PARAM_INVALID).
+ */
+int wq_quant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor* x2,
+                                       const wq_tensor* bias, const wq_tensor* x3,
+                                       const wq_tensor* dequant_scale,
+                                       const wq_tensor* pertoken_scale, const wq_tensor* output,
+                                       const wq_tensor* acc_out, uint64_t* workspace_size);
+
+/* Enqueue the W8A8 matmul on `stream`.  Same conventions as wq_antiquant_matmul. */
+int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
+                    const wq_tensor* x3, const wq_tensor* dequant_scale,
+                    const wq_tensor* pertoken_scale, const wq_tensor* output,
+                    const wq_tensor* acc_out, void* workspace, uint64_t workspace_size,
+                    void* stream);
+
+/* Static text for a status code. */
+const char* wq_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int wq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQGEMM_H */

@@ -1,0 +1,180 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Tolerances: |gpu - ref| <= 2e-3 * max(1, |ref|) for fp16 outputs and 1e-2 * max(1, |ref|)
+for bf16 outputs; the W8A8 int32 accumulator bit-exact.  Small cases are compared on every
+element and span several tiles with ragged edges; the full-size workloads are compared on
+sampled rows (every column of each sampled row), run in the same configuration the
+benchmark times.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import (ref_antiquant, ref_w8a8, run_antiquant, run_w8a8, sampled_rows, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(name):
+    print(f"[gpu-case] {name}", flush=True)
+    sys.stdout.flush()
+
+
+def check_aq(case, rows=None):
+    _announce(case.name)
+    y = run_antiquant(case)
+    got = to_f64(y).reshape(-1, case.n)
+    if rows is not None:
+        got = got[rows]
+    ref = ref_antiquant(case, rows).reshape(got.shape)
+    r = oracle.compare(got, ref, case.act)
+    assert r["ok"], (case.name, r)
+    return r
+
+
+# (name, act, weight, x1 shape, n, mode, group size, extra kwargs)
+AQ_CASES = [
+    ("c1_tiny_pertensor", None),
+    ("perchannel_bf16_i8_ragged", dict(act="bf16", weight="int8", x1_shape=(600, 288), n=544, mode="channel")),
+    ("perchannel_bf16_i8_1xn_nooff", dict(act="bf16", weight="int8", x1_shape=(300, 256), n=256, mode="channel",
+                                          channel_2d=True, with_offset=False, with_bias=False, with_x3=False)),
+    ("perchannel_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(257, 320), n=288, mode="channel")),
+    ("pertensor_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(260, 256), n=320, mode="tensor")),
+    ("perchannel_fp16_i4", dict(act="fp16", weight="int4", x1_shape=(130, 384), n=192, mode="channel")),
+    ("pergroup128_bf16_i4_3d", dict(act="bf16", weight="int4", x1_shape=(2, 300, 512), n=320, mode="group",
+                                    group_size=128, scale_dist=("uniform", 0.01, 0.05),
+                                    offset_dist=("uniform", -1, 1), with_bias=False)),
+    ("pergroup64_fp16_i8_m33", dict(act="fp16", weight="int8", x1_shape=(33, 576), n=256, mode="group",
+                                    group_size=64, offset_dist=("uniform", -4, 4))),
+    ("pergroup96_bf16_i8_partial", dict(act="bf16", weight="int8", x1_shape=(280, 320), n=160, mode="group",
+                                        group_size=96)),
+    ("pergroup32_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(100, 256), n=128, mode="group",
+                                group_size=32)),
+    ("pergroup224_bf16_i8_gkm1", dict(act="bf16", weight="int8", x1_shape=(70, 256), n=96, mode="group",
+                                      group_size=224)),
+    ("pergroup64_bf16_i8_k96", dict(act="bf16", weight="int8", x1_shape=(40, 96), n=64, mode="group",
+                                    group_size=64)),
+    ("perchannel_bf16_i8_longk", dict(act="bf16", weight="int8", x1_shape=(256, 4096), n=256, mode="channel")),
+    ("pergroup512_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(64, 2048), n=128, mode="group",
+                                 group_size=512)),
+    # small-m (split-k) path
+    ("smallm_pergroup64_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(32, 1024), n=384, mode="group",
+                                       group_size=64, offset_dist=("uniform", -4, 4), with_x3=False)),
+    ("smallm_m1_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(1, 512), n=256, mode="channel")),
+    ("smallm_m3_pergroup128_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(3, 1024), n=256, mode="group",
+                                           group_size=128)),
+    ("smallm_m17_pertensor_fp16_i4", dict(act="fp16", weight="int4", x1_shape=(17, 320), n=128, mode="tensor")),
+    ("smallm_m5_pergroup96_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(5, 544), n=160, mode="group",
+                                          group_size=96)),
+    ("smallm_m8_pergroup64_bf16_i8_k96", dict(act="bf16", weight="int8", x1_shape=(8, 96), n=64, mode="group",
+                                              group_size=64)),
+    ("smallm_3d_perchannel_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(2, 4, 2048), n=640,
+                                          mode="channel")),
+]
+
+
+@pytest.mark.parametrize("name,spec", AQ_CASES, ids=[c[0] for c in AQ_CASES])
+def test_antiquant_parity(name, spec):
+    if spec is None:
+        case = workloads.make_workload("tiny_pertensor_fp16_int8_16x256x256")
+    else:
+        case = workloads.make_antiquant(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec)
+    check_aq(case)
+
+
+def test_page_sample_antiquant_all_ones():
+    import torch
+    import weight_quantized_gemm_amd as W
+    _announce("page_sample_antiquant")
+    d = "cuda:0"
+    h = lambda *s: torch.ones(*s, dtype=torch.float16, device=d)
+    y = W.antiquant_matmul(h(32, 64), torch.ones(64, 128, dtype=torch.int8, device=d), h(128),
+                           h(128), h(128), h(32, 128))
+    assert torch.all(y.float() == 130)
+
+
+@pytest.mark.parametrize("act", ["fp16", "bf16"])
+def test_empty_k(act):
+    import torch
+    import weight_quantized_gemm_amd as W
+    _announce(f"empty_k_{act}")
+    case = workloads.make_antiquant(seed=7, act=act, weight="int8", x1_shape=(32, 0), n=128, mode="channel")
+    y = run_antiquant(case)
+    ref = ref_antiquant(case)
+    assert oracle.compare(to_f64(y), ref, act)["ok"]
+    case0 = workloads.make_antiquant(seed=8, act=act, weight="int8", x1_shape=(32, 0), n=128, mode="channel",
+                                     with_bias=False, with_x3=False)
+    assert np.all(to_f64(run_antiquant(case0)) == 0)
+
+
+def test_determinism():
+    _announce("determinism")
+    for name, spec in [("det_group", dict(act="bf16", weight="int4", x1_shape=(300, 512), n=320, mode="group",
+                                          group_size=128)),
+                       ("det_smallm", dict(act="fp16", weight="int8", x1_shape=(32, 2048), n=256, mode="group",
+                                           group_size=64))]:
+        case = workloads.make_antiquant(seed=5, name=name, **spec)
+        a = run_antiquant(case).cpu()
+        b = run_antiquant(case).cpu()
+        assert bytes(a.view(-1).view(__import__("torch").int16).numpy()) == \
+            bytes(b.view(-1).view(__import__("torch").int16).numpy())
+
+
+W8A8_CASES = [
+    ("w8a8_ragged_bf16", dict(out="bf16", x1_shape=(600, 288), n=544)),
+    ("w8a8_fp16_tensor_nopt", dict(out="fp16", x1_shape=(300, 256), n=256, dequant="tensor",
+                                   with_pertoken=False, with_bias=False, with_x3=False)),
+    ("w8a8_bf16dq", dict(out="bf16", x1_shape=(257, 320), n=288, dequant_dtype="bf16")),
+    ("w8a8_m1", dict(out="bf16", x1_shape=(1, 128), n=64)),
+    ("w8a8_3d_m3", dict(out="fp16", x1_shape=(3, 1, 256), n=96)),
+]
+
+
+@pytest.mark.parametrize("name,spec", W8A8_CASES, ids=[c[0] for c in W8A8_CASES])
+def test_w8a8_parity(name, spec):
+    _announce(name)
+    case = workloads.make_w8a8(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec)
+    y, acc = run_w8a8(case)
+    ref, racc = ref_w8a8(case)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), racc)
+    r = oracle.compare(to_f64(y).reshape(ref.shape), ref, case.out)
+    assert r["ok"], r
+
+
+def test_page_sample_w8a8_all_ones():
+    import torch
+    import weight_quantized_gemm_amd as W
+    _announce("page_sample_w8a8")
+    d = "cuda:0"
+    acc = torch.empty(32, 128, dtype=torch.int32, device=d)
+    y = W.quant_matmul(torch.ones(32, 64, dtype=torch.int8, device=d),
+                       torch.ones(64, 128, dtype=torch.int8, device=d),
+                       torch.ones(128, dtype=torch.float32, device=d),
+                       torch.ones(32, dtype=torch.float32, device=d),
+                       torch.ones(128, dtype=torch.int32, device=d),
+                       torch.ones(32, 128, dtype=torch.float16, device=d), acc_out=acc)
+    assert torch.all(acc == 65) and torch.all(y.float() == 66)
+
+
+# ---------------------------------------------------------------- full-size workloads
+FULL = [n for n, s in workloads.WORKLOADS.items()]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    _announce(f"full:{name}")
+    case = workloads.make_workload(name)
+    rows = sampled_rows(case.m)
+    if isinstance(case, workloads.AntiquantCase):
+        check_aq(case, rows)
+    else:
+        y, acc = run_w8a8(case)
+        ref, racc = ref_w8a8(case, rows)
+        assert np.array_equal(acc[rows].cpu().numpy().astype(np.int64), racc)
+        got = to_f64(y).reshape(-1, case.n)[rows]
+        r = oracle.compare(got, ref.reshape(got.shape), case.out)
+        assert r["ok"], r

@@ -1,0 +1,195 @@
+"""Argument validation through the C ABI's size queries (CPU; no device is touched).
+
+Named rows follow the unit-test CSV rows the aclnnWeightQuantMatmulAllReduce guide lists
+(section 单元测试); the other cases follow the rules of its constraint sections and of the
+aclnnQuantMatmulAllReduceV2 page (Parameters, Constraints, Return Value).  Data pointers
+are fake non-null addresses: the size query reads only the descriptors.
+"""
+import ctypes
+import json
+import os
+
+import pytest
+
+import weight_quantized_gemm_amd as W
+from weight_quantized_gemm_amd import make_desc
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+FAKE = 0x10000
+DT = {"fp16": W.WQ_F16, "bf16": W.WQ_BF16, "int8": W.WQ_I8, "int4": W.WQ_I4}
+OK, NULLPTR, INVALID = W.WQ_OK, W.WQ_ERR_PARAM_NULLPTR, W.WQ_ERR_PARAM_INVALID
+
+
+_next = [FAKE + 0x1000000]
+
+
+def D(shape, dt, ptr=None, strides=None):
+    """Descriptor with a fresh fake address unless one is given (0 = null data)."""
+    if ptr is None:
+        _next[0] += 0x100000
+        ptr = _next[0]
+    return make_desc(shape, dt, ptr, strides)
+
+
+def aq(wqlib, x1, x2, scale, out, offset=None, bias=None, x3=None, g=0, ws=True):
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    size = ctypes.c_uint64(0)
+    return wqlib.wq_antiquant_matmul_get_workspace_size(
+        r(x1), r(x2), r(bias), r(scale), r(offset), r(x3), g, r(out),
+        ctypes.byref(size) if ws else None)
+
+
+def base(act="fp16", w="int8", m=32, k=64, n=128, scale=None, g=0):
+    a, wd = DT[act], DT[w]
+    x1 = D([m, k], a, FAKE + 0x100000)
+    x2 = D([k, n], wd, FAKE + 0x200000)
+    sc = D(scale if scale is not None else [n], a, FAKE + 0x300000)
+    out = D([m, n], a, FAKE + 0x400000)
+    return x1, x2, sc, out
+
+
+@pytest.mark.parametrize("row", json.load(open(os.path.join(GOLDEN, "ut_named_rows.json")))["rows"],
+                         ids=lambda r: r["name"])
+def test_named_ut_rows(wqlib, row):
+    st = json.load(open(os.path.join(GOLDEN, "ut_named_rows.json")))["status"]
+    a, wd = DT[row["act"]], DT[row["weight"]]
+    x1 = D(row["x1"], a, FAKE + 0x100000)
+    x2 = D(row["x2"], wd, FAKE + 0x200000)
+    sc = D(row["scale"], a, FAKE + 0x300000)
+    out = D(row["out"], a, FAKE + 0x400000)
+    assert aq(wqlib, x1, x2, sc, out, g=row["group_size"]) == st[row["expect"]]
+
+
+def test_null_required(wqlib):
+    x1, x2, sc, out = base()
+    assert aq(wqlib, None, x2, sc, out) == NULLPTR
+    assert aq(wqlib, x1, None, sc, out) == NULLPTR
+    assert aq(wqlib, x1, x2, None, out) == NULLPTR
+    assert aq(wqlib, x1, x2, sc, None) == NULLPTR
+    assert aq(wqlib, x1, x2, sc, out, ws=False) == NULLPTR
+    x1n = D([32, 64], W.WQ_F16, 0)
+    assert aq(wqlib, x1n, x2, sc, out) == NULLPTR
+    # null checks come before dtype checks (the pages' order)
+    bad = D([32, 64], W.WQ_F32, 0)
+    assert aq(wqlib, bad, x2, sc, out) == NULLPTR
+
+
+def test_dtypes(wqlib):
+    x1, x2, sc, out = base()
+    assert aq(wqlib, x1, x2, sc, out) == OK
+    assert aq(wqlib, D([32, 64], W.WQ_F32), x2, sc, out) == INVALID
+    assert aq(wqlib, x1, D([64, 128], W.WQ_F16), sc, out) == INVALID
+    assert aq(wqlib, x1, x2, D([128], W.WQ_BF16), out) == INVALID           # scale != x1 dtype
+    assert aq(wqlib, x1, x2, sc, out, x3=D([32, 128], W.WQ_BF16)) == INVALID  # illegal x3 dtype
+    assert aq(wqlib, x1, x2, sc, out, bias=D([128], W.WQ_F32)) == INVALID
+    assert aq(wqlib, x1, x2, sc, D([32, 128], W.WQ_BF16)) == INVALID
+    assert aq(wqlib, x1, x2, sc, out, offset=D([128], W.WQ_BF16)) == INVALID
+
+
+def test_group_size_rule(wqlib):
+    # g = 0, or a multiple of 32 in [32, min(k-1, INT32_MAX)]
+    for g, k, expect in [(32, 64, OK), (64, 128, OK), (96, 256, OK), (224, 256, OK),
+                         (256, 256, INVALID), (16, 64, INVALID), (24, 64, INVALID),
+                         (33, 128, INVALID), (-32, 128, INVALID), (64, 64, INVALID)]:
+        groups = max(1, -(-k // g)) if g > 0 else 1
+        x1, x2, sc, out = base(k=k, scale=[groups, 128])
+        assert aq(wqlib, x1, x2, sc, out, g=g) == expect, (g, k)
+    # partial last group: k = 96, g = 64 -> scale (2, n)
+    x1, x2, sc, out = base(k=96, scale=[2, 128])
+    assert aq(wqlib, x1, x2, sc, out, g=64) == OK
+    x1, x2, sc, out = base(k=96, scale=[1, 128])
+    assert aq(wqlib, x1, x2, sc, out, g=64) == INVALID
+
+
+def test_scale_shapes(wqlib):
+    for shape, expect in [([1], OK), ([128], OK), ([1, 128], OK), ([2, 128], INVALID),
+                          ([127], INVALID), ([1, 1], INVALID), ([128, 1], INVALID)]:
+        x1, x2, sc, out = base(scale=shape)
+        assert aq(wqlib, x1, x2, sc, out) == expect, shape
+    x1, x2, sc, out = base()
+    assert aq(wqlib, x1, x2, sc, out, offset=D([1, 128], W.WQ_F16)) == INVALID  # offset != scale shape
+    assert aq(wqlib, x1, x2, sc, out, offset=D([128], W.WQ_F16)) == OK
+
+
+def test_shapes_and_ranges(wqlib):
+    f16 = W.WQ_F16
+    x1, x2, sc, out = base()
+    assert aq(wqlib, D([32, 96], f16), x2, sc, out) == INVALID                # k mismatch
+    assert aq(wqlib, x1, x2, sc, out, bias=D([64], f16)) == INVALID
+    assert aq(wqlib, x1, x2, sc, out, x3=D([32, 64], f16)) == INVALID
+    assert aq(wqlib, x1, x2, sc, D([31, 128], f16)) == INVALID
+    assert aq(wqlib, D([32], f16), x2, sc, out) == INVALID                    # 1-D x1
+    # 3-D activations: output follows x1
+    x13 = D([2, 16, 64], f16)
+    assert aq(wqlib, x13, x2, sc, D([2, 16, 128], f16)) == OK
+    assert aq(wqlib, x13, x2, sc, D([32, 128], f16)) == INVALID
+    assert aq(wqlib, D([2, 0, 64], f16, 0), x2, sc, D([2, 0, 128], f16, 0)) == INVALID
+    # n == 0, k > 65535, alignment
+    assert aq(wqlib, x1, D([64, 0], W.WQ_I8, 0), D([1], f16), D([32, 0], f16, 0)) == INVALID
+    assert aq(wqlib, D([32, 65536], f16), D([65536, 128], W.WQ_I8), sc, out) == INVALID
+    assert aq(wqlib, D([32, 48], f16), D([48, 128], W.WQ_I8), sc, out) == INVALID   # k % 32
+    assert aq(wqlib, x1, D([64, 112], W.WQ_I8), D([112], f16), D([32, 112], f16)) == INVALID
+    # int4 needs k, n multiples of 64
+    assert aq(wqlib, x1, D([64, 128], W.WQ_I4), sc, out) == OK
+    assert aq(wqlib, x1, D([64, 96], W.WQ_I4), D([96], f16), D([32, 96], f16)) == INVALID
+    assert aq(wqlib, D([32, 96], f16), D([96, 128], W.WQ_I4), sc, out) == INVALID
+
+
+def test_empty_k(wqlib):
+    f16 = W.WQ_F16
+    x1, x2 = D([32, 0], f16, 0), D([0, 128], W.WQ_I8, 0)
+    for scale, g in [([128], 0), ([1], 0), ([0, 128], 64), ([128], 16)]:
+        assert aq(wqlib, x1, x2, D(scale, f16, FAKE if scale[0] else 0), D([32, 128], f16), g=g) == OK
+
+
+def test_layout_and_alias(wqlib):
+    f16 = W.WQ_F16
+    x1, x2, sc, out = base()
+    # a transposed (non-contiguous) x2 is not accepted in this version
+    assert aq(wqlib, x1, D([64, 128], W.WQ_I8, None, [1, 64]), sc, out) == INVALID
+    # the output may not alias an input
+    assert aq(wqlib, x1, x2, sc, D([32, 128], f16, FAKE + 0x100000)) == INVALID
+
+
+def test_workspace_sizes(wqlib):
+    import ctypes as C
+    x1, x2, sc, out = base(m=32, k=8192, n=8192, scale=[128, 8192])
+    size = C.c_uint64(0)
+    r = C.byref
+    assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 64,
+                                                        r(out), r(size)) == OK
+    assert size.value > 0
+    # a workspace smaller than required is refused before anything is launched
+    st = wqlib.wq_antiquant_matmul(r(x1), r(x2), None, r(sc), None, None, 64, r(out),
+                                   C.c_void_p(FAKE), C.c_uint64(size.value - 1), None)
+    assert st == INVALID
+
+
+def qm(wqlib, x1, x2, dq, out, bias=None, x3=None, pt=None, acc=None):
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    size = ctypes.c_uint64(0)
+    return wqlib.wq_quant_matmul_get_workspace_size(r(x1), r(x2), r(bias), r(x3), r(dq), r(pt),
+                                                    r(out), r(acc), ctypes.byref(size))
+
+
+def test_w8a8_rules(wqlib):
+    i8, i32, f32, bf, f16 = W.WQ_I8, W.WQ_I32, W.WQ_F32, W.WQ_BF16, W.WQ_F16
+    x1, x2 = D([32, 64], i8, FAKE + 0x10000), D([64, 128], i8, FAKE + 0x20000)
+    dq, out = D([128], f32, FAKE + 0x30000), D([32, 128], bf, FAKE + 0x40000)
+    assert qm(wqlib, x1, x2, dq, out) == OK
+    assert qm(wqlib, x1, x2, dq, out, bias=D([128], i32), x3=D([32, 128], bf),
+              pt=D([32], f32), acc=D([32, 128], i32)) == OK
+    assert qm(wqlib, None, x2, dq, out) == NULLPTR
+    assert qm(wqlib, x1, x2, None, out) == NULLPTR
+    assert qm(wqlib, x1, x2, dq, None) == NULLPTR
+    assert qm(wqlib, D([32, 64], f16), x2, dq, out) == INVALID
+    assert qm(wqlib, x1, x2, dq, out, bias=D([128], f32)) == INVALID
+    assert qm(wqlib, x1, x2, D([128], W.WQ_I32), out) == INVALID          # packed int64 scale: no
+    assert qm(wqlib, x1, x2, dq, D([32, 128], f32)) == INVALID
+    assert qm(wqlib, x1, x2, dq, out, x3=D([32, 128], f16)) == INVALID     # x3 dtype != output
+    assert qm(wqlib, x1, x2, dq, out, pt=D([31], f32)) == INVALID
+    assert qm(wqlib, x1, x2, D([1], f32), out) == OK
+    assert qm(wqlib, x1, x2, D([1, 128], bf), out) == OK
+    assert qm(wqlib, x1, x2, D([2, 128], f32), out) == INVALID
+    assert qm(wqlib, D([32, 0], i8, 0), D([0, 128], i8, 0), dq, out) == INVALID  # no empty tensors
+    assert qm(wqlib, D([2, 16, 64], i8), x2, dq, D([2, 16, 128], bf), pt=D([32], f32)) == OK

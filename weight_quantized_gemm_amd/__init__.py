@@ -1,0 +1,210 @@
+"""weight_quantized_gemm_amd -- weight-anti-quant matmul and its W8A8 sibling on MI355X.
+
+Thin Python binding over the C ABI of ``libwqgemm.so`` (declared in ``include/wqgemm.h``).
+It only marshals arguments: tensors become ``wq_tensor`` descriptors (device pointer,
+dtype, shape, strides), the output and workspace are allocated with torch on the
+inputs' device, and the call is enqueued on torch's current HIP stream.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback path.
+
+    antiquant_matmul:  out = x1 @ ((x2 + offset) * scale) + bias + x3
+    quant_matmul:      out = dequant_scale * pertoken_scale * (x1 @ x2 + bias) + x3
+
+(the formulas of the aclnnWeightQuantMatmulAllReduce guide, section 计算公式, and of the
+aclnnQuantMatmulAllReduceV2 page, section Function, at one rank).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = ["WQ_F16", "WQ_BF16", "WQ_F32", "WQ_I8", "WQ_I4", "WQ_I32", "WQ_OK",
+           "WQ_ERR_PARAM_NULLPTR", "WQ_ERR_PARAM_INVALID", "WQ_ERR_RUNTIME", "WqTensor",
+           "WqError", "lib", "library_path", "make_desc", "antiquant_matmul",
+           "antiquant_workspace_size", "quant_matmul", "quant_workspace_size", "EXPORTS"]
+
+WQ_F16, WQ_BF16, WQ_F32, WQ_I8, WQ_I4, WQ_I32 = 1, 2, 3, 4, 5, 6
+WQ_OK, WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID, WQ_ERR_RUNTIME = 0, 161001, 161002, 561001
+
+EXPORTS = ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul",
+           "wq_quant_matmul_get_workspace_size", "wq_quant_matmul", "wq_status_string",
+           "wq_version")
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libwqgemm.so")
+
+
+class WqTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 3), ("stride", ctypes.c_int64 * 3)]
+
+
+class WqError(Exception):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is missing: build it with "
+                              "`python -m weight_quantized_gemm_amd.build`")
+        L = ctypes.CDLL(library_path)
+        P = ctypes.POINTER(WqTensor)
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        L.wq_antiquant_matmul_get_workspace_size.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, u64p]
+        L.wq_antiquant_matmul.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_void_p,
+                                          ctypes.c_uint64, ctypes.c_void_p]
+        L.wq_quant_matmul_get_workspace_size.argtypes = [P, P, P, P, P, P, P, P, u64p]
+        L.wq_quant_matmul.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_void_p, ctypes.c_uint64,
+                                      ctypes.c_void_p]
+        for f in ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul",
+                  "wq_quant_matmul_get_workspace_size", "wq_quant_matmul"):
+            getattr(L, f).restype = ctypes.c_int
+        L.wq_status_string.argtypes = [ctypes.c_int]
+        L.wq_status_string.restype = ctypes.c_char_p
+        L.wq_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status == WQ_OK:
+        return
+    msg = lib().wq_status_string(status).decode()
+    if status in (WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID):
+        raise ValueError(f"{msg} (status {status})")
+    raise WqError(status, msg)
+
+
+def make_desc(shape: Sequence[int], dtype: int, data: int, strides: Optional[Sequence[int]] = None):
+    """A descriptor from plain values (strides default to row-major contiguous)."""
+    d = WqTensor()
+    d.data = data or None
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= int(s)
+    for i in range(3):
+        d.shape[i] = int(shape[i]) if i < len(shape) else 0
+        d.stride[i] = int(strides[i]) if i < len(shape) else 0
+    return d
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float16: WQ_F16, torch.bfloat16: WQ_BF16, torch.float32: WQ_F32,
+         torch.int8: WQ_I8, torch.int32: WQ_I32}
+    if t.dtype not in m:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _desc(t, int4: bool = False):
+    if t is None:
+        return None
+    if int4:
+        torch = _torch()
+        if t.dtype not in (torch.uint8, torch.int8) or t.dim() != 2:
+            raise ValueError("packed int4 weights are a 2-D uint8/int8 tensor of shape (k, n/2)")
+        k, half = t.shape
+        st = [t.stride(0) * 2, 1] if t.stride(1) == 1 else [t.stride(0) * 2, t.stride(1) * 2]
+        return make_desc([k, 2 * half], WQ_I4, t.data_ptr(), st)
+    return make_desc(list(t.shape), _dtype_code(t), t.data_ptr(), list(t.stride()))
+
+
+def _ref(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+def _stream_of(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def antiquant_workspace_size(x1, x2, antiquant_scale, antiquant_offset=None, bias=None, x3=None,
+                             antiquant_group_size: int = 0, *, x2_int4: bool = False, out=None) -> int:
+    d = [_desc(x1), _desc(x2, x2_int4), _desc(bias), _desc(antiquant_scale),
+         _desc(antiquant_offset), _desc(x3)]
+    od = _desc(out) if out is not None else _out_desc_like(x1, x2, x2_int4)
+    ws = ctypes.c_uint64(0)
+    _check(lib().wq_antiquant_matmul_get_workspace_size(*map(_ref, d), int(antiquant_group_size),
+                                                        _ref(od), ctypes.byref(ws)))
+    return ws.value
+
+
+def _out_desc_like(x1, x2, x2_int4):
+    n = x2.shape[1] * (2 if x2_int4 else 1)
+    return make_desc(list(x1.shape[:-1]) + [n], _dtype_code(x1), 0x1)
+
+
+def antiquant_matmul(x1, x2, antiquant_scale, antiquant_offset=None, bias=None, x3=None,
+                     antiquant_group_size: int = 0, *, x2_int4: bool = False, out=None,
+                     workspace=None):
+    """out = x1 @ ((x2 + antiquant_offset) * antiquant_scale) + bias + x3 on x1's device.
+
+    x1: fp16/bf16 (m, k) or (b, s, k); x2: int8 (k, n), or with ``x2_int4`` a uint8 (k, n/2)
+    tensor of packed signed nibbles (even column in the low nibble); scale/offset: (1),
+    (n), (1, n) or (ceil(k/g), n) for group size g.  Returns the output tensor."""
+    torch = _torch()
+    n = x2.shape[1] * (2 if x2_int4 else 1)
+    if out is None:
+        out = torch.empty(tuple(x1.shape[:-1]) + (n,), dtype=x1.dtype, device=x1.device)
+    d = [_desc(x1), _desc(x2, x2_int4), _desc(bias), _desc(antiquant_scale),
+         _desc(antiquant_offset), _desc(x3)]
+    od = _desc(out)
+    ws = ctypes.c_uint64(0)
+    L = lib()
+    _check(L.wq_antiquant_matmul_get_workspace_size(*map(_ref, d), int(antiquant_group_size),
+                                                    _ref(od), ctypes.byref(ws)))
+    if workspace is None or workspace.numel() < ws.value:
+        workspace = torch.empty(max(int(ws.value), 1), dtype=torch.uint8, device=x1.device)
+    _check(L.wq_antiquant_matmul(*map(_ref, d), int(antiquant_group_size), _ref(od),
+                                 ctypes.c_void_p(workspace.data_ptr()), ctypes.c_uint64(workspace.numel()),
+                                 _stream_of(x1.device)))
+    return out
+
+
+def quant_workspace_size(x1, x2, dequant_scale, pertoken_scale=None, bias=None, x3=None, *,
+                         out=None, acc_out=None) -> int:
+    d = [_desc(x1), _desc(x2), _desc(bias), _desc(x3), _desc(dequant_scale), _desc(pertoken_scale),
+         _desc(out), _desc(acc_out)]
+    ws = ctypes.c_uint64(0)
+    _check(lib().wq_quant_matmul_get_workspace_size(*map(_ref, d), ctypes.byref(ws)))
+    return ws.value
+
+
+def quant_matmul(x1, x2, dequant_scale, pertoken_scale=None, bias=None, x3=None, *,
+                 out_dtype=None, out=None, acc_out=None):
+    """out = dequant_scale * pertoken_scale * (x1 @ x2 + bias) + x3 on x1's device.
+
+    x1, x2 int8; bias int32 (n); dequant_scale fp32/bf16 (1), (n) or (1, n); pertoken_scale
+    fp32 (m); x3 and the output fp16/bf16.  ``acc_out`` (int32, (m, n)) receives
+    x1 @ x2 + bias."""
+    torch = _torch()
+    if out is None:
+        dt = out_dtype if out_dtype is not None else (x3.dtype if x3 is not None else torch.bfloat16)
+        out = torch.empty(tuple(x1.shape[:-1]) + (x2.shape[1],), dtype=dt, device=x1.device)
+    d = [_desc(x1), _desc(x2), _desc(bias), _desc(x3), _desc(dequant_scale), _desc(pertoken_scale),
+         _desc(out), _desc(acc_out)]
+    ws = ctypes.c_uint64(0)
+    L = lib()
+    _check(L.wq_quant_matmul_get_workspace_size(*map(_ref, d), ctypes.byref(ws)))
+    workspace = torch.empty(max(int(ws.value), 1), dtype=torch.uint8, device=x1.device)
+    _check(L.wq_quant_matmul(*map(_ref, d), ctypes.c_void_p(workspace.data_ptr()),
+                             ctypes.c_uint64(workspace.numel()), _stream_of(x1.device)))
+    return out

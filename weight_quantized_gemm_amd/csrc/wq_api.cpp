@@ -1,0 +1,158 @@
+// C ABI entry points: validate, plan (kernel choice, workspace layout), launch.
+//
+// Two-phase shape after the pages ("CANN ops-transformer ... aclnnWeightQuantMatmulAllReduce
+// 完全指南", section 两段式接口与函数原型; "aclnnQuantMatmulAllReduceV2", Function
+// Prototype), without an executor object: both phases are stateless and repeatable.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "wq_kernels.h"
+#include "wq_problem.h"
+
+namespace wq {
+namespace {
+
+constexpr int64_t kAlign = 256;
+int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// The small-m split-k kernel serves m <= 32; larger m use the tiled kernel.
+constexpr int64_t kSmallM = 32;
+
+struct AqPlan {
+  bool empty_k = false;
+  bool small_m = false;
+  int splits = 1;
+  int64_t mp = 0;
+  int64_t rowsum_bytes = 0;
+  int64_t partial_bytes = 0;
+  int64_t workspace = 0;
+};
+
+AqPlan plan_antiquant(const AntiquantProblem& p) {
+  AqPlan pl;
+  if (p.k == 0) {
+    pl.empty_k = true;
+    return pl;
+  }
+  pl.mp = aq_rowsum_mp(p.m);
+  pl.rowsum_bytes = align_up(p.groups * pl.mp * (int64_t)sizeof(float));
+  pl.small_m = p.m <= kSmallM;
+  if (pl.small_m) {
+    pl.splits = aq_smallm_splits(p.m, (int)p.k, (int)p.n, (int)p.group, p.mode == QuantMode::kGroup);
+    pl.partial_bytes = align_up((int64_t)pl.splits * p.m * p.n * (int64_t)sizeof(float));
+  }
+  pl.workspace = pl.rowsum_bytes + pl.partial_bytes;
+  return pl;
+}
+
+float code_bias(const AntiquantProblem& p) {
+  if (p.act == WQ_F16) return 0.f;
+  return p.w4 ? 136.f : 128.f;  // bf16 images are code + C (see wq_device.h)
+}
+
+}  // namespace
+}  // namespace wq
+
+extern "C" {
+
+int wq_antiquant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor* x2,
+                                           const wq_tensor* bias, const wq_tensor* antiquant_scale,
+                                           const wq_tensor* antiquant_offset, const wq_tensor* x3,
+                                           int64_t antiquant_group_size, const wq_tensor* output,
+                                           uint64_t* workspace_size) {
+  wq::AntiquantProblem p;
+  int st = wq::validate_antiquant(x1, x2, bias, antiquant_scale, antiquant_offset, x3,
+                                  antiquant_group_size, output, &p);
+  if (st != WQ_OK) return st;
+  if (!workspace_size) return WQ_ERR_PARAM_NULLPTR;
+  *workspace_size = (uint64_t)wq::plan_antiquant(p).workspace;
+  return WQ_OK;
+}
+
+int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
+                        const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,
+                        const wq_tensor* x3, int64_t antiquant_group_size, const wq_tensor* output,
+                        void* workspace, uint64_t workspace_size, void* stream) {
+  wq::AntiquantProblem p;
+  int st = wq::validate_antiquant(x1, x2, bias, antiquant_scale, antiquant_offset, x3,
+                                  antiquant_group_size, output, &p);
+  if (st != WQ_OK) return st;
+  const wq::AqPlan pl = wq::plan_antiquant(p);
+  if (workspace_size < (uint64_t)pl.workspace) return WQ_ERR_PARAM_INVALID;
+  if (pl.workspace > 0 && !workspace) return WQ_ERR_PARAM_NULLPTR;
+  hipStream_t s = (hipStream_t)stream;
+
+  wq::AqArgs a{};
+  a.x1 = p.x1; a.x2 = p.x2; a.scale = p.scale; a.offset = p.offset; a.bias = p.bias;
+  a.x3 = p.x3; a.out = p.out;
+  a.m = p.m; a.k = (int32_t)p.k; a.n = (int32_t)p.n;
+  a.group = (int32_t)p.group; a.groups = (int32_t)p.groups;
+  a.bf16 = p.act == WQ_BF16; a.w4 = p.w4;
+  a.grouped = p.mode == wq::QuantMode::kGroup;
+  a.per_tensor = p.mode == wq::QuantMode::kTensor;
+  a.code_bias = wq::code_bias(p);
+  a.splits = pl.splits;
+  a.mp = pl.mp;
+
+  hipError_t e;
+  if (pl.empty_k) {
+    e = wq::launch_aq_bias_x3(a, s);
+    return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
+  }
+  a.rowsum = (const float*)workspace;
+  a.partial = pl.small_m ? (float*)((char*)workspace + pl.rowsum_bytes) : nullptr;
+  e = wq::launch_aq_rowsum(a, s);
+  if (e != hipSuccess) return WQ_ERR_RUNTIME;
+  e = pl.small_m ? wq::launch_aq_smallm(a, s) : wq::launch_aq_gemm(a, s);
+  return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
+}
+
+int wq_quant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor* x2,
+                                       const wq_tensor* bias, const wq_tensor* x3,
+                                       const wq_tensor* dequant_scale,
+                                       const wq_tensor* pertoken_scale, const wq_tensor* output,
+                                       const wq_tensor* acc_out, uint64_t* workspace_size) {
+  int st = wq::validate_quant(x1, x2, bias, x3, dequant_scale, pertoken_scale, output, acc_out,
+                              nullptr);
+  if (st != WQ_OK) return st;
+  if (!workspace_size) return WQ_ERR_PARAM_NULLPTR;
+  *workspace_size = 0;
+  return WQ_OK;
+}
+
+int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
+                    const wq_tensor* x3, const wq_tensor* dequant_scale,
+                    const wq_tensor* pertoken_scale, const wq_tensor* output,
+                    const wq_tensor* acc_out, void* workspace, uint64_t workspace_size,
+                    void* stream) {
+  (void)workspace;
+  (void)workspace_size;
+  wq::QuantProblem p;
+  int st = wq::validate_quant(x1, x2, bias, x3, dequant_scale, pertoken_scale, output, acc_out, &p);
+  if (st != WQ_OK) return st;
+  wq::QmArgs a{};
+  a.x1 = (const int8_t*)p.x1; a.x2 = (const int8_t*)p.x2; a.bias = (const int32_t*)p.bias;
+  a.x3 = p.x3; a.dq = p.dq; a.pt = (const float*)p.pt; a.out = p.out;
+  a.acc_out = (int32_t*)p.acc_out;
+  a.m = p.m; a.k = (int32_t)p.k; a.n = (int32_t)p.n;
+  a.out_bf16 = p.out_dtype == WQ_BF16; a.dq_bf16 = p.dq_dtype == WQ_BF16;
+  a.dq_per_tensor = p.dq_per_tensor;
+  hipError_t e = wq::launch_qm_gemm(a, (hipStream_t)stream);
+  return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
+}
+
+const char* wq_status_string(int status) {
+  switch (status) {
+    case WQ_OK: return "WQ_OK";
+    case WQ_ERR_PARAM_NULLPTR: return "WQ_ERR_PARAM_NULLPTR: a required argument is a null pointer";
+    case WQ_ERR_PARAM_INVALID: return "WQ_ERR_PARAM_INVALID: an argument breaks a dtype, attribute, shape, layout or workspace rule";
+    case WQ_ERR_RUNTIME: return "WQ_ERR_RUNTIME: a HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int wq_version(void) { return 100; }  // 0.1.0
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Kernel argument blocks and launchers (host side of the HIP translation units).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace wq {
+
+// Anti-quant matmul.  All 16-bit tensors are fp16 or bf16 bit patterns (act dtype).
+struct AqArgs {
+  const void* x1;        // (m, k)
+  const void* x2;        // int8 (k, n) or packed int4 (k, n/2) bytes
+  const void* scale;     // (groups, n), (n) or (1)
+  const void* offset;    // like scale, or null
+  const void* bias;      // (n) or null
+  const void* x3;        // (m, n) or null
+  void* out;             // (m, n)
+  const float* rowsum;   // [groups][mp] fp32 row sums of x1 per group (mp = rows padded)
+  float* partial;        // split-k partials [splits][m][n] (small-m path), else null
+  int64_t m;
+  int64_t mp;            // row stride of rowsum (m rounded up to 256)
+  int32_t k, n;
+  int32_t group;         // group size along k (per-group); k otherwise
+  int32_t groups;        // parameter rows (1 unless per-group)
+  int32_t splits;        // k splits (small-m path)
+  int32_t tiles_m, tiles_n;
+  float code_bias;       // C: the fed weight image is code + C
+  bool bf16, w4, grouped, per_tensor;
+};
+
+// W8A8 matmul.
+struct QmArgs {
+  const int8_t* x1;      // (m, k)
+  const int8_t* x2;      // (k, n)
+  const int32_t* bias;   // (n) or null
+  const void* x3;        // (m, n) out dtype or null
+  const void* dq;        // (1) or (n), fp32 or bf16
+  const float* pt;       // (m) or null
+  void* out;             // (m, n) fp16 / bf16
+  int32_t* acc_out;      // (m, n) or null
+  int64_t m;
+  int32_t k, n;
+  int32_t tiles_m, tiles_n;
+  bool out_bf16, dq_bf16, dq_per_tensor;
+};
+
+hipError_t launch_aq_rowsum(const AqArgs& a, hipStream_t stream);
+hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream);
+hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream);
+hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream);  // k == 0
+hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);
+
+// Row-major workspace sizes (bytes) and split choices, shared by planner and launchers.
+int64_t aq_rowsum_mp(int64_t m);
+int aq_smallm_splits(int64_t m, int k, int n, int group, bool grouped);
+
+}  // namespace wq
