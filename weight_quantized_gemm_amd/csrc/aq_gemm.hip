@@ -9,47 +9,91 @@
 //   out[m,n] = sum_g s[g,n] * ( P_g[m,n] + (off[g,n] - C) * S_g[m] ) + bias[n] + x3[m,n]
 //   P_g[m,n] = sum_{i in group g} x1[m,i] * (x2[i,n] + C),   S_g[m] = sum_{i in g} x1[m,i]
 //
-// where C is the constant bias of the fed weight images (128 for bf16/int8, 136 for
-// bf16/int4, 0 for fp16).  The matrix cores see only exact 16-bit images of the integer
-// codes and x1; scale and offset are applied in fp32 on the accumulators, per group at
-// each group boundary, or once in the epilogue for per-tensor / per-channel parameters.
-// S_g comes from the row-sum pass (aq_prep.hip).
+// C is the constant bias of the fed weight images (136 for bf16/int4, 0 otherwise).  The
+// matrix cores see only exact 16-bit images of the integer codes and x1; scale and offset
+// are applied in fp32 on the accumulators, per group at each group end, or once in the
+// epilogue for per-tensor / per-channel parameters.  S_g is summed in-kernel from the x1
+// fragments (v_dot2 against ones).
 //
-// Tiling: 256 threads = 4 waves in a 2 x 2 grid; wave tile (32*WM) x (32*WN) of 32x32x16
-// MFMA blocks; workgroup tile BM = 64*WM rows x BN = 64*WN columns; BK = 64 along k,
-// double-buffered in LDS.
-//   * x1 tile: row-major in LDS, pitch 144 B (64 values + 16 B pad), MFMA A fragments by
-//     16-byte reads;
-//   * x2 tile: converted once per workgroup while staging into 16-bit images, row-major
-//     (n-contiguous), pitch 2*BN + 64 B, MFMA B fragments by two tr16 transpose reads.
+// Pipeline: GM x GN waves, wave tile (32*WM) x (32*WN), workgroup tile 256 x (32*WN*GN),
+// BK = 64.  Operands travel global -> LDS by direct-to-LDS buffer loads
+// (no registers, out-of-range lanes read zero) through 3 LDS stages, one barrier per
+// k-step.  x1 tiles are row-major with a 16-byte-chunk XOR swizzle and are read as MFMA A
+// fragments by ds_read_b128.  Weight tiles stay raw (int8 or packed int4, n-contiguous,
+// 32-byte-pair XOR swizzle); B fragments come from ds_read_b64_tr_b8 (8 consecutive k of
+// one column per lane) and are turned into exact 16-bit images in registers.  The
+// epilogue stages fp32 results through LDS so that x3, bias and the output move in
+// 16-byte row-contiguous accesses.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
 namespace wq {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBK = 64;
-constexpr int kApitch = 72;  // u16 per x1 row in LDS (64 + 8 pad)
+constexpr int kStages = 3;
+constexpr int kArow = 128;                 // bytes per x1 row in a stage (64 x 16-bit)
+constexpr int kAbytes = 256 * kArow;       // 32 KiB: 256 rows of x1
 
-template <int WM, int WN>
-struct AqTile {
-  static constexpr int BM = 64 * WM;
-  static constexpr int BN = 64 * WN;
-  static constexpr int Bpitch = BN + 32;  // u16 per weight row in LDS
-  static constexpr int A_elems = BM * kApitch;
-  static constexpr int B_elems = kBK * Bpitch;
-  static constexpr int Stage = A_elems + B_elems;
-  static constexpr int A_chunks = BM * kBK / 8 / kThreads;  // 16-byte x1 chunks per thread
+template <bool W4, int GM, int GN, int WM, int WN>
+struct Tile {
+  static constexpr int Waves = GM * GN;              // wave grid GM x GN
+  static constexpr int Threads = 64 * Waves;
+  static constexpr int BM = 32 * WM * GM;            // 256 rows
+  static constexpr int BN = 32 * WN * GN;            // logical columns
+  static constexpr int RB = W4 ? BN / 2 : BN;        // weight bytes per k row
+  static constexpr int Bbytes = kBK * RB;
+  static constexpr int Stage = kAbytes + Bbytes;
+  static constexpr int Win = 256 / RB;               // k rows per 256-byte bank window
+  static constexpr int PairMask = 8 / Win - 1;       // swizzle span of 32-byte pairs
+  static constexpr int RowsPerKB = 1024 / RB;        // k rows per 1 KiB DMA block
+  static constexpr int Ablocks = kAbytes / 1024;     // 32
+  static constexpr int Bblocks = Bbytes / 1024;      // DMA blocks per stage (weights)
+  static constexpr int Aper = Ablocks / Waves;
+  // weights: Bblocks spread over the first Bblocks waves when there are fewer blocks
+  static constexpr int Bper = Bblocks >= Waves ? Bblocks / Waves : 1;
+  static constexpr int Bwaves = Bblocks >= Waves ? Waves : Bblocks;
+  static constexpr int WCols = 32 * WN;              // logical columns per wave
+  static constexpr int Reads = W4 ? WN / 2 : WN;     // tr8 reads per wave per 16-k step
+  // LDS layout: stages | S rows (BM fp32) | per-wave group-sum scratch (Waves x 32*WM fp32)
+  static constexpr int SOff = kStages * Stage;
+  static constexpr int GOff = SOff + BM * 4;
+  static constexpr int Total = GOff + Waves * 32 * WM * 4;
+  static_assert(BM == 256, "x1 stage holds 256 rows");
+  static_assert(Ablocks % Waves == 0, "x1 DMA blocks split evenly over the waves");
+  static_assert(Bblocks % Waves == 0 || Bblocks < Waves, "weight DMA blocks split");
+  static_assert(Win >= 1 && Win <= 4, "weight row bytes 64..256");
+  static_assert(!W4 || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
 };
 
-// Map a linear workgroup id to a tile.  Workgroups are dispatched round-robin over the 8
-// XCDs; consecutive tile ids are handed to one XCD so that its L2 sees a compact band of
-// rows and columns, and inside the band tiles are walked in groups of 4 m-tiles.
+// x1 tile swizzle: 16-byte chunk c of row r lives in slot c ^ ((r >> 1) & 7), so that 16
+// consecutive rows read at the same chunk hit 16 distinct bank groups.
+__device__ __forceinline__ int a_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// weight tile swizzle: 32-byte pair p of k row r lives in pair p ^ ((r / Win) & PairMask),
+// so that the 8 rows of a tr8 read land in 8 distinct bank groups.
+template <class T>
+__device__ __forceinline__ int b_pair(int r, int pair) { return pair ^ ((r / T::Win) & T::PairMask); }
+
+
+// vmcnt(N) then the workgroup barrier (N is the per-wave count of loads allowed in flight)
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  if constexpr (N == 0) WQ_STAGE_BARRIER(0);
+  else if constexpr (N == 4) WQ_STAGE_BARRIER(4);
+  else if constexpr (N == 5) WQ_STAGE_BARRIER(5);
+  else if constexpr (N == 6) WQ_STAGE_BARRIER(6);
+  else if constexpr (N == 8) WQ_STAGE_BARRIER(8);
+  else if constexpr (N == 9) WQ_STAGE_BARRIER(9);
+  else if constexpr (N == 10) WQ_STAGE_BARRIER(10);
+  else if constexpr (N == 12) WQ_STAGE_BARRIER(12);
+  else static_assert(N < 0, "add this vmcnt value");
+}
+
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   int t = bid;
-  if ((total & 7) == 0) t = (bid & 7) * (total >> 3) + (bid >> 3);
+  if ((total & 7) == 0) t = (bid & 7) * (total >> 3) + (bid >> 3);  // XCD-contiguous bands
   constexpr int kGroupM = 4;
   const int per_group = kGroupM * tiles_n;
   const int g = t / per_group;
@@ -60,90 +104,90 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = r / gm;
 }
 
-template <bool BF16, bool W4, int WM, int WN, bool GROUPED>
-__global__ __launch_bounds__(kThreads, 1) void aq_gemm_kernel(const AqArgs a) {
-  using T = AqTile<WM, WN>;
-  constexpr int BM = T::BM, BN = T::BN, Bp = T::Bpitch;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+// One 16-k step of MFMA operands for a wave: WM x1 fragments (16-byte reads) and the raw
+// weight bytes of its tr8 reads.
+template <int WM, int R>
+struct Frag {
+  u32x4_t a[WM];
+  u32x2_t raw[R];
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+template <class T, int WM>
+__device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, int kk, int wm, int wn,
+                                          int lane, Frag<WM, T::Reads>& f) {
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const int r = wm * (32 * WM) + 32 * i + (lane & 31);
+    const int c = 2 * kk + (lane >> 5);
+    f.a[i] = *(const u32x4_t*)(As + r * kArow + 16 * a_slot(r, c));
+  }
+  const int kr = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 1);
+#pragma unroll
+  for (int j = 0; j < T::Reads; ++j) {
+    const int pair = wn * T::Reads + j;  // 32-byte pair within the weight row
+    const int off = kr * T::RB + 32 * b_pair<T>(kr, pair) + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    f.raw[j] = lds_read_tr8(Bs + off);
+  }
+}
+
+template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
+__global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a) {
+  using T = Tile<W4, GM, GN, WM, WN>;
+  constexpr int BN = T::BN, RB = T::RB, WC = T::WCols;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave / GN, wn = wave % GN;
   int tm, tn;
   tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t m0 = (int64_t)tm * 256;
   const int n0 = tn * BN;
   const int64_t M = a.m;
   const int K = a.k, N = a.n;
+  const int64_t x2_pitch = W4 ? (N >> 1) : N;
+  const int nk = (K + kBK - 1) / kBK;
 
-  const uint16_t* __restrict__ x1 = (const uint16_t*)a.x1;
-  const uint8_t* __restrict__ x2 = (const uint8_t*)a.x2;
-
-  // ---------------------------------------------------------------- staging registers
-  // x1: thread owns 16-byte chunk (tid % 8) of rows tid/8 + 32*i.
-  const int a_chunk = tid & 7;
-  const int a_row0 = tid >> 3;
-  u32x4_t ra[T::A_chunks];
-  // x2: int8 -> 16 columns per 16-byte chunk; int4 -> 32 columns per chunk.
-  constexpr int kColsPerChunk = W4 ? 32 : 16;
-  constexpr int kChunksPerRow = BN / kColsPerChunk;
-  constexpr int kRowsPerPass = kThreads / kChunksPerRow;
-  constexpr int kBPasses = kBK / kRowsPerPass;
-  static_assert(kBPasses >= 1 && kRowsPerPass * kChunksPerRow == kThreads, "B staging shape");
-  const int b_chunk = tid % kChunksPerRow;
-  const int b_row0 = tid / kChunksPerRow;
-  u32x4_t rb[kBPasses];
-  const int64_t x2_pitch = W4 ? (N >> 1) : N;  // bytes per weight row
-
-  auto load_tiles = [&](int k0) {
+  // ---------------------------------------------------------------- DMA issue
+  // x1: wave w fills 1 KiB blocks b = w + Waves*j (8 rows each); lane -> (row, physical
+  // slot).  The per-lane byte offsets inside a stage do not depend on k: they are formed
+  // once, and each k-step only moves the (scalar) buffer base.
+  const uint8_t* x1b = (const uint8_t*)a.x1 + m0 * K * 2;
+  const int64_t x1_rows_bytes = (M - m0) * K * 2;
+  const int nb0 = W4 ? n0 / 2 : n0;
+  const uint8_t* x2b = (const uint8_t*)a.x2 + nb0;
+  uint32_t a_off[T::Aper];
+  int a_chunk[T::Aper];
 #pragma unroll
-    for (int i = 0; i < T::A_chunks; ++i) {
-      const int64_t row = m0 + a_row0 + 32 * i;
-      const int kk = k0 + a_chunk * 8;
-      if (row < M && kk < K)
-        ra[i] = *(const u32x4_t*)(x1 + row * K + kk);
-      else
-        ra[i] = u32x4_t{0, 0, 0, 0};
+  for (int j = 0; j < T::Aper; ++j) {
+    const int b = wave + T::Waves * j;
+    const int r = 8 * b + (lane >> 3);
+    a_chunk[j] = a_slot(r, lane & 7);  // logical chunk held by this physical slot
+    a_off[j] = (uint32_t)(r * K * 2 + 16 * a_chunk[j]);
+  }
+  uint32_t b_off[T::Bper];
+#pragma unroll
+  for (int j = 0; j < T::Bper; ++j) {
+    const int b = wave + T::Waves * j;
+    const int r = T::RowsPerKB * b + lane / (RB / 16);
+    const int p = lane % (RB / 16);
+    b_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * b_pair<T>(r, p >> 1) + (p & 1)));
+  }
+  auto issue = [&](int ks) {
+    uint8_t* st = smem + (ks % kStages) * T::Stage;
+    const int k0 = ks * kBK;
+    const u32x4_t ra = make_rsrc(x1b + (int64_t)k0 * 2, x1_rows_bytes - (int64_t)k0 * 2);
+    const bool tail = k0 + kBK > K;  // only the last k-step can reach past k
+#pragma unroll
+    for (int j = 0; j < T::Aper; ++j) {
+      const uint32_t off = (tail && k0 + 8 * a_chunk[j] >= K) ? kOOB : a_off[j];
+      dma16(ra, st + 1024 * (wave + T::Waves * j), off);
     }
+    if (wave >= T::Bwaves) return;
+    const u32x4_t rb = make_rsrc(x2b + (int64_t)k0 * x2_pitch, (int64_t)(K - k0) * x2_pitch - nb0);
 #pragma unroll
-    for (int i = 0; i < kBPasses; ++i) {
-      const int kr = k0 + b_row0 + kRowsPerPass * i;
-      const int col = n0 + b_chunk * kColsPerChunk;
-      if (kr < K && col < N)
-        rb[i] = *(const u32x4_t*)(x2 + (int64_t)kr * x2_pitch + (W4 ? (col >> 1) : col));
-      else
-        rb[i] = u32x4_t{0, 0, 0, 0};
-    }
-  };
-
-  auto store_tiles = [&](int stage) {
-    uint16_t* As = smem + stage * T::Stage;
-    uint16_t* Bs = As + T::A_elems;
-#pragma unroll
-    for (int i = 0; i < T::A_chunks; ++i)
-      *(u32x4_t*)(As + (a_row0 + 32 * i) * kApitch + a_chunk * 8) = ra[i];
-#pragma unroll
-    for (int i = 0; i < kBPasses; ++i) {
-      uint16_t* dst = Bs + (b_row0 + kRowsPerPass * i) * Bp + b_chunk * kColsPerChunk;
-      if constexpr (W4) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t o[4];
-          i4x8_to_act<BF16>(rb[i][q], o);
-          *(u32x4_t*)(dst + 8 * q) = u32x4_t{o[0], o[1], o[2], o[3]};
-        }
-      } else {
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (BF16) i8x4_to_bf16(rb[i][q], o[2 * q], o[2 * q + 1]);
-          else i8x4_to_f16(rb[i][q], o[2 * q], o[2 * q + 1]);
-        }
-        *(u32x4_t*)(dst) = u32x4_t{o[0], o[1], o[2], o[3]};
-        *(u32x4_t*)(dst + 8) = u32x4_t{o[4], o[5], o[6], o[7]};
-      }
-    }
+    for (int j = 0; j < T::Bper; ++j)
+      dma16(rb, st + kAbytes + 1024 * (wave + T::Waves * j), b_off[j]);
   };
 
   // ---------------------------------------------------------------- accumulators
@@ -159,43 +203,59 @@ __global__ __launch_bounds__(kThreads, 1) void aq_gemm_kernel(const AqArgs a) {
 #pragma unroll
       for (int j = 0; j < WN; ++j) tot[i][j] = f32x16_t{};
   }
+  // row sums of x1 (lane half l>>5 of row 32i + l%32 of the wave's band).  Per-channel:
+  // the GN waves of a row band share its WM i-blocks, wave wn summing blocks
+  // wn*SB .. wn*SB + SB - 1.  Per-group: every wave sums all of its rows (it needs them at
+  // each group end).
+  constexpr int SB = GROUPED ? WM : (WM / GN > 0 ? WM / GN : 1);  // blocks summed per wave
+  static_assert(GROUPED || WM % GN == 0 || GN % WM == 0, "row-sum split");
+  float ssum[SB];
+#pragma unroll
+  for (int i = 0; i < SB; ++i) ssum[i] = 0.f;
+  // the wave's first summed block (per-channel): uniform
+  const int sb0 = GROUPED ? 0 : (WM >= GN ? wn * SB : (wn < WM ? wn : WM));
 
   const uint16_t* __restrict__ scale = (const uint16_t*)a.scale;
   const uint16_t* __restrict__ offset = (const uint16_t*)a.offset;
-  const float* __restrict__ rsum = a.rowsum;  // [groups][mp]
   const float cbias = a.code_bias;
-  // lane's output column in block j and first output row of block i
-  const int lane_col = n0 + wn * (32 * WN) + (lane & 31);
-  const int64_t wave_row0 = m0 + wm * (32 * WM);
+  float* gscr = (float*)(smem + T::GOff) + wave * (32 * WM);  // this wave's S_g scratch
 
-  // fold one finished group into the totals: tot += s * acc + s * (off - C) * S_g
+  // logical column of lane's block j (int4: block 2p + e covers byte pair p, parity e)
+  auto block_col = [&](int j) -> int {
+    if constexpr (W4) return n0 + wn * WC + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
+    else return n0 + wn * WC + 32 * j + (lane & 31);
+  };
+
+  // fold group g: tot += s * acc + s * (off - C) * S_g
   auto rescale = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const float t = ssum[i] + __shfl_xor(ssum[i], 32, 64);
+      if (lane < 32) gscr[32 * i + lane] = t;
+      ssum[i] = 0.f;  // per-group: SB == WM
+    }
     float s[WN], q[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      const int col = lane_col + 32 * j;
+      const int col = block_col(j);
       const bool ok = col < N;
       const float sv = ok ? act_to_f32<BF16>(scale[(int64_t)g * N + col]) : 0.f;
       const float ov = (ok && offset) ? act_to_f32<BF16>(offset[(int64_t)g * N + col]) : 0.f;
       s[j] = sv;
       q[j] = sv * (ov - cbias);
     }
-    // rowsum rows are padded to a multiple of 256 with zeros, so every tile row is in bounds
-    const float* sg = rsum + (int64_t)g * a.mp;
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int64_t row = wave_row0 + 32 * i + 8 * rq + 4 * (lane >> 5);
-        const f32x4_t sr = *(const f32x4_t*)(sg + row);
+        const f32x4_t sr = *(const f32x4_t*)(gscr + 32 * i + 8 * rq + 4 * (lane >> 5));
 #pragma unroll
-        for (int j = 0; j < WN; ++j) {
+        for (int j = 0; j < WN; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rq + e;
             tot[i][j][r] = fmaf(s[j], acc[i][j][r], fmaf(q[j], sr[e], tot[i][j][r]));
           }
-        }
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) acc[i][j] = f32x16_t{};
@@ -203,124 +263,215 @@ __global__ __launch_bounds__(kThreads, 1) void aq_gemm_kernel(const AqArgs a) {
   };
 
   // ---------------------------------------------------------------- main loop
-  const int nk = (K + kBK - 1) / kBK;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-
+  issue(0);
+  if (nk > 1) issue(1);
   for (int ks = 0; ks < nk; ++ks) {
-    const int stage = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) load_tiles((ks + 1) * kBK);
+    // stage ks is complete once only the next stage's loads may still be in flight
+    if (ks + 1 < nk) {
+      if (wave < T::Bwaves) stage_barrier<T::Aper + T::Bper>();
+      else stage_barrier<T::Aper>();
+    } else {
+      stage_barrier<0>();
+    }
+    if (ks + 2 < nk) issue(ks + 2);
 
-    const uint16_t* As = smem + stage * T::Stage;
-    const uint16_t* Bs = As + T::A_elems;
+    const uint8_t* As = smem + (ks % kStages) * T::Stage;
+    const uint8_t* Bs = As + kAbytes;
+    // Fragments are double-buffered across the four 16-k steps: the reads of step kk + 1
+    // are issued before the MFMAs of step kk, so LDS latency hides behind them.
+    Frag<WM, T::Reads> f0, f1;
+    load_frag<T, WM>(As, Bs, 0, wm, wn, lane, f0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u32x4_t af[WM], bfr[WN];
+      Frag<WM, T::Reads>& cur = (kk & 1) ? f1 : f0;
+      Frag<WM, T::Reads>& nxt = (kk & 1) ? f0 : f1;
+      if (kk < 3) load_frag<T, WM>(As, Bs, kk + 1, wm, wn, lane, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (GROUPED) {
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        const int row = wm * (32 * WM) + 32 * i + (lane & 31);
-        af[i] = *(const u32x4_t*)(As + row * kApitch + kk * 16 + 8 * (lane >> 5));
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ssum[i] = dot2_ones<BF16>(cur.a[i][q], ssum[i]);
+      } else {
+        // select this wave's blocks without dynamic register indexing
+#pragma unroll
+        for (int t = 0; t < SB; ++t) {
+          u32x4_t v = cur.a[0];
+#pragma unroll
+          for (int i = 1; i < WM; ++i)
+            if (sb0 + t == i) v = cur.a[i];
+          if (sb0 + t < WM) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ssum[t] = dot2_ones<BF16>(v[q], ssum[t]);
+          }
+        }
       }
+      u32x4_t bfr[WN];
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int kr = kk * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
-        const int nc = wn * (32 * WN) + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const u32x2_t lo = lds_read_tr16(Bs + kr * Bp + nc);
-        const u32x2_t hi = lds_read_tr16(Bs + (kr + 4) * Bp + nc);
-        bfr[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      for (int j = 0; j < T::Reads; ++j) {
+        if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
+        else bfr[j] = i8x8_to_act<BF16>(cur.raw[j]);
       }
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], acc[i][j]);
 
       if constexpr (GROUPED) {
-        if (kk & 1) {  // a 32-wide slice of k is done; groups end on multiples of 32
+        if (kk & 1) {  // groups end on multiples of 32
           const int kdone = ks * kBK + kk * 16 + 16;
           if (kdone <= K && (kdone % a.group == 0 || kdone == K)) rescale((kdone - 1) / a.group);
         }
       }
     }
-
-    if (more) store_tiles(stage ^ 1);
-    __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogue
+  __syncthreads();  // every wave is done with the stage buffers
+  float* srow = (float*)(smem + T::SOff);
+  if constexpr (!GROUPED) {
+#pragma unroll
+    for (int t = 0; t < SB; ++t) {
+      const float v = ssum[t] + __shfl_xor(ssum[t], 32, 64);
+      if (lane < 32 && sb0 + t < WM) srow[wm * (32 * WM) + 32 * (sb0 + t) + lane] = v;
+    }
+    __syncthreads();
+  }
+  // Each wave stages one 32-row band of its tile at a time in its own LDS region, then
+  // moves 8 consecutive columns per lane with 16-byte accesses.
+  constexpr int EP = WC + 8;            // fp32 pitch of the staging rows (bank spread)
+  float* E = (float*)smem + wave * (32 * EP);
   const uint16_t* __restrict__ bias = (const uint16_t*)a.bias;
   const uint16_t* __restrict__ x3 = (const uint16_t*)a.x3;
   uint16_t* __restrict__ out = (uint16_t*)a.out;
-  float s[WN], q[WN], bcol[WN];
+  constexpr int LanesPerRow = WC / 8;
+  constexpr int RowsPerPass = 64 / LanesPerRow;
+  const int ecol = 8 * (lane % LanesPerRow);
+  const int gcol = n0 + wn * WC + ecol;   // first of this lane's 8 output columns
+  const bool col_ok = gcol < N;
+  // per-column parameters of this lane's 8 columns
+  float cs[8], cq[8], cb[8];
 #pragma unroll
-  for (int j = 0; j < WN; ++j) {
-    const int col = lane_col + 32 * j;
-    const bool ok = col < N;
-    bcol[j] = (ok && bias) ? act_to_f32<BF16>(bias[col]) : 0.f;
+  for (int e = 0; e < 8; ++e) { cs[e] = 0.f; cq[e] = 0.f; cb[e] = 0.f; }
+  if (col_ok) {
+    if (bias) {
+      const u32x4_t bv = *(const u32x4_t*)(bias + gcol);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cb[e] = act_to_f32<BF16>((uint16_t)(bv[e >> 1] >> (16 * (e & 1))));
+    }
     if constexpr (!GROUPED) {
-      const int pc = a.per_tensor ? 0 : col;
-      const float sv = ok ? act_to_f32<BF16>(scale[pc]) : 0.f;
-      const float ov = (ok && offset) ? act_to_f32<BF16>(offset[pc]) : 0.f;
-      s[j] = sv;
-      q[j] = sv * (ov - cbias);
+      if (a.per_tensor) {
+        const float sv = act_to_f32<BF16>(scale[0]);
+        const float ov = offset ? act_to_f32<BF16>(offset[0]) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { cs[e] = sv; cq[e] = sv * (ov - cbias); }
+      } else {
+        const u32x4_t sv = *(const u32x4_t*)(scale + gcol);
+        u32x4_t ov = u32x4_t{0, 0, 0, 0};
+        if (offset) ov = *(const u32x4_t*)(offset + gcol);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float s = act_to_f32<BF16>((uint16_t)(sv[e >> 1] >> (16 * (e & 1))));
+          const float o = offset ? act_to_f32<BF16>((uint16_t)(ov[e >> 1] >> (16 * (e & 1)))) : 0.f;
+          cs[e] = s;
+          cq[e] = s * (o - cbias);
+        }
+      }
     }
   }
 #pragma unroll
   for (int i = 0; i < WM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = wave_row0 + 32 * i + acc_row(r, lane);
-      if (row >= M) continue;
-      float srow = 0.f;
-      if constexpr (!GROUPED) srow = rsum[row];
+    for (int j = 0; j < WN; ++j) {
+      const int lc = block_col(j) - (n0 + wn * WC);
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int col = lane_col + 32 * j;
-        if (col >= N) continue;
-        float v;
-        if constexpr (GROUPED) v = tot[i][j][r];
-        else v = fmaf(s[j], acc[i][j][r], q[j] * srow);
-        v += bcol[j];
-        const int64_t idx = row * N + col;
-        if (x3) v += act_to_f32<BF16>(x3[idx]);
-        out[idx] = f32_to_act<BF16>(v);
+      for (int r = 0; r < 16; ++r)
+        E[acc_row(r, lane) * EP + lc] = GROUPED ? tot[i][j][r] : acc[i][j][r];
+    }
+#pragma unroll
+    for (int p = 0; p < 32 / RowsPerPass; ++p) {
+      const int er = p * RowsPerPass + lane / LanesPerRow;
+      const int64_t grow = m0 + wm * (32 * WM) + 32 * i + er;
+      const f32x4_t v0 = *(const f32x4_t*)(E + er * EP + ecol);
+      const f32x4_t v1 = *(const f32x4_t*)(E + er * EP + ecol + 4);
+      if (grow >= M || !col_ok) continue;
+      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      float sr = 0.f;
+      if constexpr (!GROUPED) sr = srow[wm * (32 * WM) + 32 * i + er];
+      const int64_t idx = grow * N + gcol;
+      u32x4_t xv = u32x4_t{0, 0, 0, 0};
+      if (x3) xv = *(const u32x4_t*)(x3 + idx);
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float y0 = v[e], y1 = v[e + 1];
+        if constexpr (!GROUPED) {
+          y0 = fmaf(cs[e], y0, cq[e] * sr);
+          y1 = fmaf(cs[e + 1], y1, cq[e + 1] * sr);
+        }
+        y0 += cb[e];
+        y1 += cb[e + 1];
+        if (x3) {
+          y0 += act_to_f32<BF16>((uint16_t)(xv[e >> 1] & 0xffffu));
+          y1 += act_to_f32<BF16>((uint16_t)(xv[e >> 1] >> 16));
+        }
+        o[e >> 1] = (uint32_t)f32_to_act<BF16>(y0) | ((uint32_t)f32_to_act<BF16>(y1) << 16);
       }
+      *(u32x4_t*)(out + idx) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
   }
 }
 
-template <bool BF16, bool W4, int WM, int WN, bool GROUPED>
+template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
 hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
-  using T = AqTile<WM, WN>;
+  using T = Tile<W4, GM, GN, WM, WN>;
   AqArgs a = a0;
-  a.tiles_m = (int)((a.m + T::BM - 1) / T::BM);
+  a.tiles_m = (int)((a.m + 255) / 256);
   a.tiles_n = (a.n + T::BN - 1) / T::BN;
-  const size_t lds = 2 * (size_t)T::Stage * sizeof(uint16_t);
-  auto kern = aq_gemm_kernel<BF16, W4, WM, WN, GROUPED>;
+  const size_t lds = (size_t)T::Total;
+  auto kern = aq_gemm_kernel<BF16, W4, GM, GN, WM, WN, GROUPED>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(T::Threads), lds, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Per-tensor / per-channel: 256 x 256 workgroup tiles (128 x 128 per wave).
-// Per-group: the group rescale needs a second accumulator set, so 256 x 128 tiles.
-hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream) {
-  const bool grouped = a.grouped;
-  if (a.bf16) {
-    if (a.w4) return grouped ? launch_one<true, true, 4, 2, true>(a, stream)
-                             : launch_one<true, true, 4, 4, false>(a, stream);
-    return grouped ? launch_one<true, false, 4, 2, true>(a, stream)
-                   : launch_one<true, false, 4, 4, false>(a, stream);
+// Tile configurations (wave grid GM x GN, blocks per wave WM x WN).  The matrix cores and
+// the VALU hardly overlap on gfx950, and one wave per SIMD leaves LDS latency exposed, so
+// the defaults run two waves per SIMD.  Index 0 is the default of each mode; the others
+// are kept for tuning.
+//   per-tensor / per-channel: 0: 2x4 waves of 128x64   1: 1x8 of 256x32   2: 1x4 of 256x64
+//                             3: 2x2 of 128x128         4: 4x2 of 64x128
+//   per-group:                0: 4x2 waves of 64x64     1: 2x2 of 128x64
+//                             2: 8x1 of 32x64 (int8)
+template <bool BF16, bool W4>
+hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
+  if (a.grouped) {
+    switch (a.tile) {
+      case 1: return launch_one<BF16, W4, 2, 2, 4, 2, true>(a, stream);
+      case 2:
+        if constexpr (!W4) return launch_one<BF16, W4, 8, 1, 1, 2, true>(a, stream);
+        else return launch_one<BF16, W4, 4, 2, 2, 2, true>(a, stream);
+      default: return launch_one<BF16, W4, 4, 2, 2, 2, true>(a, stream);
+    }
   }
-  if (a.w4) return grouped ? launch_one<false, true, 4, 2, true>(a, stream)
-                           : launch_one<false, true, 4, 4, false>(a, stream);
-  return grouped ? launch_one<false, false, 4, 2, true>(a, stream)
-                 : launch_one<false, false, 4, 4, false>(a, stream);
+  switch (a.tile) {
+    case 1:
+      if constexpr (!W4) return launch_one<BF16, W4, 1, 8, 8, 1, false>(a, stream);
+      else return launch_one<BF16, W4, 2, 4, 4, 2, false>(a, stream);
+    case 2: return launch_one<BF16, W4, 1, 4, 8, 2, false>(a, stream);
+    case 3: return launch_one<BF16, W4, 2, 2, 4, 4, false>(a, stream);
+    case 4: return launch_one<BF16, W4, 4, 2, 2, 4, false>(a, stream);
+    default: return launch_one<BF16, W4, 2, 4, 4, 2, false>(a, stream);
+  }
+}
+
+hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.w4 ? launch_mode<true, true>(a, stream) : launch_mode<true, false>(a, stream);
+  return a.w4 ? launch_mode<false, true>(a, stream) : launch_mode<false, false>(a, stream);
 }
 
 }  // namespace wq

@@ -33,33 +33,6 @@ struct SmTile {
   static constexpr int LanesPerRow = RowBytes / 16;
 };
 
-// 8 int4 k-values of two adjacent columns (from a tr8 read: byte j = row k0 + j) -> the
-// 16-bit images of the even column and of the odd column, each as 4 dwords of k pairs.
-template <bool BF16>
-__device__ __forceinline__ void i4_kpairs(u32x2_t d, u32x4_t& even, u32x4_t& odd) {
-  const uint32_t mag = BF16 ? 0x43004300u : 0x64006400u;
-  uint32_t ev[4], od[4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t u = d[h] ^ 0x88888888u;
-    const uint32_t e = u & 0x0f0f0f0fu, o = (u >> 4) & 0x0f0f0f0fu;
-    ev[2 * h] = __builtin_amdgcn_perm(e, e, 0x0c010c00u) | mag;
-    ev[2 * h + 1] = __builtin_amdgcn_perm(e, e, 0x0c030c02u) | mag;
-    od[2 * h] = __builtin_amdgcn_perm(o, o, 0x0c010c00u) | mag;
-    od[2 * h + 1] = __builtin_amdgcn_perm(o, o, 0x0c030c02u) | mag;
-  }
-  if (!BF16) {
-    const f16x2_t k = {(_Float16)1032.0f, (_Float16)1032.0f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ev[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, ev[q]) - k);
-      od[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, od[q]) - k);
-    }
-  }
-  even = u32x4_t{ev[0], ev[1], ev[2], ev[3]};
-  odd = u32x4_t{od[0], od[1], od[2], od[3]};
-}
-
 template <bool BF16, bool W4, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) {
   using T = SmTile<W4>;
@@ -174,15 +147,7 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
           acc[2 * p] = mfma32x32x16<BF16>(af[kk], ev, acc[2 * p]);
           acc[2 * p + 1] = mfma32x32x16<BF16>(af[kk], od, acc[2 * p + 1]);
         } else {
-          uint32_t o[4];
-          if constexpr (BF16) {
-            i8x4_to_bf16(d[0], o[0], o[1]);
-            i8x4_to_bf16(d[1], o[2], o[3]);
-          } else {
-            i8x4_to_f16(d[0], o[0], o[1]);
-            i8x4_to_f16(d[1], o[2], o[3]);
-          }
-          acc[p] = mfma32x32x16<BF16>(af[kk], u32x4_t{o[0], o[1], o[2], o[3]}, acc[p]);
+          acc[p] = mfma32x32x16<BF16>(af[kk], i8x8_to_act<BF16>(d), acc[p]);
         }
       }
       if constexpr (GROUPED) {

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstdlib>
 
 #include "wq_kernels.h"
 #include "wq_problem.h"
@@ -36,10 +37,10 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
     pl.empty_k = true;
     return pl;
   }
-  pl.mp = aq_rowsum_mp(p.m);
-  pl.rowsum_bytes = align_up(p.groups * pl.mp * (int64_t)sizeof(float));
   pl.small_m = p.m <= kSmallM;
+  pl.mp = aq_rowsum_mp(p.m);
   if (pl.small_m) {
+    pl.rowsum_bytes = align_up(p.groups * pl.mp * (int64_t)sizeof(float));
     pl.splits = aq_smallm_splits(p.m, (int)p.k, (int)p.n, (int)p.group, p.mode == QuantMode::kGroup);
     pl.partial_bytes = align_up((int64_t)pl.splits * p.m * p.n * (int64_t)sizeof(float));
   }
@@ -47,9 +48,19 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
   return pl;
 }
 
+// Tuning knob: WQ_AQ_TILE selects a non-default tile configuration of the large-m
+// anti-quant kernel.  Read once per process; never consulted on the launch path itself.
+int tile_override() {
+  static const int v = [] {
+    const char* e = std::getenv("WQ_AQ_TILE");
+    return e ? std::atoi(e) : 0;
+  }();
+  return v;
+}
+
 float code_bias(const AntiquantProblem& p) {
-  if (p.act == WQ_F16) return 0.f;
-  return p.w4 ? 136.f : 128.f;  // bf16 images are code + C (see wq_device.h)
+  // bf16 images of int4 codes are code + 136 (see wq_device.h); all other images are exact
+  return (p.act == WQ_BF16 && p.w4) ? 136.f : 0.f;
 }
 
 }  // namespace
@@ -95,6 +106,7 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.code_bias = wq::code_bias(p);
   a.splits = pl.splits;
   a.mp = pl.mp;
+  a.tile = wq::tile_override();
 
   hipError_t e;
   if (pl.empty_k) {
@@ -103,9 +115,13 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   }
   a.rowsum = (const float*)workspace;
   a.partial = pl.small_m ? (float*)((char*)workspace + pl.rowsum_bytes) : nullptr;
-  e = wq::launch_aq_rowsum(a, s);
-  if (e != hipSuccess) return WQ_ERR_RUNTIME;
-  e = pl.small_m ? wq::launch_aq_smallm(a, s) : wq::launch_aq_gemm(a, s);
+  if (pl.small_m) {
+    e = wq::launch_aq_rowsum(a, s);
+    if (e != hipSuccess) return WQ_ERR_RUNTIME;
+    e = wq::launch_aq_smallm(a, s);
+  } else {
+    e = wq::launch_aq_gemm(a, s);  // row sums are formed in-kernel
+  }
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
 }
 

@@ -9,6 +9,7 @@ namespace wq {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
@@ -48,53 +49,121 @@ __device__ __forceinline__ uint16_t f32_to_act(float f) {
 
 // ----------------------------------------------------------------------------- code images
 // Every int8 and int4 weight code is exact in fp16 and in bf16.  The conversions below turn
-// packed codes into 16-bit floating images, two per dword, in column order along n.
-// The bf16 images are biased by a constant C (the fed value is code + C); the kernels
-// remove C exactly in fp32 through the offset term.  fp16 images are the codes themselves.
+// packed codes into 16-bit floating images, two per dword, in the byte order of the input
+// (consecutive k after a tr8 transpose read).  bf16 images of int4 codes are biased by a
+// constant C = 136 (the fed value is code + C); the kernels remove C exactly in fp32
+// through the offset term.  All other images are the codes themselves.
 
-// 4 int8 codes (one dword, columns c..c+3) -> bf16 images of code + 128.
+// 4 int8 codes (one dword) -> two dwords of bf16 images.  The signed byte -> fp32
+// conversion is one instruction (v_cvt_f32_i32 with a sign-extended byte operand), and an
+// integer of magnitude <= 128 is exact in bf16, i.e. the top half of its fp32 pattern.
 __device__ __forceinline__ void i8x4_to_bf16(uint32_t d, uint32_t& lo, uint32_t& hi) {
-  const uint32_t u = d ^ 0x80808080u;  // two's complement -> code + 128 in [0, 255]
-  const float f0 = (float)(u & 0xffu), f1 = (float)((u >> 8) & 0xffu);
-  const float f2 = (float)((u >> 16) & 0xffu), f3 = (float)(u >> 24);
-  // an integer below 256 is exact in bf16, i.e. the top half of its fp32 pattern
+  const float f0 = (float)(int8_t)(d), f1 = (float)(int8_t)(d >> 8);
+  const float f2 = (float)(int8_t)(d >> 16), f3 = (float)(int8_t)(d >> 24);
   lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
 }
-constexpr float kBf16Int8Bias = 128.0f;
 
 // 4 int8 codes -> fp16 images of the codes (exact).  0x64xx is 1024 + xx in fp16.
 __device__ __forceinline__ void i8x4_to_f16(uint32_t d, uint32_t& lo, uint32_t& hi) {
-  const uint32_t u = d ^ 0x80808080u;
+  const uint32_t u = d ^ 0x80808080u;                      // code + 128 in [0, 255]
   const uint32_t m = 0x64646464u;
-  uint32_t a = __builtin_amdgcn_perm(m, u, 0x04010400u);  // [u0, 0x64, u1, 0x64]
-  uint32_t b = __builtin_amdgcn_perm(m, u, 0x04030402u);  // [u2, 0x64, u3, 0x64]
-  const f16x2_t k = {(_Float16)1152.0f, (_Float16)1152.0f};  // 1024 + 128
+  const uint32_t a = __builtin_amdgcn_perm(m, u, 0x04010400u);  // [u0, 0x64, u1, 0x64]
+  const uint32_t b = __builtin_amdgcn_perm(m, u, 0x04030402u);  // [u2, 0x64, u3, 0x64]
+  const f16x2_t k = {(_Float16)1152.0f, (_Float16)1152.0f};   // 1024 + 128
   lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) - k);
   hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, b) - k);
 }
 
-// 8 int4 codes (one dword, columns c..c+7, even column in the low nibble) -> 4 dwords of
-// 16-bit images.  bf16: 0x43xx is 128 + xx, so the image is code + 136.  fp16: the code.
+// 8 int8 codes of one column, consecutive k (a tr8 read) -> an MFMA B fragment.
 template <bool BF16>
-__device__ __forceinline__ void i4x8_to_act(uint32_t d, uint32_t out[4]) {
-  const uint32_t u = d ^ 0x88888888u;          // nibble -> code + 8 in [0, 15]
-  const uint32_t e = u & 0x0f0f0f0fu;          // columns c, c+2, c+4, c+6
-  const uint32_t o = (u >> 4) & 0x0f0f0f0fu;   // columns c+1, c+3, c+5, c+7
-  const uint32_t mag = BF16 ? 0x43004300u : 0x64006400u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
-    out[j] = __builtin_amdgcn_perm(o, e, sel) | mag;   // [e_j, 0, o_j, 0] | magic
+__device__ __forceinline__ u32x4_t i8x8_to_act(u32x2_t d) {
+  uint32_t o[4];
+  if constexpr (BF16) {
+    i8x4_to_bf16(d[0], o[0], o[1]);
+    i8x4_to_bf16(d[1], o[2], o[3]);
+  } else {
+    i8x4_to_f16(d[0], o[0], o[1]);
+    i8x4_to_f16(d[1], o[2], o[3]);
   }
-  if (!BF16) {
-    const f16x2_t k = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      out[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, out[j]) - k);
-  }
+  return u32x4_t{o[0], o[1], o[2], o[3]};
 }
-constexpr float kBf16Int4Bias = 136.0f;
+
+// 8 bytes of packed int4 (two adjacent columns, consecutive k: a tr8 read of a packed
+// tile) -> the MFMA B fragments of the even column and of the odd column.
+// bf16: 0x43 0x0n is 128 + n, so the image is code + 136; fp16: 0x64 0x0n is 1024 + n,
+// and subtracting 1032 leaves the code.
+template <bool BF16>
+__device__ __forceinline__ void i4_kpairs(u32x2_t d, u32x4_t& even, u32x4_t& odd) {
+  const uint32_t mag = BF16 ? 0x43434343u : 0x64646464u;
+  uint32_t ev[4], od[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t u = d[h] ^ 0x88888888u;             // nibble -> code + 8 in [0, 15]
+    const uint32_t e = u & 0x0f0f0f0fu, o = (u >> 4) & 0x0f0f0f0fu;
+    ev[2 * h] = __builtin_amdgcn_perm(mag, e, 0x04010400u);      // [e0, M, e1, M]
+    ev[2 * h + 1] = __builtin_amdgcn_perm(mag, e, 0x04030402u);  // [e2, M, e3, M]
+    od[2 * h] = __builtin_amdgcn_perm(mag, o, 0x04010400u);
+    od[2 * h + 1] = __builtin_amdgcn_perm(mag, o, 0x04030402u);
+  }
+  if constexpr (!BF16) {
+    const f16x2_t k = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ev[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, ev[q]) - k);
+      od[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, od[q]) - k);
+    }
+  }
+  even = u32x4_t{ev[0], ev[1], ev[2], ev[3]};
+  odd = u32x4_t{od[0], od[1], od[2], od[3]};
+}
+
+// row sums: a * 1 + b * 1 + c for a dword of two 16-bit activations
+template <bool BF16>
+__device__ __forceinline__ float dot2_ones(uint32_t v, float c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v),
+                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), c, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, v),
+                                  __builtin_bit_cast(f16x2_t, 0x3c003c00u), c, false);
+}
+
+// ----------------------------------------------------------------------------- LDS DMA
+// Buffer resource (4 dwords, kept in SGPRs): base, stride 0, num_records bytes.  Accesses
+// at or past num_records read zero, so it doubles as the bounds check of every tile load.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  const uint64_t b = (uint64_t)base;
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)n), 0x00020000u};
+}
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every resource: the load reads 0
+
+// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes land at lds_block + 16*l.
+// Written as a self-contained asm statement: it has no register result (the data goes to
+// LDS), and the caller accounts for it with an explicit vmcnt wait before the barrier that
+// publishes the stage.  M0 carries the LDS base (saved and restored around the load, as
+// the compiler owns M0); one wait state separates the M0 write from the load.
+__device__ __forceinline__ void dma16(const u32x4_t& rsrc, const void* lds_block, uint32_t voff) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(WQ_LDS const void*)lds_block;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding, then join the
+// workgroup barrier.  The memory clobber keeps the compiler from moving LDS accesses
+// across it; no other wait is implied.
+#define WQ_STAGE_BARRIER(n) asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory")
 
 // ----------------------------------------------------------------------------- MFMA
 template <bool BF16>

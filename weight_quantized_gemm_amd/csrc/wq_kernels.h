@@ -23,6 +23,7 @@ struct AqArgs {
   int32_t groups;        // parameter rows (1 unless per-group)
   int32_t splits;        // k splits (small-m path)
   int32_t tiles_m, tiles_n;
+  int32_t tile;          // tile configuration index (0 = default)
   float code_bias;       // C: the fed weight image is code + C
   bool bf16, w4, grouped, per_tensor;
 };
