@@ -262,6 +262,30 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
     }
   };
 
+  // ---------------------------------------------------------------- epilogue geometry
+  // The epilogue moves 8 consecutive columns of one row per lane.  Its x3 rows are
+  // prefetched into registers while the last k-step's MFMAs run (two 32-row bands ahead).
+  constexpr int EP = WC + 8;            // fp32 pitch of the staging rows (bank spread)
+  constexpr int LanesPerRow = WC / 8;
+  constexpr int RowsPerPass = 64 / LanesPerRow;
+  constexpr int kPasses = 32 / RowsPerPass;
+  const int ecol = 8 * (lane % LanesPerRow);
+  const int gcol = n0 + wn * WC + ecol;   // first of this lane's 8 output columns
+  const bool col_ok = gcol < N;
+  const uint16_t* __restrict__ x3 = (const uint16_t*)a.x3;
+  // bands of x3 held in registers ahead of use: one where the accumulators leave little room
+  constexpr int XP = (!GROUPED && WM * WN >= 8) ? 1 : 2;
+  u32x4_t xpre[XP][kPasses];
+  auto prefetch_x3 = [&](int i, int slot) {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int er = p * RowsPerPass + lane / LanesPerRow;
+      const int64_t grow = m0 + wm * (32 * WM) + 32 * i + er;
+      xpre[slot][p] = (x3 && col_ok && grow < M) ? *(const u32x4_t*)(x3 + grow * N + gcol)
+                                                 : u32x4_t{0, 0, 0, 0};
+    }
+  };
+
   // ---------------------------------------------------------------- main loop
   issue(0);
   if (nk > 1) issue(1);
@@ -274,6 +298,10 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
       stage_barrier<0>();
     }
     if (ks + 2 < nk) issue(ks + 2);
+    if (ks == nk - 1) {  // no DMA left: start the epilogue's x3 reads under the last MFMAs
+      prefetch_x3(0, 0);
+      if (XP > 1 && WM > 1) prefetch_x3(1, 1 % XP);
+    }
 
     const uint8_t* As = smem + (ks % kStages) * T::Stage;
     const uint8_t* Bs = As + kAbytes;
@@ -339,16 +367,9 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
   }
   // Each wave stages one 32-row band of its tile at a time in its own LDS region, then
   // moves 8 consecutive columns per lane with 16-byte accesses.
-  constexpr int EP = WC + 8;            // fp32 pitch of the staging rows (bank spread)
   float* E = (float*)smem + wave * (32 * EP);
   const uint16_t* __restrict__ bias = (const uint16_t*)a.bias;
-  const uint16_t* __restrict__ x3 = (const uint16_t*)a.x3;
   uint16_t* __restrict__ out = (uint16_t*)a.out;
-  constexpr int LanesPerRow = WC / 8;
-  constexpr int RowsPerPass = 64 / LanesPerRow;
-  const int ecol = 8 * (lane % LanesPerRow);
-  const int gcol = n0 + wn * WC + ecol;   // first of this lane's 8 output columns
-  const bool col_ok = gcol < N;
   // per-column parameters of this lane's 8 columns
   float cs[8], cq[8], cb[8];
 #pragma unroll
@@ -389,9 +410,10 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
         E[acc_row(r, lane) * EP + lc] = GROUPED ? tot[i][j][r] : acc[i][j][r];
     }
 #pragma unroll
-    for (int p = 0; p < 32 / RowsPerPass; ++p) {
+    for (int p = 0; p < kPasses; ++p) {
       const int er = p * RowsPerPass + lane / LanesPerRow;
       const int64_t grow = m0 + wm * (32 * WM) + 32 * i + er;
+      const u32x4_t xv = xpre[i % XP][p];
       const f32x4_t v0 = *(const f32x4_t*)(E + er * EP + ecol);
       const f32x4_t v1 = *(const f32x4_t*)(E + er * EP + ecol + 4);
       if (grow >= M || !col_ok) continue;
@@ -399,8 +421,6 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
       float sr = 0.f;
       if constexpr (!GROUPED) sr = srow[wm * (32 * WM) + 32 * i + er];
       const int64_t idx = grow * N + gcol;
-      u32x4_t xv = u32x4_t{0, 0, 0, 0};
-      if (x3) xv = *(const u32x4_t*)(x3 + idx);
       uint32_t o[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -419,6 +439,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
       }
       *(u32x4_t*)(out + idx) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
+    if (i + XP < WM) prefetch_x3(i + XP, i % XP);
   }
 }
 

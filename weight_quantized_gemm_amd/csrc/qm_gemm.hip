@@ -5,83 +5,87 @@
 // ("aclnnQuantMatmulAllReduceV2", section Function, formula case 2; case 1 has no pertoken).
 //
 // int8 x int8 products accumulate exactly in int32 on the matrix cores
-// (v_mfma_i32_32x32x32_i8); bias joins the int32 accumulator before any scaling; the
-// scaling and x3 run in fp32 in the epilogue and the result is rounded once to the output
-// dtype.  The int32 accumulator (with bias) can be stored as well.
+// (v_mfma_i32_32x32x32_i8); bias joins the int32 accumulator before any scaling (two's
+// complement wrap past the int32 range); scaling and x3 run in fp32 in the epilogue and the
+// result is rounded once to the output dtype.  The int32 accumulator (with bias) can be
+// stored as well.
 //
-// Tiling: 256 threads = 4 waves in a 2 x 2 grid, 128 x 128 per wave (4 x 4 MFMA blocks),
-// 256 x 256 per workgroup, BK = 128, double-buffered in LDS.
-//   * x1 tile row-major, pitch 144 B; A fragments (16 consecutive k of one row) by 16-byte
-//     reads;
-//   * x2 tile row-major (n-contiguous), pitch 288 B; B fragments (16 consecutive k of one
-//     column) by two tr8 transpose reads.
-#include "wq_device.h"
+// Pipeline: 8 waves (2 x 4, two per SIMD), wave tile 128 x 64, workgroup tile 256 x 256,
+// BK = 64.  x1 and x2 tiles move global -> LDS by direct-to-LDS buffer loads through a
+// 4-stage ring (three stages in flight), one barrier per k-step.  x1 rows (64 bytes) are
+// read as MFMA A fragments by 16-byte loads; x2 rows (256 bytes, n-contiguous) give B
+// fragments by two tr8 transpose reads (16 consecutive k of one column).  The epilogue
+// stages the accumulators through LDS so that x3, the output and the int32 accumulator
+// move in 16-byte row-contiguous accesses.
 #include "wq_kernels.h"
+#include "wq_pipeline.h"
 
 namespace wq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kApitch = kBK + 16;   // bytes
-constexpr int kBpitch = kBN + 32;   // bytes
-constexpr int kAbytes = kBM * kApitch;
-constexpr int kBbytes = kBK * kBpitch;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kStages = 4;
+constexpr int kRA = kBK;                        // bytes per x1 row in a stage
+constexpr int kRB = kBN;                        // bytes per x2 row in a stage
+constexpr int kAbytes = kBM * kRA;              // 16 KiB
+constexpr int kBbytes = kBK * kRB;              // 16 KiB
 constexpr int kStage = kAbytes + kBbytes;
-constexpr int kWM = 4, kWN = 4;
+constexpr int kLds = kStages * kStage;          // 128 KiB
 
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  int t = bid;
-  if ((total & 7) == 0) t = (bid & 7) * (total >> 3) + (bid >> 3);
-  constexpr int kGroupM = 4;
-  const int per_group = kGroupM * tiles_n;
-  const int g = t / per_group;
-  const int first_m = g * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int r = t - g * per_group;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
-
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 1) void qm_gemm_kernel(const QmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+// Wave grid GM x GN with WM x WN 32x32 blocks per wave (256 x 256 per workgroup).
+template <bool OUT_BF16, int kGM, int kGN>
+__global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs a) {
+  constexpr int kWaves = kGM * kGN;
+  constexpr int kWM = 8 / kGM, kWN = 8 / kGN;
+  constexpr int kAper = kAbytes / 1024 / kWaves;  // DMA blocks per wave
+  constexpr int kBper = kBbytes / 1024 / kWaves;
+  constexpr int kDma = kAper + kBper;             // DMA loads per wave per stage
+  static_assert(kAper >= 1 && kBper >= 1, "DMA split");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kGN, wn = wave % kGN;
   int tm, tn;
   tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * kBM;
   const int n0 = tn * kBN;
   const int64_t M = a.m;
   const int K = a.k, N = a.n;
+  const int nk = (K + kBK - 1) / kBK;
 
-  // staging: x1 256 rows x 128 B = 2048 chunks; x2 128 rows x 256 B = 2048 chunks
-  const int a_chunk = tid & 7, a_row0 = tid >> 3;     // rows a_row0 + 32*i
-  const int b_chunk = tid & 15, b_row0 = tid >> 4;    // rows b_row0 + 16*i
-  u32x4_t ra[8], rb[8];
-  auto load_tiles = [&](int k0) {
+  // ------------------------------------------------------------------ DMA issue
+  const uint8_t* x1b = (const uint8_t*)a.x1 + m0 * K;
+  const int64_t x1_bytes = (M - m0) * K;
+  const uint8_t* x2b = (const uint8_t*)a.x2 + n0;
+  uint32_t a_off[kAper];
+  int a_chunk[kAper];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t row = m0 + a_row0 + 32 * i;
-      const int kk = k0 + 16 * a_chunk;
-      ra[i] = (row < M && kk < K) ? *(const u32x4_t*)(a.x1 + row * K + kk) : u32x4_t{0, 0, 0, 0};
-    }
+  for (int j = 0; j < kAper; ++j) {
+    const int b = wave + kWaves * j;                 // 16 rows of 64 bytes
+    const int r = 16 * b + (lane >> 2);
+    a_chunk[j] = row_slot<kRA>(r, lane & 3);         // logical chunk in this physical slot
+    a_off[j] = (uint32_t)(r * K + 16 * a_chunk[j]);
+  }
+  uint32_t b_off[kBper];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kr = k0 + b_row0 + 16 * i;
-      const int col = n0 + 16 * b_chunk;
-      rb[i] = (kr < K && col < N) ? *(const u32x4_t*)(a.x2 + (int64_t)kr * N + col)
-                                  : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto store_tiles = [&](int stage) {
-    uint8_t* As = smem + stage * kStage;
-    uint8_t* Bs = As + kAbytes;
+  for (int j = 0; j < kBper; ++j) {
+    const int b = wave + kWaves * j;                 // 4 rows of 256 bytes
+    const int r = 4 * b + (lane >> 4);
+    const int p = lane & 15;
+    b_off[j] = (uint32_t)(r * N + 16 * (2 * pair_slot<kRB>(r, p >> 1) + (p & 1)));
+  }
+  auto issue = [&](int ks) {
+    uint8_t* st = smem + (ks % kStages) * kStage;
+    const int k0 = ks * kBK;
+    const u32x4_t ra = make_rsrc(x1b + k0, x1_bytes - k0);
+    const bool tail = k0 + kBK > K;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4_t*)(As + (a_row0 + 32 * i) * kApitch + 16 * a_chunk) = ra[i];
+    for (int j = 0; j < kAper; ++j)
+      dma16(ra, st + 1024 * (wave + kWaves * j),
+            (tail && k0 + 16 * a_chunk[j] >= K) ? kOOB : a_off[j]);
+    const u32x4_t rb = make_rsrc(x2b + (int64_t)k0 * N, (int64_t)(K - k0) * N - n0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4_t*)(Bs + (b_row0 + 16 * i) * kBpitch + 16 * b_chunk) = rb[i];
+    for (int j = 0; j < kBper; ++j) dma16(rb, st + kAbytes + 1024 * (wave + kWaves * j), b_off[j]);
   };
 
   i32x16_t acc[kWM][kWN];
@@ -90,30 +94,61 @@ __global__ __launch_bounds__(kThreads, 1) void qm_gemm_kernel(const QmArgs a) {
 #pragma unroll
     for (int j = 0; j < kWN; ++j) acc[i][j] = i32x16_t{};
 
-  const int nk = (K + kBK - 1) / kBK;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
+  // ------------------------------------------------------------------ epilogue geometry
+  // The epilogue moves 8 consecutive columns of one row per lane.  Its x3 rows are
+  // prefetched into registers while the last k-step's MFMAs run (two 32-row bands ahead).
+  constexpr int WC = 32 * kWN;          // wave columns
+  constexpr int EP = WC + 8;            // int32 pitch of the staging rows
+  constexpr int LanesPerRow = WC / 8;   // lanes per row, 8 columns each
+  constexpr int RowsPerPass = 64 / LanesPerRow;
+  constexpr int kPasses = 32 / RowsPerPass;
+  const int ecol = 8 * (lane % LanesPerRow);
+  const int gcol = n0 + wn * WC + ecol;
+  const bool col_ok = gcol < N;
+  const uint16_t* x3 = (const uint16_t*)a.x3;
+  u32x4_t xpre[2][kPasses];
+  auto prefetch_x3 = [&](int i, int slot) {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int er = p * RowsPerPass + lane / LanesPerRow;
+      const int64_t grow = m0 + wm * (32 * kWM) + 32 * i + er;
+      xpre[slot][p] = (x3 && col_ok && grow < M) ? *(const u32x4_t*)(x3 + grow * N + gcol)
+                                                 : u32x4_t{0, 0, 0, 0};
+    }
+  };
+
+  // ------------------------------------------------------------------ main loop
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
   for (int ks = 0; ks < nk; ++ks) {
-    const int stage = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) load_tiles((ks + 1) * kBK);
-    const uint8_t* As = smem + stage * kStage;
+    const int ahead = min(kStages - 2, nk - 1 - ks);  // stages issued after stage ks
+    if (ahead == 2) stage_barrier<2 * kDma>();
+    else if (ahead == 1) stage_barrier<kDma>();
+    else stage_barrier<0>();
+    if (ks + kStages - 1 < nk) issue(ks + kStages - 1);
+    if (ks == nk - 1) {  // no DMA left: start the epilogue's x3 reads under the last MFMAs
+      prefetch_x3(0, 0);
+      if (kWM > 1) prefetch_x3(1, 1);
+    }
+
+    const uint8_t* As = smem + (ks % kStages) * kStage;
     const uint8_t* Bs = As + kAbytes;
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
       u32x4_t af[kWM], bfr[kWN];
 #pragma unroll
       for (int i = 0; i < kWM; ++i) {
-        const int row = wm * 128 + 32 * i + (lane & 31);
-        af[i] = *(const u32x4_t*)(As + row * kApitch + 32 * kk + 16 * (lane >> 5));
+        const int r = wm * (32 * kWM) + 32 * i + (lane & 31);
+        af[i] = *(const u32x4_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + (lane >> 5)));
       }
+      const int kr = 32 * kk + 16 * (lane >> 5) + ((lane & 15) >> 1);
 #pragma unroll
       for (int j = 0; j < kWN; ++j) {
-        const int kr = 32 * kk + 16 * (lane >> 5) + ((lane & 15) >> 1);
-        const int nc = wn * 128 + 32 * j + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-        const u32x2_t lo = lds_read_tr8(Bs + kr * kBpitch + nc);
-        const u32x2_t hi = lds_read_tr8(Bs + (kr + 8) * kBpitch + nc);
+        const int pair = wn * kWN + j;
+        const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+        const u32x2_t lo = lds_read_tr8(Bs + kr * kRB + 32 * pair_slot<kRB>(kr, pair) + sub);
+        const u32x2_t hi = lds_read_tr8(Bs + (kr + 8) * kRB + 32 * pair_slot<kRB>(kr + 8, pair) + sub);
         bfr[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
       }
 #pragma unroll
@@ -121,45 +156,69 @@ __global__ __launch_bounds__(kThreads, 1) void qm_gemm_kernel(const QmArgs a) {
 #pragma unroll
         for (int j = 0; j < kWN; ++j) acc[i][j] = mfma32x32x32_i8(af[i], bfr[j], acc[i][j]);
     }
-    if (more) store_tiles(stage ^ 1);
-    __syncthreads();
   }
 
-  // epilogue: int32 (acc + bias), then fp32 dq[n] * pt[m] * acc + x3[m, n], rounded once
-  const int lane_col = n0 + wn * 128 + (lane & 31);
-  const int64_t wave_row0 = m0 + wm * 128;
-  int32_t bcol[kWN];
-  float dq[kWN];
+  // ------------------------------------------------------------------ epilogue
+  __syncthreads();
+  int32_t* E = (int32_t*)smem + wave * (32 * EP);
+  int32_t cb[8];
+  float cdq[8];
 #pragma unroll
-  for (int j = 0; j < kWN; ++j) {
-    const int col = lane_col + 32 * j;
-    const bool ok = col < N;
-    bcol[j] = (ok && a.bias) ? a.bias[col] : 0;
-    const int dc = a.dq_per_tensor ? 0 : col;
-    dq[j] = !ok ? 0.f
-                : (a.dq_bf16 ? bf16_bits_to_f32(((const uint16_t*)a.dq)[dc]) : ((const float*)a.dq)[dc]);
+  for (int e = 0; e < 8; ++e) { cb[e] = 0; cdq[e] = 0.f; }
+  if (col_ok) {
+    if (a.bias) {
+      const i32x4_t b0 = *(const i32x4_t*)(a.bias + gcol), b1 = *(const i32x4_t*)(a.bias + gcol + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { cb[e] = b0[e]; cb[e + 4] = b1[e]; }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int dc = a.dq_per_tensor ? 0 : gcol + e;
+      cdq[e] = a.dq_bf16 ? bf16_bits_to_f32(((const uint16_t*)a.dq)[dc]) : ((const float*)a.dq)[dc];
+    }
   }
-  const uint16_t* x3 = (const uint16_t*)a.x3;
   uint16_t* out = (uint16_t*)a.out;
 #pragma unroll
   for (int i = 0; i < kWM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = wave_row0 + 32 * i + acc_row(r, lane);
-      if (row >= M) continue;
-      const float pt = a.pt ? a.pt[row] : 1.f;
+    for (int j = 0; j < kWN; ++j)
 #pragma unroll
-      for (int j = 0; j < kWN; ++j) {
-        const int col = lane_col + 32 * j;
-        if (col >= N) continue;
-        const int32_t v = (int32_t)((uint32_t)acc[i][j][r] + (uint32_t)bcol[j]);  // wraps
-        const int64_t idx = row * N + col;
-        if (a.acc_out) a.acc_out[idx] = v;
-        float y = (float)v * dq[j] * pt;
-        if (x3) y += OUT_BF16 ? bf16_bits_to_f32(x3[idx]) : f16_bits_to_f32(x3[idx]);
-        out[idx] = OUT_BF16 ? f32_to_bf16_rne(y) : f32_to_f16_rne(y);
+      for (int r = 0; r < 16; ++r) E[acc_row(r, lane) * EP + 32 * j + (lane & 31)] = acc[i][j][r];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int er = p * RowsPerPass + lane / LanesPerRow;
+      const int64_t grow = m0 + wm * (32 * kWM) + 32 * i + er;
+      const u32x4_t xv = xpre[i & 1][p];
+      const i32x4_t v0 = *(const i32x4_t*)(E + er * EP + ecol);
+      const i32x4_t v1 = *(const i32x4_t*)(E + er * EP + ecol + 4);
+      if (grow >= M || !col_ok) continue;
+      int32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = (int32_t)((uint32_t)v0[e] + (uint32_t)cb[e]);
+        v[e + 4] = (int32_t)((uint32_t)v1[e] + (uint32_t)cb[e + 4]);
       }
+      const int64_t idx = grow * N + gcol;
+      if (a.acc_out) {
+        *(i32x4_t*)(a.acc_out + idx) = i32x4_t{v[0], v[1], v[2], v[3]};
+        *(i32x4_t*)(a.acc_out + idx + 4) = i32x4_t{v[4], v[5], v[6], v[7]};
+      }
+      const float pt = a.pt ? a.pt[grow] : 1.f;
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float y0 = (float)v[e] * cdq[e] * pt, y1 = (float)v[e + 1] * cdq[e + 1] * pt;
+        if (x3) {
+          const uint32_t xw = xv[e >> 1];
+          y0 += OUT_BF16 ? bf16_bits_to_f32(xw & 0xffffu) : f16_bits_to_f32(xw & 0xffffu);
+          y1 += OUT_BF16 ? bf16_bits_to_f32(xw >> 16) : f16_bits_to_f32(xw >> 16);
+        }
+        o[e >> 1] = (uint32_t)(OUT_BF16 ? f32_to_bf16_rne(y0) : f32_to_f16_rne(y0)) |
+                    ((uint32_t)(OUT_BF16 ? f32_to_bf16_rne(y1) : f32_to_f16_rne(y1)) << 16);
+      }
+      *(u32x4_t*)(out + idx) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
+    if (i + 2 < kWM) prefetch_x3(i + 2, i & 1);
   }
 }
 
@@ -169,12 +228,14 @@ hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   QmArgs a = a0;
   a.tiles_m = (int)((a.m + kBM - 1) / kBM);
   a.tiles_n = (a.n + kBN - 1) / kBN;
-  const size_t lds = 2 * (size_t)kStage;
-  auto kern = a.out_bf16 ? qm_gemm_kernel<true> : qm_gemm_kernel<false>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // default: 2 x 4 waves of 128 x 64 (two per SIMD); tuning tile 1: 2 x 2 waves of 128 x 128
+  auto kern = a.tile == 1 ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2> : qm_gemm_kernel<false, 2, 2>)
+                          : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4> : qm_gemm_kernel<false, 2, 4>);
+  const int threads = a.tile == 1 ? 256 : 512;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), (size_t)kLds, stream, a);
   return hipGetLastError();
 }
 

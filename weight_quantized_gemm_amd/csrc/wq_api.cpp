@@ -49,7 +49,7 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
 }
 
 // Tuning knob: WQ_AQ_TILE selects a non-default tile configuration of the large-m
-// anti-quant kernel.  Read once per process; never consulted on the launch path itself.
+// kernels.  Read once per process; never consulted on the launch path itself.
 int tile_override() {
   static const int v = [] {
     const char* e = std::getenv("WQ_AQ_TILE");
@@ -155,6 +155,7 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
   a.m = p.m; a.k = (int32_t)p.k; a.n = (int32_t)p.n;
   a.out_bf16 = p.out_dtype == WQ_BF16; a.dq_bf16 = p.dq_dtype == WQ_BF16;
   a.dq_per_tensor = p.dq_per_tensor;
+  a.tile = wq::tile_override();
   hipError_t e = wq::launch_qm_gemm(a, (hipStream_t)stream);
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
 }

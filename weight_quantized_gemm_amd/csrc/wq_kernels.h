@@ -41,6 +41,7 @@ struct QmArgs {
   int64_t m;
   int32_t k, n;
   int32_t tiles_m, tiles_n;
+  int32_t tile;          // tile configuration index (0 = default)
   bool out_bf16, dq_bf16, dq_per_tensor;
 };
 
