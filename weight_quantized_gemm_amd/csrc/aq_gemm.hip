@@ -13,7 +13,9 @@
 // matrix cores see only exact 16-bit images of the integer codes and x1; scale and offset
 // are applied in fp32 on the accumulators, per group at each group end, or once in the
 // epilogue for per-tensor / per-channel parameters.  S_g is summed in-kernel from the x1
-// fragments (v_dot2 against ones).
+// fragments (v_dot2 against ones).  Per-group scale and offset rows travel with the
+// weight tile of the k-step in which their group ends, so a fold reads them from LDS and
+// never waits on a global load (which would also wait for every stage in flight).
 //
 // Pipeline: GM x GN waves, wave tile (32*WM) x (32*WN), workgroup tile 256 x (32*WN*GN),
 // BK = 64.  Operands travel global -> LDS by direct-to-LDS buffer loads
@@ -24,8 +26,8 @@
 // one column per lane) and are turned into exact 16-bit images in registers.  The
 // epilogue stages fp32 results through LDS so that x3, bias and the output move in
 // 16-byte row-contiguous accesses.
-#include "wq_device.h"
 #include "wq_kernels.h"
+#include "wq_pipeline.h"
 
 namespace wq {
 namespace {
@@ -35,7 +37,7 @@ constexpr int kStages = 3;
 constexpr int kArow = 128;                 // bytes per x1 row in a stage (64 x 16-bit)
 constexpr int kAbytes = 256 * kArow;       // 32 KiB: 256 rows of x1
 
-template <bool W4, int GM, int GN, int WM, int WN>
+template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
 struct Tile {
   static constexpr int Waves = GM * GN;              // wave grid GM x GN
   static constexpr int Threads = 64 * Waves;
@@ -43,7 +45,8 @@ struct Tile {
   static constexpr int BN = 32 * WN * GN;            // logical columns
   static constexpr int RB = W4 ? BN / 2 : BN;        // weight bytes per k row
   static constexpr int Bbytes = kBK * RB;
-  static constexpr int Stage = kAbytes + Bbytes;
+  static constexpr int Pbytes = GROUPED ? 1024 : 0;  // per-group scale / offset rows
+  static constexpr int Stage = kAbytes + Bbytes + Pbytes;
   static constexpr int Win = 256 / RB;               // k rows per 256-byte bank window
   static constexpr int PairMask = 8 / Win - 1;       // swizzle span of 32-byte pairs
   static constexpr int RowsPerKB = 1024 / RB;        // k rows per 1 KiB DMA block
@@ -53,9 +56,10 @@ struct Tile {
   // weights: Bblocks spread over the first Bblocks waves when there are fewer blocks
   static constexpr int Bper = Bblocks >= Waves ? Bblocks / Waves : 1;
   static constexpr int Bwaves = Bblocks >= Waves ? Waves : Bblocks;
+  static constexpr int Pwave = Waves - 1;            // issues the group-parameter loads
   static constexpr int WCols = 32 * WN;              // logical columns per wave
   static constexpr int Reads = W4 ? WN / 2 : WN;     // tr8 reads per wave per 16-k step
-  // LDS layout: stages | S rows (BM fp32) | per-wave group-sum scratch (Waves x 32*WM fp32)
+  // LDS layout: stages (x1 | weights | group parameters) | S rows (BM fp32) | per-wave group-sum scratch (Waves x 32*WM fp32)
   static constexpr int SOff = kStages * Stage;
   static constexpr int GOff = SOff + BM * 4;
   static constexpr int Total = GOff + Waves * 32 * WM * 4;
@@ -65,44 +69,6 @@ struct Tile {
   static_assert(Win >= 1 && Win <= 4, "weight row bytes 64..256");
   static_assert(!W4 || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
 };
-
-// x1 tile swizzle: 16-byte chunk c of row r lives in slot c ^ ((r >> 1) & 7), so that 16
-// consecutive rows read at the same chunk hit 16 distinct bank groups.
-__device__ __forceinline__ int a_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
-
-// weight tile swizzle: 32-byte pair p of k row r lives in pair p ^ ((r / Win) & PairMask),
-// so that the 8 rows of a tr8 read land in 8 distinct bank groups.
-template <class T>
-__device__ __forceinline__ int b_pair(int r, int pair) { return pair ^ ((r / T::Win) & T::PairMask); }
-
-
-// vmcnt(N) then the workgroup barrier (N is the per-wave count of loads allowed in flight)
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-  if constexpr (N == 0) WQ_STAGE_BARRIER(0);
-  else if constexpr (N == 4) WQ_STAGE_BARRIER(4);
-  else if constexpr (N == 5) WQ_STAGE_BARRIER(5);
-  else if constexpr (N == 6) WQ_STAGE_BARRIER(6);
-  else if constexpr (N == 8) WQ_STAGE_BARRIER(8);
-  else if constexpr (N == 9) WQ_STAGE_BARRIER(9);
-  else if constexpr (N == 10) WQ_STAGE_BARRIER(10);
-  else if constexpr (N == 12) WQ_STAGE_BARRIER(12);
-  else static_assert(N < 0, "add this vmcnt value");
-}
-
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  int t = bid;
-  if ((total & 7) == 0) t = (bid & 7) * (total >> 3) + (bid >> 3);  // XCD-contiguous bands
-  constexpr int kGroupM = 4;
-  const int per_group = kGroupM * tiles_n;
-  const int g = t / per_group;
-  const int first_m = g * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int r = t - g * per_group;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
 
 // One 16-k step of MFMA operands for a wave: WM x1 fragments (16-byte reads) and the raw
 // weight bytes of its tr8 reads.
@@ -119,20 +85,20 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
   for (int i = 0; i < WM; ++i) {
     const int r = wm * (32 * WM) + 32 * i + (lane & 31);
     const int c = 2 * kk + (lane >> 5);
-    f.a[i] = *(const u32x4_t*)(As + r * kArow + 16 * a_slot(r, c));
+    f.a[i] = *(const u32x4_t*)(As + r * kArow + 16 * row_slot<kArow>(r, c));
   }
   const int kr = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 1);
 #pragma unroll
   for (int j = 0; j < T::Reads; ++j) {
     const int pair = wn * T::Reads + j;  // 32-byte pair within the weight row
-    const int off = kr * T::RB + 32 * b_pair<T>(kr, pair) + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    const int off = kr * T::RB + 32 * pair_slot<T::RB>(kr, pair) + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
     f.raw[j] = lds_read_tr8(Bs + off);
   }
 }
 
 template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
 __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a) {
-  using T = Tile<W4, GM, GN, WM, WN>;
+  using T = Tile<W4, GM, GN, WM, WN, GROUPED>;
   constexpr int BN = T::BN, RB = T::RB, WC = T::WCols;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -162,7 +128,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
   for (int j = 0; j < T::Aper; ++j) {
     const int b = wave + T::Waves * j;
     const int r = 8 * b + (lane >> 3);
-    a_chunk[j] = a_slot(r, lane & 7);  // logical chunk held by this physical slot
+    a_chunk[j] = row_slot<kArow>(r, lane & 7);  // logical chunk held by this physical slot
     a_off[j] = (uint32_t)(r * K * 2 + 16 * a_chunk[j]);
   }
   uint32_t b_off[T::Bper];
@@ -171,7 +137,15 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
     const int b = wave + T::Waves * j;
     const int r = T::RowsPerKB * b + lane / (RB / 16);
     const int p = lane % (RB / 16);
-    b_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * b_pair<T>(r, p >> 1) + (p & 1)));
+    b_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * pair_slot<RB>(r, p >> 1) + (p & 1)));
+  }
+  // per-group parameters: buffer resources over scale / offset from column n0 on
+  const bool has_offset = a.offset != nullptr;
+  u32x4_t rsc{}, rof{};
+  if constexpr (GROUPED) {
+    const int64_t pbytes = ((int64_t)a.groups * N - n0) * 2;
+    rsc = make_rsrc((const uint8_t*)a.scale + 2 * (int64_t)n0, pbytes);
+    rof = has_offset ? make_rsrc((const uint8_t*)a.offset + 2 * (int64_t)n0, pbytes) : rsc;
   }
   auto issue = [&](int ks) {
     uint8_t* st = smem + (ks % kStages) * T::Stage;
@@ -183,12 +157,22 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
       const uint32_t off = (tail && k0 + 8 * a_chunk[j] >= K) ? kOOB : a_off[j];
       dma16(ra, st + 1024 * (wave + T::Waves * j), off);
     }
+    if constexpr (GROUPED) {
+      if (wave == T::Pwave) {
+        const int ga = min((k0 + 31) / a.group, a.groups - 1);
+        const int gb = min((k0 + 63) / a.group, a.groups - 1);
+        dma_group_params<BN>(st + kAbytes + T::Bbytes, rsc, rof, has_offset, ga, gb, N, lane);
+      }
+    }
     if (wave >= T::Bwaves) return;
     const u32x4_t rb = make_rsrc(x2b + (int64_t)k0 * x2_pitch, (int64_t)(K - k0) * x2_pitch - nb0);
 #pragma unroll
     for (int j = 0; j < T::Bper; ++j)
       dma16(rb, st + kAbytes + 1024 * (wave + T::Waves * j), b_off[j]);
   };
+  // loads this wave issues per stage
+  constexpr int kOwnA = T::Aper, kOwnB = T::Bper, kOwnP = GROUPED ? 2 : 0;
+  const bool has_b = wave < T::Bwaves, has_p = GROUPED && wave == T::Pwave;
 
   // ---------------------------------------------------------------- accumulators
   f32x16_t acc[WM][WN];
@@ -218,6 +202,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
   const uint16_t* __restrict__ scale = (const uint16_t*)a.scale;
   const uint16_t* __restrict__ offset = (const uint16_t*)a.offset;
   const float cbias = a.code_bias;
+  (void)has_offset;
   float* gscr = (float*)(smem + T::GOff) + wave * (32 * WM);  // this wave's S_g scratch
 
   // logical column of lane's block j (int4: block 2p + e covers byte pair p, parity e)
@@ -226,8 +211,9 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
     else return n0 + wn * WC + 32 * j + (lane & 31);
   };
 
-  // fold group g: tot += s * acc + s * (off - C) * S_g
-  auto rescale = [&](int g) {
+  // fold the group that ends at row 32 (e = 0) or 64 (e = 1) of the k-step whose
+  // parameter rows are at Ps: tot += s * acc + s * (off - C) * S_g
+  auto rescale = [&](const uint16_t* Ps, int e) {
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       const float t = ssum[i] + __shfl_xor(ssum[i], 32, 64);
@@ -237,10 +223,9 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
     float s[WN], q[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      const int col = block_col(j);
-      const bool ok = col < N;
-      const float sv = ok ? act_to_f32<BF16>(scale[(int64_t)g * N + col]) : 0.f;
-      const float ov = (ok && offset) ? act_to_f32<BF16>(offset[(int64_t)g * N + col]) : 0.f;
+      const int lc = block_col(j) - n0;
+      const float sv = act_to_f32<BF16>(Ps[e * BN + lc]);
+      const float ov = act_to_f32<BF16>(Ps[256 + e * BN + lc]);
       s[j] = sv;
       q[j] = sv * (ov - cbias);
     }
@@ -291,12 +276,11 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
   if (nk > 1) issue(1);
   for (int ks = 0; ks < nk; ++ks) {
     // stage ks is complete once only the next stage's loads may still be in flight
-    if (ks + 1 < nk) {
-      if (wave < T::Bwaves) stage_barrier<T::Aper + T::Bper>();
-      else stage_barrier<T::Aper>();
-    } else {
-      stage_barrier<0>();
-    }
+    if (ks + 1 == nk) stage_barrier<0>();
+    else if (has_b && has_p) stage_barrier<kOwnA + kOwnB + kOwnP>();
+    else if (has_b) stage_barrier<kOwnA + kOwnB>();
+    else if (has_p) stage_barrier<kOwnA + kOwnP>();
+    else stage_barrier<kOwnA>();
     if (ks + 2 < nk) issue(ks + 2);
     if (ks == nk - 1) {  // no DMA left: start the epilogue's x3 reads under the last MFMAs
       prefetch_x3(0, 0);
@@ -348,7 +332,8 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
       if constexpr (GROUPED) {
         if (kk & 1) {  // groups end on multiples of 32
           const int kdone = ks * kBK + kk * 16 + 16;
-          if (kdone <= K && (kdone % a.group == 0 || kdone == K)) rescale((kdone - 1) / a.group);
+          if (kdone <= K && (kdone % a.group == 0 || kdone == K))
+            rescale((const uint16_t*)(Bs + T::Bbytes), kk >> 1);
         }
       }
     }
@@ -445,7 +430,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 
 template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
 hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
-  using T = Tile<W4, GM, GN, WM, WN>;
+  using T = Tile<W4, GM, GN, WM, WN, GROUPED>;
   AqArgs a = a0;
   a.tiles_m = (int)((a.m + 255) / 256);
   a.tiles_n = (a.n + T::BN - 1) / T::BN;

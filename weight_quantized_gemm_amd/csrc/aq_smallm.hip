@@ -5,90 +5,110 @@
 // ("CANN ops-transformer ... aclnnWeightQuantMatmulAllReduce 完全指南", section 计算公式),
 // evaluated in the same factored form as the large-m kernel (aq_gemm.hip).
 //
-// Work split: a workgroup owns a 128-column slab of x2 and a contiguous range of k (split-k);
-// its 4 waves take the 64-row blocks of that range round-robin.  Each wave streams its
-// block (global -> registers -> wave-private LDS, row-major int8 / packed int4), reads MFMA
-// B fragments back with tr8 transpose reads (8 consecutive k of one column per lane),
-// turns them into exact 16-bit images and runs 32x32x16 MFMAs against the 32 rows of x1.
-// Per-group parameters are folded at every group end; a group cut by the end of a wave's
-// block is folded with its scale only, and its offset term is added once, by the block
-// that holds the group's end.  The 4 waves are reduced through LDS in a fixed order, the
-// splits by a finishing kernel in a fixed order: results are deterministic.
-#include "wq_device.h"
+// Work split: a workgroup owns a 128-column slab of x2 and a contiguous k range (split-k).
+// Its 8 waves (two per SIMD, so that one wave's LDS, matrix-core and VALU latencies hide
+// behind the other's work) take 64-row units of the range round-robin.  Each wave streams
+// its 32-row blocks -- weights, the matching 32 x 32 slice of x1 and, per-group, the
+// block's scale / offset row -- into its own 3-stage LDS ring with direct-to-LDS loads (no
+// barriers; vmcnt waits only), reads B fragments with tr8 transpose reads, converts them to
+// exact 16-bit images and runs 32x32x16 MFMAs.  Row sums of x1 come from the A fragments
+// (v_dot2).  Per-group parameters are applied at each group end and at each unit end: the
+// fold is linear in the accumulators and row sums, so a group split between waves or
+// workgroups is folded piecewise with its own scale and offset.  The 8 waves are reduced
+// through LDS in a fixed order and the splits by a finishing kernel in a fixed order:
+// results are deterministic.
 #include "wq_kernels.h"
+#include "wq_pipeline.h"
 
 namespace wq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kSlab = 128;   // logical columns per workgroup
-constexpr int kRows = 64;    // k rows per wave block
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSlab = 128;    // logical columns per workgroup
+constexpr int kRows = 32;     // k rows per block
+constexpr int kUnit = 64;     // k rows per work unit (blocks of one unit run back to back)
+constexpr int kStages = 3;    // blocks in flight per wave
 
-template <bool W4>
+template <bool W4, bool GROUPED>
 struct SmTile {
-  static constexpr int RowBytes = W4 ? kSlab / 2 : kSlab;   // 64 or 128 bytes per k row
-  static constexpr int Pitch = RowBytes + 32;                // 96 or 160: tr8 bank spread
-  static constexpr int Buf = kRows * Pitch;                  // bytes of the wave's LDS tile
-  static constexpr int Loads = kRows * RowBytes / 16 / 64;   // 16-byte loads per lane
-  static constexpr int LanesPerRow = RowBytes / 16;
+  static constexpr int RB = W4 ? kSlab / 2 : kSlab;   // weight bytes per k row
+  static constexpr int Wbytes = kRows * RB;           // 4 or 2 KiB
+  static constexpr int Xbytes = 32 * kRows * 2;       // 2 KiB of x1 (32 rows x 32 k)
+  static constexpr int Pbytes = GROUPED ? 512 : 0;    // the block's scale / offset row
+  static constexpr int Stage = Wbytes + Xbytes + Pbytes;
+  static constexpr int WDma = Wbytes / 1024;
+  static constexpr int XDma = Xbytes / 1024;
+  static constexpr int Dma = WDma + XDma + (GROUPED ? 2 : 0);  // loads per block
+  static constexpr int Ring = kStages * Stage;        // per wave
+  static constexpr int Red = kWaves * 32 * kSlab * 4; // wave reduction buffer
+  static constexpr int Body = kWaves * Ring > Red ? kWaves * Ring : Red;
+  static constexpr int GOff = Body;                   // per-wave group row-sum scratch
+  static constexpr int SOff = GOff + kWaves * 32 * 4; // per-wave row sums (per-channel)
+  static constexpr int Lds = SOff + kWaves * 32 * 4;
+  static_assert(Lds <= 160 * 1024, "one workgroup per CU");
+  static_assert(2 * Dma <= 63, "vmcnt range");
 };
 
 template <bool BF16, bool W4, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) {
-  using T = SmTile<W4>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * T::Buf > 4 * 32 * kSlab * 4
-                                                            ? 4 * T::Buf
-                                                            : 4 * 32 * kSlab * 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slab = blockIdx.x, split = blockIdx.y;
-  const int n0 = slab * kSlab;
-  const int K = a.k, N = a.n;
-  const int M = (int)a.m;
-  const int kchunk = ((K + a.splits - 1) / a.splits + kRows - 1) / kRows * kRows;
-  const int kbeg = split * kchunk;
-  const int kend = min(K, kbeg + kchunk);
-  const int nblocks = kend > kbeg ? (kend - kbeg + kRows - 1) / kRows : 0;
+  using T = SmTile<W4, GROUPED>;
+  constexpr int RB = T::RB;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * kSlab, split = blockIdx.y;
+  const int K = a.k, N = a.n, M = (int)a.m;
+  const int kbeg = split * a.kchunk;
+  const int kend = min(K, kbeg + a.kchunk);
+  constexpr int bpu = kUnit / kRows;                      // blocks per unit
+  const int nunits = kend > kbeg ? (kend - kbeg + kUnit - 1) / kUnit : 0;
+  // this wave's blocks: units wave, wave + 8, ...; the blocks of a unit in order
+  const int my_units = wave < nunits ? (nunits - wave + kWaves - 1) / kWaves : 0;
+  auto block_k0 = [&](int t) { return kbeg + (wave + kWaves * (t / bpu)) * kUnit + (t % bpu) * kRows; };
+  int nb = my_units * bpu;
+  while (nb > 0 && block_k0(nb - 1) >= kend) --nb;         // a trailing block past the range
 
-  const uint16_t* __restrict__ x1 = (const uint16_t*)a.x1;
-  const uint8_t* __restrict__ x2 = (const uint8_t*)a.x2;
   const int64_t x2_pitch = W4 ? (N >> 1) : N;
-  // One LDS tile per wave suffices: a wave's LDS instructions execute in issue order, so
-  // the transpose reads of block b complete before the stores of block b + 4 land.
-  uint8_t* wbuf = smem + wave * T::Buf;
+  const int nb0 = W4 ? n0 / 2 : n0;
+  uint8_t* ring = smem + wave * T::Ring;
 
-  // ---- per-lane load pattern: LanesPerRow lanes cover one k row of the slab
-  const int l_row = lane / T::LanesPerRow;
-  const int l_byte = 16 * (lane % T::LanesPerRow);
-  constexpr int kRowsPerLoad = 64 / T::LanesPerRow;
-  const int col_bytes0 = (W4 ? n0 / 2 : n0) + l_byte;
-  const bool col_ok = (W4 ? 2 * col_bytes0 : col_bytes0) < N;
-
-  // two register sets: blocks b and b + 4 are in flight while block b - 4 is computed
-  u32x4_t rb[2][T::Loads];
-  u32x4_t ra[2][4];
-  auto load_block = [&](int set, int blk) {
-    const int k0 = kbeg + blk * kRows;
+  // per-lane DMA offsets inside a block
+  uint32_t w_off[T::WDma];
 #pragma unroll
-    for (int q = 0; q < T::Loads; ++q) {
-      const int kr = k0 + l_row + kRowsPerLoad * q;
-      rb[set][q] = (kr < kend && col_ok) ? *(const u32x4_t*)(x2 + (int64_t)kr * x2_pitch + col_bytes0)
-                                         : u32x4_t{0, 0, 0, 0};
-    }
-    const int arow = lane & 31;
+  for (int j = 0; j < T::WDma; ++j) {
+    const int r = (1024 / RB) * j + lane / (RB / 16);
+    const int p = lane % (RB / 16);
+    w_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * pair_slot<RB>(r, p >> 1) + (p & 1)));
+  }
+  uint32_t x_off[T::XDma];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int kc = k0 + 16 * kk + 8 * (lane >> 5);
-      ra[set][kk] = (arow < M && kc < kend) ? *(const u32x4_t*)(x1 + (int64_t)arow * K + kc)
-                                            : u32x4_t{0, 0, 0, 0};
-    }
+  for (int j = 0; j < T::XDma; ++j) {
+    const int r = 16 * j + (lane >> 2);
+    x_off[j] = (uint32_t)(r * K * 2 + 16 * row_slot<64>(r, lane & 3));
+  }
+  const bool has_offset = a.offset != nullptr;
+  u32x4_t rsc{}, rof{};
+  if constexpr (GROUPED) {
+    const int64_t pbytes = ((int64_t)a.groups * N - n0) * 2;
+    rsc = make_rsrc((const uint8_t*)a.scale + 2 * (int64_t)n0, pbytes);
+    rof = has_offset ? make_rsrc((const uint8_t*)a.offset + 2 * (int64_t)n0, pbytes) : rsc;
+  }
+  auto issue = [&](int t) {
+    uint8_t* st = ring + (t % kStages) * T::Stage;
+    const int k0 = block_k0(t);
+    const u32x4_t rw = make_rsrc((const uint8_t*)a.x2 + (int64_t)k0 * x2_pitch + nb0,
+                                 (int64_t)(kend - k0) * x2_pitch - nb0);
+#pragma unroll
+    for (int j = 0; j < T::WDma; ++j) dma16(rw, st + 1024 * j, w_off[j]);
+    // blocks never straddle kend (both are multiples of 32): only rows >= m read zeros
+    const u32x4_t rx = make_rsrc((const uint8_t*)a.x1 + (int64_t)k0 * 2, (int64_t)M * K * 2 - (int64_t)k0 * 2);
+#pragma unroll
+    for (int j = 0; j < T::XDma; ++j) dma16(rx, st + T::Wbytes + 1024 * j, x_off[j]);
+    if constexpr (GROUPED)
+      dma_group_row<kSlab>(st + T::Wbytes + T::Xbytes, rsc, rof, has_offset, k0 / a.group, N, lane);
   };
-  auto store_block = [&](int set) {
-#pragma unroll
-    for (int q = 0; q < T::Loads; ++q)
-      *(u32x4_t*)(wbuf + (l_row + kRowsPerLoad * q) * T::Pitch + l_byte) = rb[set][q];
-  };
 
-  // accumulators: 4 blocks of 32 columns (int4: byte-column pair p, parity e -> block 2p+e)
   f32x16_t acc[4], tot[GROUPED ? 4 : 1];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x16_t{};
@@ -96,31 +116,33 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
 #pragma unroll
     for (int j = 0; j < 4; ++j) tot[j] = f32x16_t{};
   }
-  // logical column of this lane in block j
+  float ssum = 0.f;  // row sum of x1 (row lane % 32, k half lane / 32)
+  // logical column of this lane in block j (int4: byte pair p = j >> 1, parity j & 1)
   auto block_col = [&](int j) -> int {
     if constexpr (W4) return n0 + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
     else return n0 + 32 * j + (lane & 31);
   };
-
-  const uint16_t* __restrict__ scale = (const uint16_t*)a.scale;
-  const uint16_t* __restrict__ offset = (const uint16_t*)a.offset;
   const float cbias = a.code_bias;
-  // fold the running group g: tot += s*acc (+ s*(off-C)*S_g when the group ends here)
-  auto fold = [&](int g, bool group_end) {
+  float* gscr = (float*)(smem + T::GOff) + wave * 32;
+
+  // fold the accumulators of the current group with the group's parameter rows at Ps:
+  // tot += s * acc + s * (off - C) * S, S the row sums since the last fold
+  auto fold = [&](const uint16_t* Ps) {
+    const float t = ssum + __shfl_xor(ssum, 32, 64);
+    if (lane < 32) gscr[lane] = t;
+    ssum = 0.f;
     float s[4], q[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int col = block_col(j);
-      const bool ok = col < N;
-      const float sv = ok ? act_to_f32<BF16>(scale[(int64_t)g * N + col]) : 0.f;
-      const float ov = (ok && offset) ? act_to_f32<BF16>(offset[(int64_t)g * N + col]) : 0.f;
+      const int lc = block_col(j) - n0;
+      const float sv = act_to_f32<BF16>(Ps[lc]);
+      const float ov = act_to_f32<BF16>(Ps[128 + lc]);
       s[j] = sv;
-      q[j] = group_end ? sv * (ov - cbias) : 0.f;
+      q[j] = sv * (ov - cbias);
     }
-    const float* sg = a.rowsum + (int64_t)g * a.mp;
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const f32x4_t sr = *(const f32x4_t*)(sg + 8 * rq + 4 * (lane >> 5));
+      const f32x4_t sr = *(const f32x4_t*)(gscr + 8 * rq + 4 * (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -131,80 +153,86 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
     for (int j = 0; j < 4; ++j) acc[j] = f32x16_t{};
   };
 
-  // compute one block from the wave's LDS tile (already stored) with x1 fragments af
-  auto compute_block = [&](const u32x4_t* af, int blk) {
-    const int k0 = kbeg + blk * kRows;
+  // ------------------------------------------------------------------ stream
+  for (int t = 0; t < nb && t < kStages; ++t) issue(t);
+  for (int t = 0; t < nb; ++t) {
+    const int ahead = min(kStages - 1, nb - 1 - t);  // blocks issued after block t
+    if (ahead == 2) wave_wait<2 * T::Dma>();
+    else if (ahead == 1) wave_wait<T::Dma>();
+    else wave_wait<0>();
+    const uint8_t* W = ring + (t % kStages) * T::Stage;
+    const uint8_t* X = W + T::Wbytes;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int row = kk * 16 + 8 * (lane >> 5) + ((lane & 15) >> 1);
+    for (int kk = 0; kk < kRows / 16; ++kk) {
+      const int r = lane & 31;
+      const u32x4_t af = *(const u32x4_t*)(X + r * 64 + 16 * row_slot<64>(r, 2 * kk + (lane >> 5)));
+      const int kr = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 1);
+      const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 #pragma unroll
       for (int p = 0; p < (W4 ? 2 : 4); ++p) {
-        const int cb = 32 * p + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-        const u32x2_t d = lds_read_tr8(wbuf + row * T::Pitch + cb);
+        const u32x2_t d = lds_read_tr8(W + kr * RB + 32 * pair_slot<RB>(kr, p) + sub);
         if constexpr (W4) {
           u32x4_t ev, od;
           i4_kpairs<BF16>(d, ev, od);
-          acc[2 * p] = mfma32x32x16<BF16>(af[kk], ev, acc[2 * p]);
-          acc[2 * p + 1] = mfma32x32x16<BF16>(af[kk], od, acc[2 * p + 1]);
+          acc[2 * p] = mfma32x32x16<BF16>(af, ev, acc[2 * p]);
+          acc[2 * p + 1] = mfma32x32x16<BF16>(af, od, acc[2 * p + 1]);
         } else {
-          acc[p] = mfma32x32x16<BF16>(af[kk], i8x8_to_act<BF16>(d), acc[p]);
+          acc[p] = mfma32x32x16<BF16>(af, i8x8_to_act<BF16>(d), acc[p]);
         }
       }
-      if constexpr (GROUPED) {
-        if (kk & 1) {  // groups end on multiples of 32
-          const int kdone = k0 + 16 * kk + 16;
-          const bool ends = kdone <= kend && (kdone % a.group == 0 || kdone == K);
-          const bool last = kdone >= min(kend, k0 + kRows);  // end of this block
-          if (ends) fold((kdone - 1) / a.group, true);
-          else if (last) fold((min(kdone, kend) - 1) / a.group, false);
-        }
-      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ssum = dot2_ones<BF16>(af[q], ssum);
     }
-  };
-
-  // ---- stream this wave's blocks: wave, wave + 4, ... with two blocks in flight
-  int blk = wave;
-  if (blk < nblocks) load_block(0, blk);
-  if (blk + 4 < nblocks) load_block(1, blk + 4);
-  while (blk < nblocks) {
-    store_block(0);
-    const u32x4_t a0[4] = {ra[0][0], ra[0][1], ra[0][2], ra[0][3]};
-    if (blk + 8 < nblocks) load_block(0, blk + 8);
-    compute_block(a0, blk);
-    blk += 4;
-    if (blk >= nblocks) break;
-    store_block(1);
-    const u32x4_t a1[4] = {ra[1][0], ra[1][1], ra[1][2], ra[1][3]};
-    if (blk + 8 < nblocks) load_block(1, blk + 8);
-    compute_block(a1, blk);
-    blk += 4;
+    if constexpr (GROUPED) {
+      // fold at a group end, and wherever the wave's next block does not continue this one
+      const int kdone = block_k0(t) + kRows;
+      if (kdone % a.group == 0 || kdone == kend || t % bpu == bpu - 1 || t == nb - 1)
+        fold((const uint16_t*)(X + T::Xbytes));
+    }
+    // refill the slot of block t: its LDS reads must have completed first, since the
+    // direct-to-LDS writes land whenever their data returns
+    if (t + kStages < nb) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(t + kStages);
+    }
   }
 
-  // ---- reduce the 4 waves in a fixed order, write this split's partial [split][m][n]
+  // ------------------------------------------------------------------ wave reduction
   __syncthreads();
-  float* red = (float*)smem;  // [4][32][kSlab]
+  float* red = (float*)smem;  // [kWaves][32][kSlab]
+  float* sred = (float*)(smem + T::SOff);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int lc = block_col(j) - n0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = acc_row(r, lane);
-      red[(wave * 32 + row) * kSlab + lc] = GROUPED ? tot[j][r] : acc[j][r];
-    }
+    for (int r = 0; r < 16; ++r) red[(wave * 32 + acc_row(r, lane)) * kSlab + lc] = GROUPED ? tot[j][r] : acc[j][r];
+  }
+  if constexpr (!GROUPED) {
+    const float t = ssum + __shfl_xor(ssum, 32, 64);
+    if (lane < 32) sred[wave * 32 + lane] = t;
   }
   __syncthreads();
   float* part = a.partial + (int64_t)split * a.m * N;
   for (int o = tid; o < 32 * kSlab; o += kThreads) {
     const int row = o / kSlab, lc = o % kSlab;
     if (row >= M || n0 + lc >= N) continue;
-    const float v = red[(0 * 32 + row) * kSlab + lc] + red[(1 * 32 + row) * kSlab + lc] +
-                    red[(2 * 32 + row) * kSlab + lc] + red[(3 * 32 + row) * kSlab + lc];
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += red[(w * 32 + row) * kSlab + lc];
     part[(int64_t)row * N + n0 + lc] = v;
+  }
+  if constexpr (!GROUPED) {
+    if (blockIdx.x == 0 && tid < M) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += sred[w * 32 + tid];
+      a.rowsum_part[(int64_t)split * a.m + tid] = v;
+    }
   }
 }
 
 // out = [s*P + s*(off-C)*S]  (per-tensor / per-channel)  or  T (per-group), + bias + x3,
-// where P / T is the sum of the split partials in split order.
+// where P / T and S are the sums of the split partials in split order.
 template <bool BF16, bool GROUPED>
 __global__ __launch_bounds__(256) void aq_smallm_finish(const AqArgs a) {
   const int64_t total = a.m * a.n;
@@ -221,10 +249,12 @@ __global__ __launch_bounds__(256) void aq_smallm_finish(const AqArgs a) {
     float v = 0.f;
     for (int s = 0; s < a.splits; ++s) v += a.partial[(int64_t)s * total + i];
     if constexpr (!GROUPED) {
+      float srow = 0.f;
+      for (int s = 0; s < a.splits; ++s) srow += a.rowsum_part[(int64_t)s * a.m + row];
       const int pc = a.per_tensor ? 0 : col;
       const float sv = act_to_f32<BF16>(scale[pc]);
       const float ov = offset ? act_to_f32<BF16>(offset[pc]) : 0.f;
-      v = fmaf(sv, v, sv * (ov - a.code_bias) * a.rowsum[row]);
+      v = fmaf(sv, v, sv * (ov - a.code_bias) * srow);
     }
     if (bias) v += act_to_f32<BF16>(bias[col]);
     if (x3) v += act_to_f32<BF16>(x3[i]);
@@ -234,10 +264,13 @@ __global__ __launch_bounds__(256) void aq_smallm_finish(const AqArgs a) {
 
 template <bool BF16, bool W4, bool GROUPED>
 hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
+  using T = SmTile<W4, GROUPED>;
   const int slabs = (a.n + kSlab - 1) / kSlab;
-  hipLaunchKernelGGL((aq_smallm_kernel<BF16, W4, GROUPED>), dim3(slabs, a.splits), dim3(kThreads),
-                     0, stream, a);
-  hipError_t e = hipGetLastError();
+  auto kern = aq_smallm_kernel<BF16, W4, GROUPED>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::Lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(slabs, a.splits), dim3(kThreads), (size_t)T::Lds, stream, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = a.m * a.n;
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 4096));
@@ -248,12 +281,17 @@ hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int aq_smallm_splits(int64_t m, int k, int n, int group, bool grouped) {
+SmallmPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped) {
   (void)m; (void)group; (void)grouped;
+  SmallmPlan p;
   const int slabs = (n + kSlab - 1) / kSlab;
-  int splits = std::max(1, 256 / std::max(1, slabs));  // about one workgroup per CU
-  const int max_splits = std::max(1, (k + 4 * kRows - 1) / (4 * kRows));  // >= 4 blocks per split
-  return std::min(splits, max_splits);
+  const int want = std::max(1, 256 / std::max(1, slabs));  // about one workgroup per CU
+  // whole units per split, a multiple of kWaves units when the range allows (balance)
+  const int per = (k + want - 1) / want;
+  const int step = per >= kWaves * kUnit ? kWaves * kUnit : kUnit;
+  p.kchunk = std::max(kUnit, (per + step - 1) / step * step);
+  p.splits = std::max(1, (k + p.kchunk - 1) / p.kchunk);
+  return p;
 }
 
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream) {

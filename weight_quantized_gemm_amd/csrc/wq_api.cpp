@@ -24,10 +24,9 @@ constexpr int64_t kSmallM = 32;
 struct AqPlan {
   bool empty_k = false;
   bool small_m = false;
-  int splits = 1;
-  int64_t mp = 0;
-  int64_t rowsum_bytes = 0;
+  SmallmPlan sm;
   int64_t partial_bytes = 0;
+  int64_t rowsum_bytes = 0;
   int64_t workspace = 0;
 };
 
@@ -38,13 +37,13 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
     return pl;
   }
   pl.small_m = p.m <= kSmallM;
-  pl.mp = aq_rowsum_mp(p.m);
   if (pl.small_m) {
-    pl.rowsum_bytes = align_up(p.groups * pl.mp * (int64_t)sizeof(float));
-    pl.splits = aq_smallm_splits(p.m, (int)p.k, (int)p.n, (int)p.group, p.mode == QuantMode::kGroup);
-    pl.partial_bytes = align_up((int64_t)pl.splits * p.m * p.n * (int64_t)sizeof(float));
+    const bool grouped = p.mode == QuantMode::kGroup;
+    pl.sm = aq_smallm_plan(p.m, (int)p.k, (int)p.n, (int)p.group, grouped);
+    pl.partial_bytes = align_up((int64_t)pl.sm.splits * p.m * p.n * (int64_t)sizeof(float));
+    pl.rowsum_bytes = grouped ? 0 : align_up((int64_t)pl.sm.splits * p.m * (int64_t)sizeof(float));
   }
-  pl.workspace = pl.rowsum_bytes + pl.partial_bytes;
+  pl.workspace = pl.partial_bytes + pl.rowsum_bytes;
   return pl;
 }
 
@@ -104,8 +103,8 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.grouped = p.mode == wq::QuantMode::kGroup;
   a.per_tensor = p.mode == wq::QuantMode::kTensor;
   a.code_bias = wq::code_bias(p);
-  a.splits = pl.splits;
-  a.mp = pl.mp;
+  a.splits = pl.sm.splits;
+  a.kchunk = pl.sm.kchunk;
   a.tile = wq::tile_override();
 
   hipError_t e;
@@ -113,14 +112,12 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
     e = wq::launch_aq_bias_x3(a, s);
     return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
   }
-  a.rowsum = (const float*)workspace;
-  a.partial = pl.small_m ? (float*)((char*)workspace + pl.rowsum_bytes) : nullptr;
   if (pl.small_m) {
-    e = wq::launch_aq_rowsum(a, s);
-    if (e != hipSuccess) return WQ_ERR_RUNTIME;
+    a.partial = (float*)workspace;
+    a.rowsum_part = pl.rowsum_bytes ? (float*)((char*)workspace + pl.partial_bytes) : nullptr;
     e = wq::launch_aq_smallm(a, s);
   } else {
-    e = wq::launch_aq_gemm(a, s);  // row sums are formed in-kernel
+    e = wq::launch_aq_gemm(a, s);  // row sums are formed in-kernel; no workspace
   }
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
 }

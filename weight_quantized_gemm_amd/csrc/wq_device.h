@@ -160,10 +160,6 @@ __device__ __forceinline__ void dma16(const u32x4_t& rsrc, const void* lds_block
       : "memory");
 }
 
-// Wait until at most n vector-memory loads of this wave are outstanding, then join the
-// workgroup barrier.  The memory clobber keeps the compiler from moving LDS accesses
-// across it; no other wait is implied.
-#define WQ_STAGE_BARRIER(n) asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory")
 
 // ----------------------------------------------------------------------------- MFMA
 template <bool BF16>

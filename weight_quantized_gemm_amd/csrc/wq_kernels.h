@@ -14,14 +14,14 @@ struct AqArgs {
   const void* bias;      // (n) or null
   const void* x3;        // (m, n) or null
   void* out;             // (m, n)
-  const float* rowsum;   // [groups][mp] fp32 row sums of x1 per group (mp = rows padded)
-  float* partial;        // split-k partials [splits][m][n] (small-m path), else null
+  float* partial;        // small-m path: split-k partials [splits][m][n]
+  float* rowsum_part;    // small-m path, per-tensor / per-channel: row sums [splits][m]
   int64_t m;
-  int64_t mp;            // row stride of rowsum (m rounded up to 256)
   int32_t k, n;
   int32_t group;         // group size along k (per-group); k otherwise
   int32_t groups;        // parameter rows (1 unless per-group)
-  int32_t splits;        // k splits (small-m path)
+  int32_t splits;        // small-m path: k splits
+  int32_t kchunk;        // small-m path: k rows per split (a multiple of 64)
   int32_t tiles_m, tiles_n;
   int32_t tile;          // tile configuration index (0 = default)
   float code_bias;       // C: the fed weight image is code + C
@@ -45,14 +45,16 @@ struct QmArgs {
   bool out_bf16, dq_bf16, dq_per_tensor;
 };
 
-hipError_t launch_aq_rowsum(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream);  // k == 0
 hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);
 
-// Row-major workspace sizes (bytes) and split choices, shared by planner and launchers.
-int64_t aq_rowsum_mp(int64_t m);
-int aq_smallm_splits(int64_t m, int k, int n, int group, bool grouped);
+// Split-k plan of the small-m path, shared by the planner (workspace size) and the launch.
+struct SmallmPlan {
+  int kchunk = 64;   // k rows per split (a multiple of 64)
+  int splits = 1;
+};
+SmallmPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped);
 
 }  // namespace wq

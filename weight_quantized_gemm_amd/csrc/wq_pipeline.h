@@ -41,23 +41,51 @@ __device__ __forceinline__ int pair_slot(int r, int p) {
   return p ^ ((r / W) & (8 / W - 1));
 }
 
-// vmcnt(N) then the workgroup barrier (N: per-wave loads allowed to stay in flight)
+// Wait until at most N vector-memory loads of this wave are in flight and all of its LDS
+// reads have completed, then join the workgroup barrier.  After it, no wave still reads a
+// stage that a direct-to-LDS load issued after the barrier may overwrite.
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
-  if constexpr (N == 0) WQ_STAGE_BARRIER(0);
-  else if constexpr (N == 2) WQ_STAGE_BARRIER(2);
-  else if constexpr (N == 4) WQ_STAGE_BARRIER(4);
-  else if constexpr (N == 5) WQ_STAGE_BARRIER(5);
-  else if constexpr (N == 6) WQ_STAGE_BARRIER(6);
-  else if constexpr (N == 8) WQ_STAGE_BARRIER(8);
-  else if constexpr (N == 9) WQ_STAGE_BARRIER(9);
-  else if constexpr (N == 10) WQ_STAGE_BARRIER(10);
-  else if constexpr (N == 12) WQ_STAGE_BARRIER(12);
-  else if constexpr (N == 16) WQ_STAGE_BARRIER(16);
-  else if constexpr (N == 18) WQ_STAGE_BARRIER(18);
-  else if constexpr (N == 20) WQ_STAGE_BARRIER(20);
-  else if constexpr (N == 24) WQ_STAGE_BARRIER(24);
-  else static_assert(N < 0, "add this vmcnt value");
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Wave-local form: at most N vector-memory loads of this wave in flight, no barrier.
+template <int N>
+__device__ __forceinline__ void wave_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Direct-to-LDS load of the per-group scale and offset rows that a 64-row k block needs:
+// the groups ga and gb that hold its rows 31 and 63 (group ends fall on multiples of 32,
+// so these are the only groups a fold inside the block can close).  COLS 16-bit values
+// from column n0 of each row land in a 1 KiB block: scale rows at +0 and +2*COLS, offset
+// rows at +512 and +512 + 2*COLS.  Two loads per wave (one per half-wave); with no offset
+// tensor the offset half reads zeros.  rs / ro cover the tensors from column n0 on.
+template <int COLS>
+__device__ __forceinline__ void dma_group_params(uint8_t* dst, const u32x4_t& rs, const u32x4_t& ro,
+                                                 bool has_offset, int ga, int gb, int n, int lane) {
+  static_assert(COLS % 8 == 0 && 4 * COLS <= 512, "two rows of COLS 16-bit values per half");
+  constexpr int L = COLS / 8;  // 16-byte chunks per row
+  const int h = lane & 31, e = h / L, c = h % L;
+  const uint32_t off = h < 2 * L ? (uint32_t)(e ? gb : ga) * (uint32_t)n * 2u + 16u * (uint32_t)c : kOOB;
+  if (lane < 32) dma16(rs, dst, off);
+  else dma16(has_offset ? ro : rs, dst, has_offset ? off : kOOB);  // lands at dst + 512 + 16 h
+}
+
+// Direct-to-LDS load of one group's scale and offset rows (COLS 16-bit values from column
+// n0 each) for a 32-row k block, which lies inside one group (group sizes are multiples of
+// 32): scale at +0, offset at +256 bytes.  Two loads per wave, each by a quarter of the
+// wave (lanes 0..15, then 16..31; the other lanes stay inactive and write nothing); with
+// no offset tensor the offset row reads zeros.
+template <int COLS>
+__device__ __forceinline__ void dma_group_row(uint8_t* dst, const u32x4_t& rs, const u32x4_t& ro,
+                                              bool has_offset, int g, int n, int lane) {
+  static_assert(COLS == 128, "one 256-byte row per quarter wave");
+  const uint32_t off = (uint32_t)g * (uint32_t)n * 2u + 16u * (uint32_t)(lane & 15);
+  if (lane < 16) dma16(rs, dst, off);                                            // dst + 16 lane
+  else if (lane < 32) dma16(has_offset ? ro : rs, dst, has_offset ? off : kOOB);  // dst + 256 + ...
 }
 
 }  // namespace wq
