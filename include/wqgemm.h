@@ -143,6 +143,17 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
                     const wq_tensor* acc_out, void* workspace, uint64_t workspace_size,
                     void* stream);
 
+/* Profiling hook (not part of the pages' interface; for timing the device work of one
+ * call).  `before` and `after` are hipEvent_t handles, created by the caller (with timing
+ * enabled) and owned by it.  The next wq_antiquant_matmul or wq_quant_matmul call made on
+ * the calling host thread that launches work records `before` on its stream immediately
+ * before the launch of its main kernel (the one that carries the matmul) and `after`
+ * immediately after it, then disarms the hook; hipEventElapsedTime(before, after) is then
+ * that kernel's device time plus the dispatch gap in front of it.  Passing two nulls
+ * disarms the hook.  Returns WQ_OK, or WQ_ERR_PARAM_NULLPTR if exactly one is null.  A
+ * failing hipEventRecord makes the armed call return WQ_ERR_RUNTIME. */
+int wq_profile_next_call(void* before, void* after);
+
 /* Static text for a status code. */
 const char* wq_status_string(int status);
 

@@ -6,6 +6,10 @@ dtype, shape, strides), the output and workspace are allocated with torch on the
 inputs' device, and the call is enqueued on torch's current HIP stream.  Every step of
 the computation runs in the library's HIP kernels; there is no fallback path.
 
+``AntiquantMatmul`` / ``QuantMatmul`` are prepared calls, the counterpart of the
+executor of the pages' two-phase interface: descriptors, workspace size and workspace
+are settled once, and each call only enqueues the kernels (for tight loops).
+
     antiquant_matmul:  out = x1 @ ((x2 + offset) * scale) + bias + x3
     quant_matmul:      out = dequant_scale * pertoken_scale * (x1 @ x2 + bias) + x3
 
@@ -21,14 +25,15 @@ from typing import Optional, Sequence
 __all__ = ["WQ_F16", "WQ_BF16", "WQ_F32", "WQ_I8", "WQ_I4", "WQ_I32", "WQ_OK",
            "WQ_ERR_PARAM_NULLPTR", "WQ_ERR_PARAM_INVALID", "WQ_ERR_RUNTIME", "WqTensor",
            "WqError", "lib", "library_path", "make_desc", "antiquant_matmul",
-           "antiquant_workspace_size", "quant_matmul", "quant_workspace_size", "EXPORTS"]
+           "antiquant_workspace_size", "quant_matmul", "quant_workspace_size", "AntiquantMatmul",
+           "QuantMatmul", "profile_next_call", "EXPORTS"]
 
 WQ_F16, WQ_BF16, WQ_F32, WQ_I8, WQ_I4, WQ_I32 = 1, 2, 3, 4, 5, 6
 WQ_OK, WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID, WQ_ERR_RUNTIME = 0, 161001, 161002, 561001
 
 EXPORTS = ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul",
-           "wq_quant_matmul_get_workspace_size", "wq_quant_matmul", "wq_status_string",
-           "wq_version")
+           "wq_quant_matmul_get_workspace_size", "wq_quant_matmul", "wq_profile_next_call",
+           "wq_status_string", "wq_version")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libwqgemm.so")
@@ -67,6 +72,8 @@ def lib():
         for f in ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul",
                   "wq_quant_matmul_get_workspace_size", "wq_quant_matmul"):
             getattr(L, f).restype = ctypes.c_int
+        L.wq_profile_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.wq_profile_next_call.restype = ctypes.c_int
         L.wq_status_string.argtypes = [ctypes.c_int]
         L.wq_status_string.restype = ctypes.c_char_p
         L.wq_version.restype = ctypes.c_int
@@ -131,9 +138,25 @@ def _ref(d):
     return ctypes.byref(d) if d is not None else None
 
 
-def _stream_of(device):
-    torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+def _stream_handle(stream, device) -> ctypes.c_void_p:
+    """A raw stream handle: `stream` may be None (torch's current stream on `device`), a
+    torch stream, or an integer handle."""
+    if stream is None:
+        stream = _torch().cuda.current_stream(device)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def profile_next_call(before, after):
+    """Arm the library's profiling hook: the next call on this thread records the torch
+    events `before` / `after` (created with enable_timing=True and recorded once before, so
+    that their HIP events exist) around the launch of its main kernel."""
+    b = before.cuda_event if before is not None else 0
+    a = after.cuda_event if after is not None else 0
+    if (before is not None and not b) or (after is not None and not a):
+        raise ValueError("record the events once before arming the hook")
+    _check(lib().wq_profile_next_call(ctypes.c_void_p(b or None), ctypes.c_void_p(a or None)))
 
 
 def antiquant_workspace_size(x1, x2, antiquant_scale, antiquant_offset=None, bias=None, x3=None,
@@ -152,31 +175,52 @@ def _out_desc_like(x1, x2, x2_int4):
     return make_desc(list(x1.shape[:-1]) + [n], _dtype_code(x1), 0x1)
 
 
+class AntiquantMatmul:
+    """Prepared anti-quant call: out = x1 @ ((x2 + offset) * scale) + bias + x3.
+
+    Arguments as for :func:`antiquant_matmul`.  The descriptors are validated and the
+    workspace is sized (and allocated unless given) once; ``call(stream=None)`` enqueues
+    the kernels on `stream` (default: torch's current stream) and returns ``out``.  The
+    prepared call holds references to its tensors; their storage must not change."""
+
+    def __init__(self, x1, x2, antiquant_scale, antiquant_offset=None, bias=None, x3=None,
+                 antiquant_group_size: int = 0, *, x2_int4: bool = False, out=None, workspace=None):
+        torch = _torch()
+        n = x2.shape[1] * (2 if x2_int4 else 1)
+        if out is None:
+            out = torch.empty(tuple(x1.shape[:-1]) + (n,), dtype=x1.dtype, device=x1.device)
+        self._descs = [_desc(x1), _desc(x2, x2_int4), _desc(bias), _desc(antiquant_scale),
+                       _desc(antiquant_offset), _desc(x3)]
+        od = _desc(out)
+        L = lib()
+        ws = ctypes.c_uint64(0)
+        g = int(antiquant_group_size)
+        _check(L.wq_antiquant_matmul_get_workspace_size(*map(_ref, self._descs), g, _ref(od),
+                                                        ctypes.byref(ws)))
+        if workspace is None or workspace.numel() < ws.value:
+            workspace = torch.empty(max(int(ws.value), 1), dtype=torch.uint8, device=x1.device)
+        self.workspace_size = int(ws.value)
+        self.out, self.workspace, self.device = out, workspace, x1.device
+        self._keep = (x1, x2, antiquant_scale, antiquant_offset, bias, x3, od)
+        self._fn = L.wq_antiquant_matmul
+        self._args = (*map(_ref, self._descs), g, _ref(od), ctypes.c_void_p(workspace.data_ptr()),
+                      ctypes.c_uint64(workspace.numel()))
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream_handle(stream, self.device)))
+        return self.out
+
+
 def antiquant_matmul(x1, x2, antiquant_scale, antiquant_offset=None, bias=None, x3=None,
                      antiquant_group_size: int = 0, *, x2_int4: bool = False, out=None,
-                     workspace=None):
+                     workspace=None, stream=None):
     """out = x1 @ ((x2 + antiquant_offset) * antiquant_scale) + bias + x3 on x1's device.
 
     x1: fp16/bf16 (m, k) or (b, s, k); x2: int8 (k, n), or with ``x2_int4`` a uint8 (k, n/2)
     tensor of packed signed nibbles (even column in the low nibble); scale/offset: (1),
     (n), (1, n) or (ceil(k/g), n) for group size g.  Returns the output tensor."""
-    torch = _torch()
-    n = x2.shape[1] * (2 if x2_int4 else 1)
-    if out is None:
-        out = torch.empty(tuple(x1.shape[:-1]) + (n,), dtype=x1.dtype, device=x1.device)
-    d = [_desc(x1), _desc(x2, x2_int4), _desc(bias), _desc(antiquant_scale),
-         _desc(antiquant_offset), _desc(x3)]
-    od = _desc(out)
-    ws = ctypes.c_uint64(0)
-    L = lib()
-    _check(L.wq_antiquant_matmul_get_workspace_size(*map(_ref, d), int(antiquant_group_size),
-                                                    _ref(od), ctypes.byref(ws)))
-    if workspace is None or workspace.numel() < ws.value:
-        workspace = torch.empty(max(int(ws.value), 1), dtype=torch.uint8, device=x1.device)
-    _check(L.wq_antiquant_matmul(*map(_ref, d), int(antiquant_group_size), _ref(od),
-                                 ctypes.c_void_p(workspace.data_ptr()), ctypes.c_uint64(workspace.numel()),
-                                 _stream_of(x1.device)))
-    return out
+    return AntiquantMatmul(x1, x2, antiquant_scale, antiquant_offset, bias, x3, antiquant_group_size,
+                           x2_int4=x2_int4, out=out, workspace=workspace)(stream)
 
 
 def quant_workspace_size(x1, x2, dequant_scale, pertoken_scale=None, bias=None, x3=None, *,
@@ -188,23 +232,42 @@ def quant_workspace_size(x1, x2, dequant_scale, pertoken_scale=None, bias=None, 
     return ws.value
 
 
-def quant_matmul(x1, x2, dequant_scale, pertoken_scale=None, bias=None, x3=None, *,
+class QuantMatmul:
+    """Prepared W8A8 call: out = dequant_scale * pertoken_scale * (x1 @ x2 + bias) + x3.
+
+    Arguments as for :func:`quant_matmul`; ``call(stream=None)`` enqueues the kernel and
+    returns ``out``."""
+
+    def __init__(self, x1, x2, dequant_scale, pertoken_scale=None, bias=None, x3=None, *,
                  out_dtype=None, out=None, acc_out=None):
+        torch = _torch()
+        if out is None:
+            dt = out_dtype if out_dtype is not None else (x3.dtype if x3 is not None else torch.bfloat16)
+            out = torch.empty(tuple(x1.shape[:-1]) + (x2.shape[1],), dtype=dt, device=x1.device)
+        self._descs = [_desc(x1), _desc(x2), _desc(bias), _desc(x3), _desc(dequant_scale),
+                       _desc(pertoken_scale), _desc(out), _desc(acc_out)]
+        L = lib()
+        ws = ctypes.c_uint64(0)
+        _check(L.wq_quant_matmul_get_workspace_size(*map(_ref, self._descs), ctypes.byref(ws)))
+        workspace = torch.empty(max(int(ws.value), 1), dtype=torch.uint8, device=x1.device)
+        self.workspace_size = int(ws.value)
+        self.out, self.acc_out, self.workspace, self.device = out, acc_out, workspace, x1.device
+        self._keep = (x1, x2, dequant_scale, pertoken_scale, bias, x3)
+        self._fn = L.wq_quant_matmul
+        self._args = (*map(_ref, self._descs), ctypes.c_void_p(workspace.data_ptr()),
+                      ctypes.c_uint64(workspace.numel()))
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream_handle(stream, self.device)))
+        return self.out
+
+
+def quant_matmul(x1, x2, dequant_scale, pertoken_scale=None, bias=None, x3=None, *,
+                 out_dtype=None, out=None, acc_out=None, stream=None):
     """out = dequant_scale * pertoken_scale * (x1 @ x2 + bias) + x3 on x1's device.
 
     x1, x2 int8; bias int32 (n); dequant_scale fp32/bf16 (1), (n) or (1, n); pertoken_scale
     fp32 (m); x3 and the output fp16/bf16.  ``acc_out`` (int32, (m, n)) receives
     x1 @ x2 + bias."""
-    torch = _torch()
-    if out is None:
-        dt = out_dtype if out_dtype is not None else (x3.dtype if x3 is not None else torch.bfloat16)
-        out = torch.empty(tuple(x1.shape[:-1]) + (x2.shape[1],), dtype=dt, device=x1.device)
-    d = [_desc(x1), _desc(x2), _desc(bias), _desc(x3), _desc(dequant_scale), _desc(pertoken_scale),
-         _desc(out), _desc(acc_out)]
-    ws = ctypes.c_uint64(0)
-    L = lib()
-    _check(L.wq_quant_matmul_get_workspace_size(*map(_ref, d), ctypes.byref(ws)))
-    workspace = torch.empty(max(int(ws.value), 1), dtype=torch.uint8, device=x1.device)
-    _check(L.wq_quant_matmul(*map(_ref, d), ctypes.c_void_p(workspace.data_ptr()),
-                             ctypes.c_uint64(workspace.numel()), _stream_of(x1.device)))
-    return out
+    return QuantMatmul(x1, x2, dequant_scale, pertoken_scale, bias, x3, out_dtype=out_dtype, out=out,
+                       acc_out=acc_out)(stream)

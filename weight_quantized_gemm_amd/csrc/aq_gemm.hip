@@ -436,11 +436,13 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   a.tiles_n = (a.n + T::BN - 1) / T::BN;
   const size_t lds = (size_t)T::Total;
   auto kern = aq_gemm_kernel<BF16, W4, GM, GN, WM, WN, GROUPED>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = raise_lds_limit((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+  if ((e = profile_begin(stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(T::Threads), lds, stream, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return profile_end(stream);
 }
 
 }  // namespace

@@ -26,13 +26,16 @@ __global__ __launch_bounds__(256) void bias_x3_kernel(const uint16_t* __restrict
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream) {
   const int64_t total = a.m * a.n;
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 65536));
+  hipError_t e = profile_begin(stream);
+  if (e != hipSuccess) return e;
   if (a.bf16)
     hipLaunchKernelGGL(bias_x3_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint16_t*)a.bias, (const uint16_t*)a.x3, (uint16_t*)a.out, a.m, a.n);
   else
     hipLaunchKernelGGL(bias_x3_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint16_t*)a.bias, (const uint16_t*)a.x3, (uint16_t*)a.out, a.m, a.n);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return profile_end(stream);
 }
 
 }  // namespace wq

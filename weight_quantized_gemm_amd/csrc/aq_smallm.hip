@@ -267,11 +267,12 @@ hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
   using T = SmTile<W4, GROUPED>;
   const int slabs = (a.n + kSlab - 1) / kSlab;
   auto kern = aq_smallm_kernel<BF16, W4, GROUPED>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::Lds);
+  hipError_t e = raise_lds_limit((const void*)kern, T::Lds);
   if (e != hipSuccess) return e;
+  if ((e = profile_begin(stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(slabs, a.splits), dim3(kThreads), (size_t)T::Lds, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = profile_end(stream)) != hipSuccess) return e;
   const int64_t total = a.m * a.n;
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 4096));
   hipLaunchKernelGGL((aq_smallm_finish<BF16, GROUPED>), dim3((unsigned)blocks), dim3(256), 0,

@@ -232,11 +232,13 @@ hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   auto kern = a.tile == 1 ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2> : qm_gemm_kernel<false, 2, 2>)
                           : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4> : qm_gemm_kernel<false, 2, 4>);
   const int threads = a.tile == 1 ? 256 : 512;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  hipError_t e = raise_lds_limit((const void*)kern, kLds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+  if ((e = profile_begin(stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), (size_t)kLds, stream, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return profile_end(stream);
 }
 
 }  // namespace wq

@@ -8,6 +8,9 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
+#include <tuple>
+#include <vector>
 
 #include "wq_kernels.h"
 #include "wq_problem.h"
@@ -62,7 +65,39 @@ float code_bias(const AntiquantProblem& p) {
   return (p.act == WQ_BF16 && p.w4) ? 136.f : 0.f;
 }
 
+// the events armed by wq_profile_next_call on this host thread
+struct ProfileHook {
+  hipEvent_t before = nullptr;
+  hipEvent_t after = nullptr;
+};
+thread_local ProfileHook g_hook;
+
 }  // namespace
+
+hipError_t raise_lds_limit(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::vector<std::tuple<const void*, int, int>> done;  // (kernel, device, bytes)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& d : done)
+    if (std::get<0>(d) == kernel && std::get<1>(d) == dev && std::get<2>(d) >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(kernel, dev, bytes);
+  return e;
+}
+
+hipError_t profile_begin(hipStream_t stream) {
+  return g_hook.before ? hipEventRecord(g_hook.before, stream) : hipSuccess;
+}
+
+hipError_t profile_end(hipStream_t stream) {
+  hipError_t e = g_hook.after ? hipEventRecord(g_hook.after, stream) : hipSuccess;
+  g_hook = ProfileHook{};
+  return e;
+}
+
 }  // namespace wq
 
 extern "C" {
@@ -155,6 +190,13 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
   a.tile = wq::tile_override();
   hipError_t e = wq::launch_qm_gemm(a, (hipStream_t)stream);
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
+}
+
+int wq_profile_next_call(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return WQ_ERR_PARAM_NULLPTR;
+  wq::g_hook.before = (hipEvent_t)before;
+  wq::g_hook.after = (hipEvent_t)after;
+  return WQ_OK;
 }
 
 const char* wq_status_string(int status) {

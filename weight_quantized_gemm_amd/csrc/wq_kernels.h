@@ -45,6 +45,14 @@ struct QmArgs {
   bool out_bf16, dq_bf16, dq_per_tensor;
 };
 
+// Raise a kernel's dynamic LDS limit; done once per (kernel, device, size) in a process.
+hipError_t raise_lds_limit(const void* kernel, int bytes);
+
+// Profiling hook (wq_profile_next_call): record the armed events on `stream` right before
+// and right after the launch of a call's main kernel; profile_end disarms the hook.
+hipError_t profile_begin(hipStream_t stream);
+hipError_t profile_end(hipStream_t stream);
+
 hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream);  // k == 0
