@@ -211,6 +211,23 @@ def bench_one(name, args, torch, dev):
     return line
 
 
+def copy_calibration(args, torch, dev):
+    """A plain copy of known size: it reads and writes copy_mib MiB per launch."""
+    nbytes = args.copy_mib << 20
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "us_per_copy": round(dt * 1e6, 2),
+            "gbps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +236,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", dest="cpu", action="store_false", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the matmul, time a plain device-to-device copy of this many MiB "
+                         "(the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is "
@@ -228,6 +248,9 @@ def main():
     import weight_quantized_gemm_amd as W
     W.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.copy_mib > 0:
+        print(json.dumps(copy_calibration(args, torch, dev)), flush=True)
+        return
     names = sorted(workloads.WORKLOADS) if args.all else [args.workload]
     for name in names:
         print(json.dumps(bench_one(name, args, torch, dev)), flush=True)
