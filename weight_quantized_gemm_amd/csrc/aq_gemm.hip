@@ -96,15 +96,15 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
   }
 }
 
-template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
-__global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a) {
+// The kernel body, specialised on the wave's column index WNI in the GM x GN wave grid:
+// column offsets and the per-channel row-sum block become compile-time constants.
+template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED, int WNI>
+__device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int wave) {
   using T = Tile<W4, GM, GN, WM, WN, GROUPED>;
   constexpr int BN = T::BN, RB = T::RB, WC = T::WCols;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave / GN, wn = wave % GN;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / GN;
+  constexpr int wn = WNI;
   int tm, tn;
   tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * 256;
@@ -119,17 +119,19 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
   // slot).  The per-lane byte offsets inside a stage do not depend on k: they are formed
   // once, and each k-step only moves the (scalar) buffer base.
   const uint8_t* x1b = (const uint8_t*)a.x1 + m0 * K * 2;
-  const int64_t x1_rows_bytes = (M - m0) * K * 2;
+  // bytes of x1 from the tile's first row on that the tile may read (at most 256 rows)
+  const uint32_t x1_bytes = (uint32_t)((M - m0 < 256 ? M - m0 : 256) * K * 2);
   const int nb0 = W4 ? n0 / 2 : n0;
   const uint8_t* x2b = (const uint8_t*)a.x2 + nb0;
   uint32_t a_off[T::Aper];
-  int a_chunk[T::Aper];
+  int a_k[T::Aper];  // first k (within the stage) of the chunk this lane loads
 #pragma unroll
   for (int j = 0; j < T::Aper; ++j) {
     const int b = wave + T::Waves * j;
     const int r = 8 * b + (lane >> 3);
-    a_chunk[j] = row_slot<kArow>(r, lane & 7);  // logical chunk held by this physical slot
-    a_off[j] = (uint32_t)(r * K * 2 + 16 * a_chunk[j]);
+    const int c = row_slot<kArow>(r, lane & 7);  // logical chunk held by this physical slot
+    a_k[j] = 8 * c;
+    a_off[j] = (uint32_t)(r * K * 2 + 16 * c);
   }
   uint32_t b_off[T::Bper];
 #pragma unroll
@@ -147,32 +149,67 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
     rsc = make_rsrc((const uint8_t*)a.scale + 2 * (int64_t)n0, pbytes);
     rof = has_offset ? make_rsrc((const uint8_t*)a.offset + 2 * (int64_t)n0, pbytes) : rsc;
   }
-  auto issue = [&](int ks) {
-    uint8_t* st = smem + (ks % kStages) * T::Stage;
-    const int k0 = ks * kBK;
-    const u32x4_t ra = make_rsrc(x1b + (int64_t)k0 * 2, x1_rows_bytes - (int64_t)k0 * 2);
-    const bool tail = k0 + kBK > K;  // only the last k-step can reach past k
-#pragma unroll
-    for (int j = 0; j < T::Aper; ++j) {
-      const uint32_t off = (tail && k0 + 8 * a_chunk[j] >= K) ? kOOB : a_off[j];
-      dma16(ra, st + 1024 * (wave + T::Waves * j), off);
-    }
-    if constexpr (GROUPED) {
-      if (wave == T::Pwave) {
-        const int ga = min((k0 + 31) / a.group, a.groups - 1);
-        const int gb = min((k0 + 63) / a.group, a.groups - 1);
-        dma_group_params<BN>(st + kAbytes + T::Bbytes, rsc, rof, has_offset, ga, gb, N, lane);
-      }
-    }
-    if (wave >= T::Bwaves) return;
-    const u32x4_t rb = make_rsrc(x2b + (int64_t)k0 * x2_pitch, (int64_t)(K - k0) * x2_pitch - nb0);
-#pragma unroll
-    for (int j = 0; j < T::Bper; ++j)
-      dma16(rb, st + kAbytes + 1024 * (wave + T::Waves * j), b_off[j]);
-  };
   // loads this wave issues per stage
   constexpr int kOwnA = T::Aper, kOwnB = T::Bper, kOwnP = GROUPED ? 2 : 0;
   const bool has_b = wave < T::Bwaves, has_p = GROUPED && wave == T::Pwave;
+
+  // The loads of one stage, as items that can be issued separately: x1 blocks j (kind 0),
+  // weight blocks j (kind 1) and the group-parameter rows (kind 2).  A stage's resources
+  // are formed once by stage_rsrc; the items are then spread over the four 16-k steps of
+  // the k-step that issues them, so that the texture unit is not handed a burst of loads
+  // that stalls the waves' matrix-core work.
+  struct StageRsrc {
+    u32x4_t ra, rb;
+    uint8_t* st;
+    int k0;
+    bool tail;
+  };
+  auto stage_rsrc = [&](int ks) {
+    StageRsrc r;
+    r.k0 = ks * kBK;
+    r.st = smem + (ks % kStages) * T::Stage;
+    r.ra = make_rsrc32(x1b + (int64_t)r.k0 * 2, x1_bytes - (uint32_t)r.k0 * 2);
+    const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
+    r.rb = make_rsrc32(x2b + (int64_t)r.k0 * x2_pitch, (uint32_t)(rows * x2_pitch - nb0));
+    r.tail = r.k0 + kBK > K;  // only the last k-step can reach past k
+    return r;
+  };
+  auto issue_a = [&](const StageRsrc& r, int j) {
+    uint8_t* dst = r.st + 1024 * (wave + T::Waves * j);
+    if (!r.tail) {
+      dma16(r.ra, dst, a_off[j]);
+    } else {
+      dma16(r.ra, dst, r.k0 + a_k[j] >= K ? kOOB : a_off[j]);
+    }
+  };
+  auto issue_b = [&](const StageRsrc& r, int j) {
+    dma16(r.rb, r.st + kAbytes + 1024 * (wave + T::Waves * j), b_off[j]);
+  };
+  auto issue_p = [&](const StageRsrc& r) {
+    if constexpr (GROUPED) {
+      const int ga = min((r.k0 + 31) / a.group, a.groups - 1);
+      const int gb = min((r.k0 + 63) / a.group, a.groups - 1);
+      dma_group_params<BN>(r.st + kAbytes + T::Bbytes, rsc, rof, has_offset, ga, gb, N, lane);
+    }
+  };
+  // the items of 16-k step kk: x1 blocks j with j % 4 == kk, weight blocks j with
+  // (j + 2) % 4 == kk, the parameter rows at kk == 1
+  auto issue_step = [&](const StageRsrc& r, int kk) {
+#pragma unroll
+    for (int j = 0; j < T::Aper; ++j)
+      if (j % 4 == kk) issue_a(r, j);
+    if (has_b) {
+#pragma unroll
+      for (int j = 0; j < T::Bper; ++j)
+        if ((j + 2) % 4 == kk) issue_b(r, j);
+    }
+    if (has_p && kk == 1) issue_p(r);
+  };
+  auto issue = [&](int ks) {
+    const StageRsrc r = stage_rsrc(ks);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) issue_step(r, kk);
+  };
 
   // ---------------------------------------------------------------- accumulators
   f32x16_t acc[WM][WN];
@@ -196,8 +233,8 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
   float ssum[SB];
 #pragma unroll
   for (int i = 0; i < SB; ++i) ssum[i] = 0.f;
-  // the wave's first summed block (per-channel): uniform
-  const int sb0 = GROUPED ? 0 : (WM >= GN ? wn * SB : (wn < WM ? wn : WM));
+  // the wave's first summed block (per-channel)
+  constexpr int sb0 = GROUPED ? 0 : (WM >= GN ? wn * SB : (wn < WM ? wn : WM));
 
   const uint16_t* __restrict__ scale = (const uint16_t*)a.scale;
   const uint16_t* __restrict__ offset = (const uint16_t*)a.offset;
@@ -281,7 +318,9 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
     else if (has_b) stage_barrier<kOwnA + kOwnB>();
     else if (has_p) stage_barrier<kOwnA + kOwnP>();
     else stage_barrier<kOwnA>();
-    if (ks + 2 < nk) issue(ks + 2);
+    const bool more = ks + 2 < nk;
+    StageRsrc nr{};
+    if (more) nr = stage_rsrc(ks + 2);
     if (ks == nk - 1) {  // no DMA left: start the epilogue's x3 reads under the last MFMAs
       prefetch_x3(0, 0);
       if (XP > 1 && WM > 1) prefetch_x3(1, 1 % XP);
@@ -305,16 +344,14 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #pragma unroll
           for (int q = 0; q < 4; ++q) ssum[i] = dot2_ones<BF16>(cur.a[i][q], ssum[i]);
       } else {
-        // select this wave's blocks without dynamic register indexing
 #pragma unroll
         for (int t = 0; t < SB; ++t) {
-          u32x4_t v = cur.a[0];
-#pragma unroll
-          for (int i = 1; i < WM; ++i)
-            if (sb0 + t == i) v = cur.a[i];
+          // sb0 is a constant and t an unrolled index: the block is chosen at compile time
+          constexpr int kLast = WM - 1;
+          const int blk = sb0 + t < WM ? sb0 + t : kLast;
           if (sb0 + t < WM) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ssum[t] = dot2_ones<BF16>(v[q], ssum[t]);
+            for (int q = 0; q < 4; ++q) ssum[t] = dot2_ones<BF16>(cur.a[blk][q], ssum[t]);
           }
         }
       }
@@ -328,6 +365,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
       for (int i = 0; i < WM; ++i)
 #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], acc[i][j]);
+      if (more) issue_step(nr, kk);  // behind this step's matrix-core work
 
       if constexpr (GROUPED) {
         if (kk & 1) {  // groups end on multiples of 32
@@ -429,7 +467,25 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 }
 
 template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
+__global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
+  const int wn = wave % GN;
+#define WQ_WAVE_COLUMN(c)                                                      \
+  if constexpr (GN > c) {                                                     \
+    if (wn == c) {                                                            \
+      aq_gemm_body<BF16, W4, GM, GN, WM, WN, GROUPED, c>(a, smem, wave);       \
+      return;                                                                 \
+    }                                                                         \
+  }
+  WQ_WAVE_COLUMN(0) WQ_WAVE_COLUMN(1) WQ_WAVE_COLUMN(2) WQ_WAVE_COLUMN(3)
+  WQ_WAVE_COLUMN(4) WQ_WAVE_COLUMN(5) WQ_WAVE_COLUMN(6) WQ_WAVE_COLUMN(7)
+#undef WQ_WAVE_COLUMN
+}
+
+template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
 hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
+  static_assert(GN <= 8, "wave grids have at most 8 columns");
   using T = Tile<W4, GM, GN, WM, WN, GROUPED>;
   AqArgs a = a0;
   a.tiles_m = (int)((a.m + 255) / 256);

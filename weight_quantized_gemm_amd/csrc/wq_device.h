@@ -139,6 +139,13 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, int64_t bytes) {
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)n), 0x00020000u};
 }
+// The same with a range the caller has already bounded (bytes <= 0x7fffffff): no clamp.
+__device__ __forceinline__ u32x4_t make_rsrc32(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+}
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every resource: the load reads 0
 
 // One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes land at lds_block + 16*l.
