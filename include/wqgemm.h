@@ -110,6 +110,11 @@ int wq_antiquant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor*
  * (at least what the size query returned; NULL allowed when that is 0).
  * Repeats every check of the size query; a workspace smaller than required is
  * WQ_ERR_PARAM_INVALID.  Returns WQ_ERR_RUNTIME if a launch fails.
+
+ *
+ * Workspace contents: none are expected on entry; the small-m path (m <= 32) with its
+ * k split over several workgroups keeps the fp32 partial sums there until a finishing
+ * kernel of the same call has added them.
  */
 int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
                         const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,

@@ -14,7 +14,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import (ref_antiquant, ref_w8a8, run_antiquant, run_w8a8, sampled_rows, to_f64)
+from gpu_util import (dev_tensor, ref_antiquant, ref_w8a8, run_antiquant, run_w8a8, sampled_rows,
+                      to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +123,29 @@ def test_determinism():
         b = run_antiquant(case).cpu()
         assert bytes(a.view(-1).view(__import__("torch").int16).numpy()) == \
             bytes(b.view(-1).view(__import__("torch").int16).numpy())
+
+
+def test_smallm_workspace_reuse():
+    """One workspace (the small-m split-k partials) serves consecutive calls on different
+    inputs and parameter modes; every call is checked against the oracle."""
+    import torch
+    import weight_quantized_gemm_amd as W
+    _announce("smallm_workspace_reuse")
+    ws = None
+    for i, (mode, g) in enumerate([("group", 64), ("group", 64), ("channel", 0), ("group", 96)]):
+        case = workloads.make_antiquant(seed=700 + i, name=f"reuse{i}", act="fp16", weight="int8",
+                                        x1_shape=(24, 2304), n=384, mode=mode, group_size=g)
+        act = case.act
+        call_args = (dev_tensor(case.x1, act), dev_tensor(case.x2, "raw"), dev_tensor(case.scale, act),
+                     dev_tensor(case.offset, act), dev_tensor(case.bias, act), dev_tensor(case.x3, act),
+                     case.group_size)
+        call = W.AntiquantMatmul(*call_args, workspace=ws)
+        assert call.workspace_size > 0  # the split-k path
+        ws = call.workspace
+        y = call()
+        torch.cuda.synchronize()
+        r = oracle.compare(to_f64(y).reshape(case.out_shape), ref_antiquant(case), act)
+        assert r["ok"], (i, r)
 
 
 W8A8_CASES = [

@@ -7,16 +7,18 @@
 //
 // Work split: a workgroup owns a 128-column slab of x2 and a contiguous k range (split-k).
 // Its 8 waves (two per SIMD, so that one wave's LDS, matrix-core and VALU latencies hide
-// behind the other's work) take 64-row units of the range round-robin.  Each wave streams
-// its 32-row blocks -- weights, the matching 32 x 32 slice of x1 and, per-group, the
-// block's scale / offset row -- into its own 3-stage LDS ring with direct-to-LDS loads (no
-// barriers; vmcnt waits only), reads B fragments with tr8 transpose reads, converts them to
-// exact 16-bit images and runs 32x32x16 MFMAs.  Row sums of x1 come from the A fragments
-// (v_dot2).  Per-group parameters are applied at each group end and at each unit end: the
-// fold is linear in the accumulators and row sums, so a group split between waves or
-// workgroups is folded piecewise with its own scale and offset.  The 8 waves are reduced
-// through LDS in a fixed order and the splits by a finishing kernel in a fixed order:
-// results are deterministic.
+// behind the other's work) take the range's 64-row blocks round-robin.  Each block --
+// weights, the matching 32 x 64 slice of x1 (full 128-byte rows) and, per-group, the scale
+// / offset rows of its two 32-row halves -- streams into the wave's own LDS stage by
+// direct-to-LDS loads (no barriers; vmcnt waits only).  The wave copies the block into
+// registers (A fragments by ds_read_b128, B fragments by tr8 transpose reads), hands the
+// stage to its next block at once, and then converts the codes to exact 16-bit images and
+// runs 32x32x16 MFMAs while that block streams in.  Row sums of x1 come from the A
+// fragments (v_dot2).  Per-group parameters are applied at each group end and at each
+// block end: the fold is linear in the accumulators and row sums, so a group split between
+// waves or workgroups is folded piecewise with its own scale and offset.  The 8 waves are
+// reduced through LDS in a fixed order and the splits by a finishing kernel in a fixed
+// order: results are deterministic.
 #include "wq_kernels.h"
 #include "wq_pipeline.h"
 
@@ -26,28 +28,24 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlab = 128;    // logical columns per workgroup
-constexpr int kRows = 32;     // k rows per block
-constexpr int kUnit = 64;     // k rows per work unit (blocks of one unit run back to back)
-constexpr int kStages = 3;    // blocks in flight per wave
+constexpr int kRows = 64;     // k rows per block, a wave's unit of work
 
 template <bool W4, bool GROUPED>
 struct SmTile {
   static constexpr int RB = W4 ? kSlab / 2 : kSlab;   // weight bytes per k row
-  static constexpr int Wbytes = kRows * RB;           // 4 or 2 KiB
-  static constexpr int Xbytes = 32 * kRows * 2;       // 2 KiB of x1 (32 rows x 32 k)
-  static constexpr int Pbytes = GROUPED ? 512 : 0;    // the block's scale / offset row
-  static constexpr int Stage = Wbytes + Xbytes + Pbytes;
+  static constexpr int Wbytes = kRows * RB;           // 8 or 4 KiB
+  static constexpr int Xbytes = 32 * kRows * 2;       // 4 KiB of x1 (32 rows x 64 k)
+  static constexpr int Pbytes = GROUPED ? 1024 : 0;   // scale / offset rows of the block's groups
+  static constexpr int Stage = Wbytes + Xbytes + Pbytes;  // one per wave
   static constexpr int WDma = Wbytes / 1024;
   static constexpr int XDma = Xbytes / 1024;
-  static constexpr int Dma = WDma + XDma + (GROUPED ? 2 : 0);  // loads per block
-  static constexpr int Ring = kStages * Stage;        // per wave
-  static constexpr int Red = kWaves * 32 * kSlab * 4; // wave reduction buffer
-  static constexpr int Body = kWaves * Ring > Red ? kWaves * Ring : Red;
+  static constexpr int RedPitch = 36;                 // floats per column (32 rows + bank pad)
+  static constexpr int Red = kWaves * kSlab * RedPitch * 4;  // column-major wave reduction
+  static constexpr int Body = kWaves * Stage > Red ? kWaves * Stage : Red;
   static constexpr int GOff = Body;                   // per-wave group row-sum scratch
   static constexpr int SOff = GOff + kWaves * 32 * 4; // per-wave row sums (per-channel)
   static constexpr int Lds = SOff + kWaves * 32 * 4;
   static_assert(Lds <= 160 * 1024, "one workgroup per CU");
-  static_assert(2 * Dma <= 63, "vmcnt range");
 };
 
 template <bool BF16, bool W4, bool GROUPED>
@@ -61,17 +59,14 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   const int K = a.k, N = a.n, M = (int)a.m;
   const int kbeg = split * a.kchunk;
   const int kend = min(K, kbeg + a.kchunk);
-  constexpr int bpu = kUnit / kRows;                      // blocks per unit
-  const int nunits = kend > kbeg ? (kend - kbeg + kUnit - 1) / kUnit : 0;
-  // this wave's blocks: units wave, wave + 8, ...; the blocks of a unit in order
-  const int my_units = wave < nunits ? (nunits - wave + kWaves - 1) / kWaves : 0;
-  auto block_k0 = [&](int t) { return kbeg + (wave + kWaves * (t / bpu)) * kUnit + (t % bpu) * kRows; };
-  int nb = my_units * bpu;
-  while (nb > 0 && block_k0(nb - 1) >= kend) --nb;         // a trailing block past the range
+  const int nblocks = kend > kbeg ? (kend - kbeg + kRows - 1) / kRows : 0;
+  // this wave's blocks: wave, wave + 8, ... of the workgroup's k range
+  const int nb = wave < nblocks ? (nblocks - wave + kWaves - 1) / kWaves : 0;
+  auto block_k0 = [&](int t) { return kbeg + (wave + kWaves * t) * kRows; };
 
   const int64_t x2_pitch = W4 ? (N >> 1) : N;
   const int nb0 = W4 ? n0 / 2 : n0;
-  uint8_t* ring = smem + wave * T::Ring;
+  uint8_t* const st = smem + wave * T::Stage;  // the wave's one LDS stage
 
   // per-lane DMA offsets inside a block
   uint32_t w_off[T::WDma];
@@ -82,10 +77,13 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
     w_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * pair_slot<RB>(r, p >> 1) + (p & 1)));
   }
   uint32_t x_off[T::XDma];
+  int x_k[T::XDma];  // first k (within the block) of the x1 chunk this lane loads
 #pragma unroll
   for (int j = 0; j < T::XDma; ++j) {
-    const int r = 16 * j + (lane >> 2);
-    x_off[j] = (uint32_t)(r * K * 2 + 16 * row_slot<64>(r, lane & 3));
+    const int r = 8 * j + (lane >> 3);
+    const int c = row_slot<128>(r, lane & 7);
+    x_k[j] = 8 * c;
+    x_off[j] = (uint32_t)(r * K * 2 + 16 * c);
   }
   const bool has_offset = a.offset != nullptr;
   u32x4_t rsc{}, rof{};
@@ -95,18 +93,21 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
     rof = has_offset ? make_rsrc((const uint8_t*)a.offset + 2 * (int64_t)n0, pbytes) : rsc;
   }
   auto issue = [&](int t) {
-    uint8_t* st = ring + (t % kStages) * T::Stage;
     const int k0 = block_k0(t);
     const u32x4_t rw = make_rsrc((const uint8_t*)a.x2 + (int64_t)k0 * x2_pitch + nb0,
                                  (int64_t)(kend - k0) * x2_pitch - nb0);
 #pragma unroll
     for (int j = 0; j < T::WDma; ++j) dma16(rw, st + 1024 * j, w_off[j]);
-    // blocks never straddle kend (both are multiples of 32): only rows >= m read zeros
+    // rows >= m lie past the resource; k >= kend (a 32-row tail block) is masked per chunk
     const u32x4_t rx = make_rsrc((const uint8_t*)a.x1 + (int64_t)k0 * 2, (int64_t)M * K * 2 - (int64_t)k0 * 2);
 #pragma unroll
-    for (int j = 0; j < T::XDma; ++j) dma16(rx, st + T::Wbytes + 1024 * j, x_off[j]);
-    if constexpr (GROUPED)
-      dma_group_row<kSlab>(st + T::Wbytes + T::Xbytes, rsc, rof, has_offset, k0 / a.group, N, lane);
+    for (int j = 0; j < T::XDma; ++j)
+      dma16(rx, st + T::Wbytes + 1024 * j, k0 + x_k[j] < kend ? x_off[j] : kOOB);
+    if constexpr (GROUPED) {
+      const int ga = min(k0 / a.group, a.groups - 1);
+      const int gb = min((k0 + 32) / a.group, a.groups - 1);
+      dma_group_params<kSlab>(st + T::Wbytes + T::Xbytes, rsc, rof, has_offset, ga, gb, N, lane);
+    }
   };
 
   f32x16_t acc[4], tot[GROUPED ? 4 : 1];
@@ -125,20 +126,19 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   const float cbias = a.code_bias;
   float* gscr = (float*)(smem + T::GOff) + wave * 32;
 
-  // fold the accumulators of the current group with the group's parameter rows at Ps:
-  // tot += s * acc + s * (off - C) * S, S the row sums since the last fold
-  auto fold = [&](const uint16_t* Ps) {
+  // fold the accumulators of the current group with the group's scale / offset values of
+  // this lane's four column blocks: tot += s * acc + s * (off - C) * S, S the row sums
+  // since the last fold
+  auto fold = [&](const uint16_t (&ps)[4], const uint16_t (&po)[4]) {
     const float t = ssum + __shfl_xor(ssum, 32, 64);
     if (lane < 32) gscr[lane] = t;
     ssum = 0.f;
     float s[4], q[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int lc = block_col(j) - n0;
-      const float sv = act_to_f32<BF16>(Ps[lc]);
-      const float ov = act_to_f32<BF16>(Ps[128 + lc]);
+      const float sv = act_to_f32<BF16>(ps[j]);
       s[j] = sv;
-      q[j] = sv * (ov - cbias);
+      q[j] = sv * (act_to_f32<BF16>(po[j]) - cbias);
     }
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
@@ -154,111 +154,210 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   };
 
   // ------------------------------------------------------------------ stream
-  for (int t = 0; t < nb && t < kStages; ++t) issue(t);
+  // One block in flight per wave in LDS, one in registers: the wave reads block t out of
+  // its stage, hands the stage to block t + 1 at once, then computes on block t while
+  // block t + 1 streams in.  Eight waves keep 96-104 KiB in flight per CU.
+  if (nb > 0) issue(0);
   for (int t = 0; t < nb; ++t) {
-    const int ahead = min(kStages - 1, nb - 1 - t);  // blocks issued after block t
-    if (ahead == 2) wave_wait<2 * T::Dma>();
-    else if (ahead == 1) wave_wait<T::Dma>();
-    else wave_wait<0>();
-    const uint8_t* W = ring + (t % kStages) * T::Stage;
-    const uint8_t* X = W + T::Wbytes;
+    wave_wait<0>();
+    const uint8_t* W = st;
+    const uint8_t* X = st + T::Wbytes;
+    constexpr int kP = W4 ? 2 : 4;            // tr8 reads per 16-k step
+    u32x4_t af[kRows / 16];
+    u32x2_t braw[kRows / 16][kP];
 #pragma unroll
     for (int kk = 0; kk < kRows / 16; ++kk) {
       const int r = lane & 31;
-      const u32x4_t af = *(const u32x4_t*)(X + r * 64 + 16 * row_slot<64>(r, 2 * kk + (lane >> 5)));
+      af[kk] = *(const u32x4_t*)(X + r * 128 + 16 * row_slot<128>(r, 2 * kk + (lane >> 5)));
       const int kr = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 1);
       const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 #pragma unroll
-      for (int p = 0; p < (W4 ? 2 : 4); ++p) {
-        const u32x2_t d = lds_read_tr8(W + kr * RB + 32 * pair_slot<RB>(kr, p) + sub);
+      for (int p = 0; p < kP; ++p) braw[kk][p] = lds_read_tr8(W + kr * RB + 32 * pair_slot<RB>(kr, p) + sub);
+    }
+    // the parameter rows of the block's first (e = 0) and second (e = 1) 32-row halves
+    uint16_t ps[2][4], po[2][4];
+    if constexpr (GROUPED) {
+      const uint16_t* Ps = (const uint16_t*)(X + T::Xbytes);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int lc = block_col(j) - n0;
+          ps[e][j] = Ps[e * kSlab + lc];
+          po[e][j] = Ps[2 * kSlab + e * kSlab + lc];
+        }
+    }
+    // the stage's LDS reads have completed (the direct-to-LDS writes land whenever their
+    // data returns, so they must not be issued earlier): hand it to the next block
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t + 1 < nb) issue(t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int k0 = block_k0(t);
+#pragma unroll
+    for (int kk = 0; kk < kRows / 16; ++kk) {
+#pragma unroll
+      for (int p = 0; p < kP; ++p) {
         if constexpr (W4) {
           u32x4_t ev, od;
-          i4_kpairs<BF16>(d, ev, od);
-          acc[2 * p] = mfma32x32x16<BF16>(af, ev, acc[2 * p]);
-          acc[2 * p + 1] = mfma32x32x16<BF16>(af, od, acc[2 * p + 1]);
+          i4_kpairs<BF16>(braw[kk][p], ev, od);
+          acc[2 * p] = mfma32x32x16<BF16>(af[kk], ev, acc[2 * p]);
+          acc[2 * p + 1] = mfma32x32x16<BF16>(af[kk], od, acc[2 * p + 1]);
         } else {
-          acc[p] = mfma32x32x16<BF16>(af, i8x8_to_act<BF16>(d), acc[p]);
+          acc[p] = mfma32x32x16<BF16>(af[kk], i8x8_to_act<BF16>(braw[kk][p]), acc[p]);
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ssum = dot2_ones<BF16>(af[q], ssum);
-    }
-    if constexpr (GROUPED) {
-      // fold at a group end, and wherever the wave's next block does not continue this one
-      const int kdone = block_k0(t) + kRows;
-      if (kdone % a.group == 0 || kdone == kend || t % bpu == bpu - 1 || t == nb - 1)
-        fold((const uint16_t*)(X + T::Xbytes));
-    }
-    // refill the slot of block t: its LDS reads must have completed first, since the
-    // direct-to-LDS writes land whenever their data returns
-    if (t + kStages < nb) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue(t + kStages);
+      for (int q = 0; q < 4; ++q) ssum = dot2_ones<BF16>(af[kk][q], ssum);
+      if constexpr (GROUPED) {
+        // folds: where a group ends inside the block (group sizes are multiples of 32), and
+        // at the block end, after which the wave continues elsewhere in k
+        if (kk == 1 && ((k0 + 32) % a.group == 0 || k0 + 32 >= kend)) fold(ps[0], po[0]);
+        if (kk == 3 && k0 + 32 < kend) fold(ps[1], po[1]);
+      }
     }
   }
 
   // ------------------------------------------------------------------ wave reduction
-  __syncthreads();
-  float* red = (float*)smem;  // [kWaves][32][kSlab]
+  // The eight waves' tiles are staged column-major (32 rows per column, padded): a lane
+  // moves its 16 accumulators of a column block as four 16-byte writes, and thread t then
+  // sums, in wave order, rows 8*(t/128) .. +7 of column t % 128 with 16-byte reads.
+  __syncthreads();  // every wave has left the stream: the stages are free
+  constexpr int RP = T::RedPitch;
+  float* red = (float*)smem;
   float* sred = (float*)(smem + T::SOff);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int lc = block_col(j) - n0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[(wave * 32 + acc_row(r, lane)) * kSlab + lc] = GROUPED ? tot[j][r] : acc[j][r];
+    for (int rq = 0; rq < 4; ++rq) {
+      const f32x16_t& v = GROUPED ? tot[j] : acc[j];
+      *(f32x4_t*)(red + (wave * kSlab + lc) * RP + 8 * rq + 4 * (lane >> 5)) =
+          f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]};
+    }
   }
   if constexpr (!GROUPED) {
     const float t = ssum + __shfl_xor(ssum, 32, 64);
     if (lane < 32) sred[wave * 32 + lane] = t;
   }
   __syncthreads();
-  float* part = a.partial + (int64_t)split * a.m * N;
-  for (int o = tid; o < 32 * kSlab; o += kThreads) {
-    const int row = o / kSlab, lc = o % kSlab;
-    if (row >= M || n0 + lc >= N) continue;
-    float v = 0.f;
+  const int c = tid & (kSlab - 1), r0 = 8 * (tid >> 7);
+  const int gcol = n0 + c;
+  const bool col_ok = gcol < N;
+  float v[8];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[(w * 32 + row) * kSlab + lc];
-    part[(int64_t)row * N + n0 + lc] = v;
-  }
-  if constexpr (!GROUPED) {
-    if (blockIdx.x == 0 && tid < M) {
-      float v = 0.f;
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += sred[w * 32 + tid];
-      a.rowsum_part[(int64_t)split * a.m + tid] = v;
+  for (int w = 0; w < kWaves; ++w) {
+    const f32x4_t lo = *(const f32x4_t*)(red + (w * kSlab + c) * RP + r0);
+    const f32x4_t hi = *(const f32x4_t*)(red + (w * kSlab + c) * RP + r0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] += lo[i];
+      v[4 + i] += hi[i];
     }
+  }
+  float srow[8];  // per-channel: this workgroup's row sums of rows r0 .. r0 + 7
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    srow[i] = 0.f;
+    if constexpr (!GROUPED) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) srow[i] += sred[w * 32 + r0 + i];
+    }
+  }
+
+  // ------------------------------------------------------------------ split-k
+  // With several k splits every workgroup writes its partial sums (and, per-channel, its
+  // row sums); the finishing kernel adds the splits in split order and writes the output.
+  const int S = a.splits;
+  if (S > 1) {
+    float* part = a.partial + (int64_t)split * a.m * N;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (r0 + i < M && col_ok) part[(int64_t)(r0 + i) * N + gcol] = v[i];
+    if constexpr (!GROUPED) {
+      if (c == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (r0 + i < M) a.rowsum_part[(int64_t)split * a.m + r0 + i] = srow[i];
+      }
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------------ output (one split)
+  // out = [s*P + s*(off-C)*S] (per-tensor / per-channel) or T (per-group), + bias + x3
+  if (!col_ok) return;
+  float cs = 1.f, cq = 0.f;
+  if constexpr (!GROUPED) {
+    const uint16_t* scale = (const uint16_t*)a.scale;
+    const uint16_t* offset = (const uint16_t*)a.offset;
+    const int pc = a.per_tensor ? 0 : gcol;
+    cs = act_to_f32<BF16>(scale[pc]);
+    cq = cs * ((offset ? act_to_f32<BF16>(offset[pc]) : 0.f) - cbias);
+  }
+  const float cb = a.bias ? act_to_f32<BF16>(((const uint16_t*)a.bias)[gcol]) : 0.f;
+  const uint16_t* x3 = (const uint16_t*)a.x3;
+  uint16_t* out = (uint16_t*)a.out;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = r0 + i;
+    if (row >= M) continue;
+    const int64_t idx = (int64_t)row * N + gcol;
+    float y = GROUPED ? v[i] : fmaf(cs, v[i], cq * srow[i]);
+    y += cb;
+    if (x3) y += act_to_f32<BF16>(x3[idx]);
+    out[idx] = f32_to_act<BF16>(y);
   }
 }
 
-// out = [s*P + s*(off-C)*S]  (per-tensor / per-channel)  or  T (per-group), + bias + x3,
-// where P / T and S are the sums of the split partials in split order.
+// Split-k finish: out = [s*P + s*(off-C)*S] (per-tensor / per-channel) or T (per-group),
+// + bias + x3, where P / T and S are the sums of the split partials in split order.  A
+// thread handles four consecutive columns of one row (n is a multiple of 32).
 template <bool BF16, bool GROUPED>
 __global__ __launch_bounds__(256) void aq_smallm_finish(const AqArgs a) {
-  const int64_t total = a.m * a.n;
   const int N = a.n;
+  const int64_t quads = a.m * (N / 4);
+  const int64_t plane = a.m * N;
   const uint16_t* scale = (const uint16_t*)a.scale;
   const uint16_t* offset = (const uint16_t*)a.offset;
   const uint16_t* bias = (const uint16_t*)a.bias;
   const uint16_t* x3 = (const uint16_t*)a.x3;
   uint16_t* out = (uint16_t*)a.out;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = i / N;
-    const int col = (int)(i - row * N);
-    float v = 0.f;
-    for (int s = 0; s < a.splits; ++s) v += a.partial[(int64_t)s * total + i];
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = q / (N / 4);
+    const int col = 4 * (int)(q - row * (N / 4));
+    const int64_t idx = row * N + col;
+    f32x4_t v = *(const f32x4_t*)(a.partial + idx);
+    for (int s = 1; s < a.splits; ++s) {
+      const f32x4_t p = *(const f32x4_t*)(a.partial + (int64_t)s * plane + idx);
+      v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+    }
+    float y[4] = {v[0], v[1], v[2], v[3]};
     if constexpr (!GROUPED) {
       float srow = 0.f;
       for (int s = 0; s < a.splits; ++s) srow += a.rowsum_part[(int64_t)s * a.m + row];
-      const int pc = a.per_tensor ? 0 : col;
-      const float sv = act_to_f32<BF16>(scale[pc]);
-      const float ov = offset ? act_to_f32<BF16>(offset[pc]) : 0.f;
-      v = fmaf(sv, v, sv * (ov - a.code_bias) * srow);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pc = a.per_tensor ? 0 : col + e;
+        const float sv = act_to_f32<BF16>(scale[pc]);
+        const float ov = offset ? act_to_f32<BF16>(offset[pc]) : 0.f;
+        y[e] = fmaf(sv, y[e], sv * (ov - a.code_bias) * srow);
+      }
     }
-    if (bias) v += act_to_f32<BF16>(bias[col]);
-    if (x3) v += act_to_f32<BF16>(x3[i]);
-    out[i] = f32_to_act<BF16>(v);
+    if (bias) {
+      const u32x2_t b = *(const u32x2_t*)(bias + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] += act_to_f32<BF16>((uint16_t)(b[e >> 1] >> (16 * (e & 1))));
+    }
+    if (x3) {
+      const u32x2_t x = *(const u32x2_t*)(x3 + idx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] += act_to_f32<BF16>((uint16_t)(x[e >> 1] >> (16 * (e & 1))));
+    }
+    *(u32x2_t*)(out + idx) = u32x2_t{(uint32_t)f32_to_act<BF16>(y[0]) | ((uint32_t)f32_to_act<BF16>(y[1]) << 16),
+                                     (uint32_t)f32_to_act<BF16>(y[2]) | ((uint32_t)f32_to_act<BF16>(y[3]) << 16)};
   }
 }
 
@@ -273,10 +372,10 @@ hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3(slabs, a.splits), dim3(kThreads), (size_t)T::Lds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = profile_end(stream)) != hipSuccess) return e;
-  const int64_t total = a.m * a.n;
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 4096));
-  hipLaunchKernelGGL((aq_smallm_finish<BF16, GROUPED>), dim3((unsigned)blocks), dim3(256), 0,
-                     stream, a);
+  if (a.splits == 1) return hipSuccess;  // the kernel wrote the output
+  const int64_t quads = a.m * (a.n / 4);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((quads + 255) / 256, 8192));
+  hipLaunchKernelGGL((aq_smallm_finish<BF16, GROUPED>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -289,8 +388,8 @@ SmallmPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped) {
   const int want = std::max(1, 256 / std::max(1, slabs));  // about one workgroup per CU
   // whole units per split, a multiple of kWaves units when the range allows (balance)
   const int per = (k + want - 1) / want;
-  const int step = per >= kWaves * kUnit ? kWaves * kUnit : kUnit;
-  p.kchunk = std::max(kUnit, (per + step - 1) / step * step);
+  const int step = per >= kWaves * kRows ? kWaves * kRows : kRows;
+  p.kchunk = std::max(kRows, (per + step - 1) / step * step);
   p.splits = std::max(1, (k + p.kchunk - 1) / p.kchunk);
   return p;
 }

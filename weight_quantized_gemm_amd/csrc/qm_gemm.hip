@@ -74,18 +74,42 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
     const int p = lane & 15;
     b_off[j] = (uint32_t)(r * N + 16 * (2 * pair_slot<kRB>(r, p >> 1) + (p & 1)));
   }
+  // A stage's loads are formed once (stage_rsrc) and issued in two halves, one behind
+  // each 32-k step of the k-step that issues them, so that the texture unit is not handed
+  // a burst of loads that stalls the waves' matrix-core work.
+  struct StageRsrc {
+    u32x4_t ra, rb;
+    uint8_t* st;
+    int k0;
+    bool tail;
+  };
+  auto stage_rsrc = [&](int ks) {
+    StageRsrc r;
+    r.k0 = ks * kBK;
+    r.st = smem + (ks % kStages) * kStage;
+    r.ra = make_rsrc(x1b + r.k0, x1_bytes - r.k0);
+    const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
+    r.rb = make_rsrc32(x2b + (int64_t)r.k0 * N, (uint32_t)(rows * N - n0));
+    r.tail = r.k0 + kBK > K;
+    return r;
+  };
+  // half h of a stage: x1 blocks j with j % 2 == h, weight blocks j with j % 2 == h
+  auto issue_half = [&](const StageRsrc& r, int h) {
+#pragma unroll
+    for (int j = 0; j < kAper; ++j) {
+      if (j % 2 != h) continue;
+      uint8_t* dst = r.st + 1024 * (wave + kWaves * j);
+      if (!r.tail) dma16(r.ra, dst, a_off[j]);
+      else dma16(r.ra, dst, r.k0 + 16 * a_chunk[j] >= K ? kOOB : a_off[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kBper; ++j)
+      if (j % 2 == h) dma16(r.rb, r.st + kAbytes + 1024 * (wave + kWaves * j), b_off[j]);
+  };
   auto issue = [&](int ks) {
-    uint8_t* st = smem + (ks % kStages) * kStage;
-    const int k0 = ks * kBK;
-    const u32x4_t ra = make_rsrc(x1b + k0, x1_bytes - k0);
-    const bool tail = k0 + kBK > K;
-#pragma unroll
-    for (int j = 0; j < kAper; ++j)
-      dma16(ra, st + 1024 * (wave + kWaves * j),
-            (tail && k0 + 16 * a_chunk[j] >= K) ? kOOB : a_off[j]);
-    const u32x4_t rb = make_rsrc(x2b + (int64_t)k0 * N, (int64_t)(K - k0) * N - n0);
-#pragma unroll
-    for (int j = 0; j < kBper; ++j) dma16(rb, st + kAbytes + 1024 * (wave + kWaves * j), b_off[j]);
+    const StageRsrc r = stage_rsrc(ks);
+    issue_half(r, 0);
+    issue_half(r, 1);
   };
 
   i32x16_t acc[kWM][kWN];
@@ -126,7 +150,9 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
     if (ahead == 2) stage_barrier<2 * kDma>();
     else if (ahead == 1) stage_barrier<kDma>();
     else stage_barrier<0>();
-    if (ks + kStages - 1 < nk) issue(ks + kStages - 1);
+    const bool more = ks + kStages - 1 < nk;
+    StageRsrc nr{};
+    if (more) nr = stage_rsrc(ks + kStages - 1);
     if (ks == nk - 1) {  // no DMA left: start the epilogue's x3 reads under the last MFMAs
       prefetch_x3(0, 0);
       if (kWM > 1) prefetch_x3(1, 1);
@@ -155,6 +181,7 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
       for (int i = 0; i < kWM; ++i)
 #pragma unroll
         for (int j = 0; j < kWN; ++j) acc[i][j] = mfma32x32x32_i8(af[i], bfr[j], acc[i][j]);
+      if (more) issue_half(nr, kk);  // behind this step's matrix-core work
     }
   }
 

@@ -43,8 +43,10 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
   if (pl.small_m) {
     const bool grouped = p.mode == QuantMode::kGroup;
     pl.sm = aq_smallm_plan(p.m, (int)p.k, (int)p.n, (int)p.group, grouped);
-    pl.partial_bytes = align_up((int64_t)pl.sm.splits * p.m * p.n * (int64_t)sizeof(float));
-    pl.rowsum_bytes = grouped ? 0 : align_up((int64_t)pl.sm.splits * p.m * (int64_t)sizeof(float));
+    if (pl.sm.splits > 1) {
+      pl.partial_bytes = align_up((int64_t)pl.sm.splits * p.m * p.n * (int64_t)sizeof(float));
+      pl.rowsum_bytes = grouped ? 0 : align_up((int64_t)pl.sm.splits * p.m * (int64_t)sizeof(float));
+    }
   }
   pl.workspace = pl.partial_bytes + pl.rowsum_bytes;
   return pl;
@@ -148,8 +150,9 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
     return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
   }
   if (pl.small_m) {
-    a.partial = (float*)workspace;
-    a.rowsum_part = pl.rowsum_bytes ? (float*)((char*)workspace + pl.partial_bytes) : nullptr;
+    char* w = (char*)workspace;
+    a.partial = pl.partial_bytes ? (float*)w : nullptr;
+    a.rowsum_part = pl.rowsum_bytes ? (float*)(w + pl.partial_bytes) : nullptr;
     e = wq::launch_aq_smallm(a, s);
   } else {
     e = wq::launch_aq_gemm(a, s);  // row sums are formed in-kernel; no workspace
