@@ -17,7 +17,7 @@
 // weight tile of the k-step in which their group ends, so a fold reads them from LDS and
 // never waits on a global load (which would also wait for every stage in flight).
 //
-// Pipeline: GM x GN waves, wave tile (32*WM) x (32*WN), workgroup tile 256 x (32*WN*GN),
+// Pipeline: GM x GN waves, wave tile (32*WM) x (32*WN), workgroup tile (32*WM*GM) x (32*WN*GN),
 // BK = 64.  Operands travel global -> LDS by direct-to-LDS buffer loads
 // (no registers, out-of-range lanes read zero) through 3 LDS stages, one barrier per
 // k-step.  x1 tiles are row-major with a 16-byte-chunk XOR swizzle and are read as MFMA A
@@ -33,24 +33,24 @@ namespace wq {
 namespace {
 
 constexpr int kBK = 64;
-constexpr int kStages = 3;
 constexpr int kArow = 128;                 // bytes per x1 row in a stage (64 x 16-bit)
-constexpr int kAbytes = 256 * kArow;       // 32 KiB: 256 rows of x1
 
 template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
 struct Tile {
   static constexpr int Waves = GM * GN;              // wave grid GM x GN
   static constexpr int Threads = 64 * Waves;
-  static constexpr int BM = 32 * WM * GM;            // 256 rows
+  static constexpr int BM = 32 * WM * GM;            // rows of the workgroup tile
+  static constexpr int Abytes = BM * kArow;          // x1 stage
   static constexpr int BN = 32 * WN * GN;            // logical columns
   static constexpr int RB = W4 ? BN / 2 : BN;        // weight bytes per k row
   static constexpr int Bbytes = kBK * RB;
-  static constexpr int Pbytes = GROUPED ? 1024 : 0;  // per-group scale / offset rows
-  static constexpr int Stage = kAbytes + Bbytes + Pbytes;
+  // per-group scale and offset rows of the two groups a k-step can close
+  static constexpr int Pbytes = GROUPED ? (BN > 128 ? 2048 : 1024) : 0;
+  static constexpr int Stage = Abytes + Bbytes + Pbytes;
   static constexpr int Win = 256 / RB;               // k rows per 256-byte bank window
   static constexpr int PairMask = 8 / Win - 1;       // swizzle span of 32-byte pairs
   static constexpr int RowsPerKB = 1024 / RB;        // k rows per 1 KiB DMA block
-  static constexpr int Ablocks = kAbytes / 1024;     // 32
+  static constexpr int Ablocks = Abytes / 1024;      // 1 KiB DMA blocks of x1
   static constexpr int Bblocks = Bbytes / 1024;      // DMA blocks per stage (weights)
   static constexpr int Aper = Ablocks / Waves;
   // weights: Bblocks spread over the first Bblocks waves when there are fewer blocks
@@ -59,16 +59,37 @@ struct Tile {
   static constexpr int Pwave = Waves - 1;            // issues the group-parameter loads
   static constexpr int WCols = 32 * WN;              // logical columns per wave
   static constexpr int Reads = W4 ? WN / 2 : WN;     // tr8 reads per wave per 16-k step
-  // LDS layout: stages (x1 | weights | group parameters) | S rows (BM fp32) | per-wave group-sum scratch (Waves x 32*WM fp32)
-  static constexpr int SOff = kStages * Stage;
+  // LDS layout: stages (x1 | weights | group parameters) | S rows (BM fp32) | per-wave
+  // group-sum scratch (Waves x 32*WM fp32).  As many stages as fit (3 to 6): a deeper
+  // pipeline hides more load latency where a stage is small.
+  static constexpr int Extra = BM * 4 + Waves * 32 * WM * 4;
+  static constexpr int FitStages = (160 * 1024 - Extra) / Stage;
+  static constexpr int Stages = FitStages > 6 ? 6 : FitStages;
+  static constexpr int SOff = Stages * Stage;
   static constexpr int GOff = SOff + BM * 4;
   static constexpr int Total = GOff + Waves * 32 * WM * 4;
-  static_assert(BM == 256, "x1 stage holds 256 rows");
+  static_assert(Stages >= 3, "at least three stages");
+  static_assert(BM == 128 || BM == 256, "x1 stage holds 128 or 256 rows");
   static_assert(Ablocks % Waves == 0, "x1 DMA blocks split evenly over the waves");
   static_assert(Bblocks % Waves == 0 || Bblocks < Waves, "weight DMA blocks split");
   static_assert(Win >= 1 && Win <= 4, "weight row bytes 64..256");
   static_assert(!W4 || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
 };
+
+// Stage barrier allowing `ahead` later stages (OWN loads each) to stay in flight, for a
+// run-time ahead in [0, MAXA].
+template <int OWN, int MAXA>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if constexpr (MAXA > 0) {
+    if (ahead >= MAXA) {
+      stage_barrier<OWN * MAXA>();
+      return;
+    }
+    wait_stage<OWN, MAXA - 1>(ahead);
+  } else {
+    stage_barrier<0>();
+  }
+}
 
 // One 16-k step of MFMA operands for a wave: WM x1 fragments (16-byte reads) and the raw
 // weight bytes of its tr8 reads.
@@ -107,7 +128,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   constexpr int wn = WNI;
   int tm, tn;
   tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * 256;
+  const int64_t m0 = (int64_t)tm * T::BM;
   const int n0 = tn * BN;
   const int64_t M = a.m;
   const int K = a.k, N = a.n;
@@ -119,8 +140,8 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   // slot).  The per-lane byte offsets inside a stage do not depend on k: they are formed
   // once, and each k-step only moves the (scalar) buffer base.
   const uint8_t* x1b = (const uint8_t*)a.x1 + m0 * K * 2;
-  // bytes of x1 from the tile's first row on that the tile may read (at most 256 rows)
-  const uint32_t x1_bytes = (uint32_t)((M - m0 < 256 ? M - m0 : 256) * K * 2);
+  // bytes of x1 from the tile's first row on that the tile may read (at most BM rows)
+  const uint32_t x1_bytes = (uint32_t)((M - m0 < T::BM ? M - m0 : T::BM) * K * 2);
   const int nb0 = W4 ? n0 / 2 : n0;
   const uint8_t* x2b = (const uint8_t*)a.x2 + nb0;
   uint32_t a_off[T::Aper];
@@ -167,7 +188,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   auto stage_rsrc = [&](int ks) {
     StageRsrc r;
     r.k0 = ks * kBK;
-    r.st = smem + (ks % kStages) * T::Stage;
+    r.st = smem + (ks % T::Stages) * T::Stage;
     r.ra = make_rsrc32(x1b + (int64_t)r.k0 * 2, x1_bytes - (uint32_t)r.k0 * 2);
     const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
     r.rb = make_rsrc32(x2b + (int64_t)r.k0 * x2_pitch, (uint32_t)(rows * x2_pitch - nb0));
@@ -183,13 +204,13 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     }
   };
   auto issue_b = [&](const StageRsrc& r, int j) {
-    dma16(r.rb, r.st + kAbytes + 1024 * (wave + T::Waves * j), b_off[j]);
+    dma16(r.rb, r.st + T::Abytes + 1024 * (wave + T::Waves * j), b_off[j]);
   };
   auto issue_p = [&](const StageRsrc& r) {
     if constexpr (GROUPED) {
       const int ga = min((r.k0 + 31) / a.group, a.groups - 1);
       const int gb = min((r.k0 + 63) / a.group, a.groups - 1);
-      dma_group_params<BN>(r.st + kAbytes + T::Bbytes, rsc, rof, has_offset, ga, gb, N, lane);
+      dma_group_params<BN>(r.st + T::Abytes + T::Bbytes, rsc, rof, has_offset, ga, gb, N, lane);
     }
   };
   // the items of 16-k step kk: x1 blocks j with j % 4 == kk, weight blocks j with
@@ -262,7 +283,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     for (int j = 0; j < WN; ++j) {
       const int lc = block_col(j) - n0;
       const float sv = act_to_f32<BF16>(Ps[e * BN + lc]);
-      const float ov = act_to_f32<BF16>(Ps[256 + e * BN + lc]);
+      const float ov = act_to_f32<BF16>(Ps[T::Pbytes / 4 + e * BN + lc]);
       s[j] = sv;
       q[j] = sv * (ov - cbias);
     }
@@ -279,9 +300,8 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
             tot[i][j][r] = fmaf(s[j], acc[i][j][r], fmaf(q[j], sr[e], tot[i][j][r]));
           }
       }
-#pragma unroll
-      for (int j = 0; j < WN; ++j) acc[i][j] = f32x16_t{};
     }
+    // acc is not cleared: the next group's first MFMA starts from zero
   };
 
   // ---------------------------------------------------------------- epilogue geometry
@@ -309,25 +329,24 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   };
 
   // ---------------------------------------------------------------- main loop
-  issue(0);
-  if (nk > 1) issue(1);
+  constexpr int S = T::Stages;
+  for (int ks = 0; ks < S - 1 && ks < nk; ++ks) issue(ks);
   for (int ks = 0; ks < nk; ++ks) {
-    // stage ks is complete once only the next stage's loads may still be in flight
-    if (ks + 1 == nk) stage_barrier<0>();
-    else if (has_b && has_p) stage_barrier<kOwnA + kOwnB + kOwnP>();
-    else if (has_b) stage_barrier<kOwnA + kOwnB>();
-    else if (has_p) stage_barrier<kOwnA + kOwnP>();
-    else stage_barrier<kOwnA>();
-    const bool more = ks + 2 < nk;
-    StageRsrc nr{};
-    if (more) nr = stage_rsrc(ks + 2);
+    // stage ks is complete once only the stages issued after it may still be in flight
+    const int ahead = min(S - 2, nk - 1 - ks);
+    if (has_b && has_p) wait_stage<kOwnA + kOwnB + kOwnP, S - 2>(ahead);
+    else if (has_b) wait_stage<kOwnA + kOwnB, S - 2>(ahead);
+    else if (has_p) wait_stage<kOwnA + kOwnP, S - 2>(ahead);
+    else wait_stage<kOwnA, S - 2>(ahead);
+    const bool more = ks + S - 1 < nk;
+    const StageRsrc nr = stage_rsrc(ks + S - 1);  // scalar work; unused on the last steps
     if (ks == nk - 1) {  // no DMA left: start the epilogue's x3 reads under the last MFMAs
       prefetch_x3(0, 0);
       if (XP > 1 && WM > 1) prefetch_x3(1, 1 % XP);
     }
 
-    const uint8_t* As = smem + (ks % kStages) * T::Stage;
-    const uint8_t* Bs = As + kAbytes;
+    const uint8_t* As = smem + (ks % T::Stages) * T::Stage;
+    const uint8_t* Bs = As + T::Abytes;
     // Fragments are double-buffered across the four 16-k steps: the reads of step kk + 1
     // are issued before the MFMAs of step kk, so LDS latency hides behind them.
     Frag<WM, T::Reads> f0, f1;
@@ -361,10 +380,24 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
         if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
         else bfr[j] = i8x8_to_act<BF16>(cur.raw[j]);
       }
+      // Per-group: a group's first 16-k step (group starts fall on multiples of 32, so on
+      // steps 0 and 2) starts its accumulators from zero through the MFMA's own operand
+      // instead of clearing them after the previous group's fold.
+      bool fresh = false;
+      if constexpr (GROUPED) {
+        if (kk % 2 == 0) fresh = (ks * kBK + kk * 16) % a.group == 0;
+      }
+      if (fresh) {
 #pragma unroll
-      for (int i = 0; i < WM; ++i)
+        for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], acc[i][j]);
+          for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], f32x16_t{});
+      } else {
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], acc[i][j]);
+      }
       if (more) issue_step(nr, kk);  // behind this step's matrix-core work
 
       if constexpr (GROUPED) {
@@ -488,7 +521,7 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   static_assert(GN <= 8, "wave grids have at most 8 columns");
   using T = Tile<W4, GM, GN, WM, WN, GROUPED>;
   AqArgs a = a0;
-  a.tiles_m = (int)((a.m + 255) / 256);
+  a.tiles_m = (int)((a.m + T::BM - 1) / T::BM);
   a.tiles_n = (a.n + T::BN - 1) / T::BN;
   const size_t lds = (size_t)T::Total;
   auto kern = aq_gemm_kernel<BF16, W4, GM, GN, WM, WN, GROUPED>;
@@ -505,21 +538,24 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
 
 // Tile configurations (wave grid GM x GN, blocks per wave WM x WN).  The matrix cores and
 // the VALU hardly overlap on gfx950, and one wave per SIMD leaves LDS latency exposed, so
-// the defaults run two waves per SIMD.  Index 0 is the default of each mode; the others
-// are kept for tuning.
-//   per-tensor / per-channel: 0: 2x4 waves of 128x64   1: 1x8 of 256x32   2: 1x4 of 256x64
-//                             3: 2x2 of 128x128         4: 4x2 of 64x128
-//   per-group:                0: 4x2 waves of 64x64     1: 2x2 of 128x64
-//                             2: 8x1 of 32x64 (int8)
+// the defaults run two waves per SIMD.  Per-group tiles are wide in n and short in m: the
+// x1 tile (16-bit) costs more load bandwidth per MFMA than the packed weights, and the
+// per-group accumulators (current group + folded total) leave room for 64x64 wave tiles
+// only.  Index 0 is the default of each mode; the others are kept for tuning.
+//   per-tensor / per-channel: 0: 2x4 waves of 128x64 (256x256)   1: 1x8 of 256x32
+//                             2: 1x4 of 256x64   3: 2x2 of 128x128   4: 4x2 of 64x128
+//   per-group:                0: 2x4 waves of 64x64 (128x256)   1: 4x2 of 64x64 (256x128)
+//                             2: 2x2 of 128x64 (256x128)        3: 8x1 of 32x64 (int8)
 template <bool BF16, bool W4>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   if (a.grouped) {
     switch (a.tile) {
-      case 1: return launch_one<BF16, W4, 2, 2, 4, 2, true>(a, stream);
-      case 2:
+      case 1: return launch_one<BF16, W4, 4, 2, 2, 2, true>(a, stream);
+      case 2: return launch_one<BF16, W4, 2, 2, 4, 2, true>(a, stream);
+      case 3:
         if constexpr (!W4) return launch_one<BF16, W4, 8, 1, 1, 2, true>(a, stream);
-        else return launch_one<BF16, W4, 4, 2, 2, 2, true>(a, stream);
-      default: return launch_one<BF16, W4, 4, 2, 2, 2, true>(a, stream);
+        else return launch_one<BF16, W4, 2, 4, 2, 2, true>(a, stream);
+      default: return launch_one<BF16, W4, 2, 4, 2, 2, true>(a, stream);
     }
   }
   switch (a.tile) {

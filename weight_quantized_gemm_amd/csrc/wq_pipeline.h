@@ -60,18 +60,26 @@ __device__ __forceinline__ void wave_wait() {
 // Direct-to-LDS load of the per-group scale and offset rows that a 64-row k block needs:
 // the groups ga and gb that hold its rows 31 and 63 (group ends fall on multiples of 32,
 // so these are the only groups a fold inside the block can close).  COLS 16-bit values
-// from column n0 of each row land in a 1 KiB block: scale rows at +0 and +2*COLS, offset
-// rows at +512 and +512 + 2*COLS.  Two loads per wave (one per half-wave); with no offset
-// tensor the offset half reads zeros.  rs / ro cover the tensors from column n0 on.
+// from column n0 of each row land in an LDS block: scale rows at +0 and +2*COLS, offset
+// rows at +P/2 and +P/2 + 2*COLS, where P = 1 KiB for COLS <= 128 (two loads, one per
+// half-wave) and 2 KiB for COLS == 256 (two full-wave loads).  With no offset tensor the
+// offset rows read zeros.  rs / ro cover the tensors from column n0 on.
 template <int COLS>
 __device__ __forceinline__ void dma_group_params(uint8_t* dst, const u32x4_t& rs, const u32x4_t& ro,
                                                  bool has_offset, int ga, int gb, int n, int lane) {
-  static_assert(COLS % 8 == 0 && 4 * COLS <= 512, "two rows of COLS 16-bit values per half");
-  constexpr int L = COLS / 8;  // 16-byte chunks per row
-  const int h = lane & 31, e = h / L, c = h % L;
-  const uint32_t off = h < 2 * L ? (uint32_t)(e ? gb : ga) * (uint32_t)n * 2u + 16u * (uint32_t)c : kOOB;
-  if (lane < 32) dma16(rs, dst, off);
-  else dma16(has_offset ? ro : rs, dst, has_offset ? off : kOOB);  // lands at dst + 512 + 16 h
+  if constexpr (COLS == 256) {
+    const int e = lane >> 5, c = lane & 31;  // 32 chunks of 16 bytes per row
+    const uint32_t off = (uint32_t)(e ? gb : ga) * (uint32_t)n * 2u + 16u * (uint32_t)c;
+    dma16(rs, dst, off);
+    dma16(has_offset ? ro : rs, dst + 1024, has_offset ? off : kOOB);
+  } else {
+    static_assert(COLS % 8 == 0 && 4 * COLS <= 512, "two rows of COLS 16-bit values per half");
+    constexpr int L = COLS / 8;  // 16-byte chunks per row
+    const int h = lane & 31, e = h / L, c = h % L;
+    const uint32_t off = h < 2 * L ? (uint32_t)(e ? gb : ga) * (uint32_t)n * 2u + 16u * (uint32_t)c : kOOB;
+    if (lane < 32) dma16(rs, dst, off);
+    else dma16(has_offset ? ro : rs, dst, has_offset ? off : kOOB);  // lands at dst + 512 + 16 h
+  }
 }
 
 // Direct-to-LDS load of one group's scale and offset rows (COLS 16-bit values from column
