@@ -75,6 +75,13 @@ AQ_CASES = [
                                               group_size=64)),
     ("smallm_3d_perchannel_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(2, 4, 2048), n=640,
                                           mode="channel")),
+    # the largest k and n the shape rules allow (k, n <= 65535, multiples of 32 / 64)
+    ("maxk_smallm_pergroup32_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(3, 65504), n=64, mode="group",
+                                            group_size=32)),
+    ("maxk_pergroup128_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(96, 65472), n=128, mode="group",
+                                      group_size=128, with_bias=False)),
+    ("maxn_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(40, 64), n=65504, mode="channel")),
+    ("maxn_smallm_pertensor_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(8, 64), n=65504, mode="tensor")),
 ]
 
 
@@ -148,6 +155,87 @@ def test_smallm_workspace_reuse():
         assert r["ok"], (i, r)
 
 
+def _antiquant_tensors(case):
+    act = case.act
+    return dict(x1=dev_tensor(case.x1, act), x2=dev_tensor(case.x2, "raw"), scale=dev_tensor(case.scale, act),
+                offset=dev_tensor(case.offset, act), bias=dev_tensor(case.bias, act), x3=dev_tensor(case.x3, act))
+
+
+@pytest.mark.parametrize("name,spec", [
+    ("graph_smallm_pergroup64_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(16, 2048), n=384, mode="group",
+                                             group_size=64)),
+    ("graph_largem_pergroup128_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(300, 512), n=256,
+                                              mode="group", group_size=128)),
+    ("graph_largem_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(260, 256), n=320,
+                                             mode="channel")),
+], ids=["graph_smallm_pergroup64_fp16_i8", "graph_largem_pergroup128_bf16_i4", "graph_largem_perchannel_bf16_i8"])
+def test_graph_replay_antiquant(name, spec):
+    """A prepared call captured in a HIP graph and replayed on new inputs (copied into the
+    captured buffers, with eager work and synchronisation between replays): every replay
+    equals an eager call bit for bit and passes the oracle comparison."""
+    import torch
+    import weight_quantized_gemm_amd as W
+    _announce(name)
+    cases = [workloads.make_antiquant(seed=900 + i, name=f"{name}{i}", **spec) for i in range(3)]
+    buf = _antiquant_tensors(cases[0])
+    int4 = spec["weight"] == "int4"
+    call = W.AntiquantMatmul(buf["x1"], buf["x2"], buf["scale"], buf["offset"], buf["bias"], buf["x3"],
+                             cases[0].group_size, x2_int4=int4)
+    call()  # eager warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for case in cases:
+        new = _antiquant_tensors(case)
+        for k, t in buf.items():
+            if t is not None:
+                t.copy_(new[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = call.out.clone()
+        eager = run_antiquant(case)
+        torch.cuda.synchronize()
+        assert torch.equal(replayed.view(torch.int16), eager.view(torch.int16)), case.name
+        r = oracle.compare(to_f64(replayed).reshape(case.out_shape), ref_antiquant(case), case.act)
+        assert r["ok"], (case.name, r)
+
+
+def test_graph_replay_w8a8():
+    """The W8A8 prepared call captured and replayed on new inputs, checked like the
+    anti-quant graph test (the int32 accumulator bit-exact)."""
+    import torch
+    import weight_quantized_gemm_amd as W
+    _announce("graph_w8a8")
+    cases = [workloads.make_w8a8(seed=950 + i, name=f"graph_w8a8_{i}", out="bf16", x1_shape=(300, 256), n=320)
+             for i in range(3)]
+
+    def tensors(c):
+        return dict(x1=dev_tensor(c.x1, "raw"), x2=dev_tensor(c.x2, "raw"), dq=dev_tensor(c.dequant_scale, c.dequant_dtype),
+                    pt=dev_tensor(c.pertoken_scale, "fp32"), bias=dev_tensor(c.bias, "raw"), x3=dev_tensor(c.x3, c.out))
+    buf = tensors(cases[0])
+    acc = torch.empty(cases[0].out_shape, dtype=torch.int32, device="cuda:0")
+    call = W.QuantMatmul(buf["x1"], buf["x2"], buf["dq"], buf["pt"], buf["bias"], buf["x3"], acc_out=acc)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for c in cases:
+        new = tensors(c)
+        for k, t in buf.items():
+            if t is not None:
+                t.copy_(new[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref, racc = ref_w8a8(c)
+        assert np.array_equal(acc.cpu().numpy().astype(np.int64), racc.reshape(acc.shape))
+        r = oracle.compare(to_f64(call.out).reshape(ref.shape), ref, c.out)
+        assert r["ok"], (c.name, r)
+
+
 W8A8_CASES = [
     ("w8a8_ragged_bf16", dict(out="bf16", x1_shape=(600, 288), n=544)),
     ("w8a8_fp16_tensor_nopt", dict(out="fp16", x1_shape=(300, 256), n=256, dequant="tensor",
@@ -155,6 +243,7 @@ W8A8_CASES = [
     ("w8a8_bf16dq", dict(out="bf16", x1_shape=(257, 320), n=288, dequant_dtype="bf16")),
     ("w8a8_m1", dict(out="bf16", x1_shape=(1, 128), n=64)),
     ("w8a8_3d_m3", dict(out="fp16", x1_shape=(3, 1, 256), n=96)),
+    ("w8a8_maxk", dict(out="bf16", x1_shape=(64, 65504), n=64)),
 ]
 
 
