@@ -25,11 +25,11 @@ Every function is pinned by tests that do not re-type its formula: exact rationa
 force on tiny inputs, the pages' all-ones samples in closed form, identity and
 granularity reductions, invariants and decoding of hand-written bit patterns.
 """
-from .storage import decode, decode_bf16, decode_fp16, unpack_int4
+from .storage import decode, decode_bf16, decode_fp16, decode_fp8e4m3, unpack_int4
 from .antiquant import resolve_mode, expand_params, ref_antiquant
 from .w8a8 import ref_w8a8_acc, ref_w8a8
 from .compare import compare, TOLERANCE
 
-__all__ = ["decode", "decode_bf16", "decode_fp16", "unpack_int4", "resolve_mode",
+__all__ = ["decode", "decode_bf16", "decode_fp16", "decode_fp8e4m3", "unpack_int4", "resolve_mode",
            "expand_params", "ref_antiquant", "ref_w8a8_acc", "ref_w8a8", "compare",
            "TOLERANCE"]

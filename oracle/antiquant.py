@@ -15,7 +15,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .storage import decode, unpack_int4
+from .storage import decode, decode_fp8e4m3, unpack_int4
 
 
 def resolve_mode(scale_shape, group_size: int, n: int) -> str:
@@ -57,7 +57,8 @@ def ref_antiquant(x1, x2, scale, offset=None, bias=None, x3=None, group_size: in
     """fp64 result of the anti-quant matmul, unrounded, in the output's shape.
 
     Inputs are stored arrays: x1/scale/offset/bias/x3 in ``act`` ("fp16" -> float16,
-    "bf16" -> uint16 bit patterns); x2 int8 (k, n) or packed int4 uint8 (k, n/2).
+    "bf16" -> uint16 bit patterns); x2 int8 (k, n), packed int4 uint8 (k, n/2), or
+    FLOAT8_E4M3FN bit patterns uint8 (k, n) for weight="fp8e4m3".
     None means an absent optional input: offset 0, bias 0, x3 0 ([guide] shape
     constraints: those inputs may be empty)."""
     x1f = decode(x1, act)
@@ -67,6 +68,10 @@ def ref_antiquant(x1, x2, scale, offset=None, bias=None, x3=None, group_size: in
     a = x1f.reshape(m, k)
     if weight == "int4":
         codes = unpack_int4(x2).astype(np.float64)
+    elif weight == "fp8e4m3":
+        # FLOAT8_E4M3FN weights ([guide] "支持矩阵", 950 series): the stored values enter
+        # the same formula; the guide allows them per-channel only and without an offset
+        codes = decode_fp8e4m3(x2)
     else:
         assert x2.dtype == np.int8
         codes = x2.astype(np.float64)

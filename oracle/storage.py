@@ -2,8 +2,8 @@
 
 Test infrastructure only (see the package docstring).
 
-Every fp16 and bf16 value is a dyadic rational exactly representable in fp64, and every
-int8 / int4 code is an integer, so decoding is exact: the oracle always works on the
+Every fp16, bf16 and fp8-e4m3 value is a dyadic rational exactly representable in fp64,
+and every int8 / int4 code is an integer, so decoding is exact: the oracle always works on the
 values *as stored* (for instance fp16(0.02) is 0.0200042724609375, not 0.02).
 """
 from __future__ import annotations
@@ -42,6 +42,24 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def decode_fp8e4m3(bits: np.ndarray) -> np.ndarray:
+    """FLOAT8_E4M3FN codes (uint8) -> fp64.
+
+    The 950-series weight dtype FLOAT8_E4M3FN ([guide] "支持矩阵") is the 8-bit float with
+    a sign bit, a 4-bit exponent of bias 7 and a 3-bit mantissa, finite only ("FN"):
+    exponent field 0 holds the subnormals m/8 * 2^-6; exponent fields 1..15 hold
+    (1 + m/8) * 2^(e-7), except S.1111.111, the only NaN (so the largest value is 448)."""
+    assert bits.dtype == np.uint8
+    b = bits.astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    out = sign * mag
+    out[(e == 15) & ((b & 7) == 7)] = np.nan
+    return out
+
+
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
     """Stored array of a named storage dtype -> exact fp64 values."""
     if dtype == "fp16":
@@ -55,4 +73,6 @@ def decode(a: np.ndarray, dtype: str) -> np.ndarray:
         return a.astype(np.float64)
     if dtype == "int4":
         return unpack_int4(a).astype(np.float64)
+    if dtype == "fp8e4m3":
+        return decode_fp8e4m3(a)
     raise ValueError(dtype)

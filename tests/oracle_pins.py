@@ -106,6 +106,62 @@ def pin_bruteforce_w8a8(ref_w8a8):
     assert np.all(np.abs(got - want) <= 1e-12 * np.maximum(1.0, np.abs(want)))
 
 
+# ------------------------------------------------------------------ FLOAT8_E4M3FN weights
+# bit pattern -> value, worked by hand from the format (sign | 4-bit exponent, bias 7 |
+# 3-bit mantissa; exponent 0 subnormal m/8 * 2^-6; S.1111.111 NaN)
+FP8_HAND = [(0x00, 0.0), (0x80, -0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+            (0x38, 1.0), (0x39, 1.125), (0x40, 2.0), (0xB8, -1.0), (0x7E, 448.0), (0xFE, -448.0),
+            (0x77, 240.0), (0x30, 0.5)]
+
+
+def torch_fp8_values(codes):
+    """All codes through torch's CPU float8_e4m3fn conversion (a library routine, independent
+    of the oracle's decoder)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def pin_fp8_decode(decode_fp8e4m3):
+    for code, value in FP8_HAND:
+        got = decode_fp8e4m3(np.array([code], dtype=np.uint8))[0]
+        assert got == value and np.signbit(got) == np.signbit(value), (hex(code), got, value)
+    for code in (0x7F, 0xFF):
+        assert np.isnan(decode_fp8e4m3(np.array([code], dtype=np.uint8))[0])
+    codes = np.arange(256, dtype=np.uint8)
+    got, lib = decode_fp8e4m3(codes), torch_fp8_values(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(lib))
+    fin = ~np.isnan(lib)
+    assert np.array_equal(got[fin], lib[fin])
+
+
+def fp8_codes(rng, shape):
+    """Random finite FLOAT8_E4M3FN codes (every code except the two NaNs)."""
+    c = rng.integers(0, 254, size=shape)
+    return np.where(c >= 0x7F, c + 1, c).astype(np.uint8)  # skip 0x7F, and 0xFF at the top
+
+
+def pin_bruteforce_fp8(ref_antiquant):
+    """fp8 weights, per-channel scale, no offset: the oracle against exact rationals, with
+    the weight values taken from torch's float8 conversion."""
+    for seed, act, lead, k, n in [(21, "bf16", (3,), 64, 4), (22, "fp16", (2, 2), 96, 3)]:
+        rng = np.random.default_rng(seed)
+        mb = MANT[act]
+        x1v = dyadic(rng, tuple(lead) + (k,), mb, -6, 0)
+        codes = fp8_codes(rng, (k, n))
+        sv = dyadic(rng, (n,), mb, -8, -3)
+        bv = dyadic(rng, (n,), mb, -6, -2)
+        x3v = dyadic(rng, tuple(lead) + (n,), mb, -6, -2)
+        got = ref_antiquant(encode(x1v, act), codes, encode(sv, act), None, encode(bv, act),
+                            encode(x3v, act), 0, act=act, weight="fp8e4m3")
+        wvals = torch_fp8_values(codes)
+        F = lambda a: [[Fraction(float(v)) for v in row] for row in np.asarray(a).reshape(-1, a.shape[-1])]
+        want = bruteforce.antiquant(F(x1v), F(wvals), [Fraction(float(v)) for v in sv], None,
+                                    [Fraction(float(v)) for v in bv], F(x3v), "channel", 0)
+        want = np.array([[float(v) for v in row] for row in want]).reshape(got.shape)
+        assert np.all(np.abs(got - want) <= 1e-12 * np.maximum(1.0, np.abs(want))), seed
+
+
 # ------------------------------------------------------------------ page samples
 def pin_page_sample_antiquant(ref_antiquant):
     gd = golden("page_sample_antiquant_all_ones.json")

@@ -142,3 +142,27 @@ def _w8a8_mutant(kind):
 @pytest.mark.parametrize("kind", ["bias_after_scale", "drop_pertoken", "drop_x3"])
 def test_w8a8_mutants(kind):
     assert caught([P.pin_bruteforce_w8a8, P.pin_page_sample_w8a8], _w8a8_mutant(kind)), kind
+
+
+def _fp8_mutant(kind):
+    def dec(bits):
+        b = bits.astype(np.int64)
+        sign = np.where(b >> 7, -1.0, 1.0)
+        e = (b >> 3) & 15
+        m = (b & 7).astype(np.float64)
+        bias = 8 if kind == "bias8" else 7
+        sub = 2.0 ** (-7 if kind == "subnormal_scale" else -6)
+        mag = np.where(e == 0, m / 8.0 * sub, (1.0 + m / 8.0) * np.exp2((e - bias).astype(np.float64)))
+        out = mag if kind == "no_sign" else sign * mag
+        out[(e == 15) & ((b & 7) == 7)] = np.nan
+        return out
+    return dec
+
+
+@pytest.mark.parametrize("kind", ["bias8", "subnormal_scale", "no_sign"])
+def test_fp8_decode_mutants(kind, monkeypatch):
+    bad = _fp8_mutant(kind)
+    assert caught([P.pin_fp8_decode], bad), kind
+    # through the formula too: the brute-force pin sees the mutant via the oracle
+    monkeypatch.setattr(AQ, "decode_fp8e4m3", bad)
+    assert caught([P.pin_bruteforce_fp8], oracle.ref_antiquant), kind

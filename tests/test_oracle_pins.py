@@ -56,3 +56,11 @@ def test_compare_tolerance():
     r = oracle.compare(bad, ref, "fp16")
     assert not r["ok"] and r["n_fail"] == 1 and r["worst_index"] == (2,)
     assert not oracle.compare(np.array([np.nan]), np.array([0.0]), "bf16")["ok"]
+
+
+def test_fp8_decode():
+    P.pin_fp8_decode(oracle.decode_fp8e4m3)
+
+
+def test_bruteforce_fp8():
+    P.pin_bruteforce_fp8(oracle.ref_antiquant)
