@@ -47,6 +47,8 @@ DOMINANT = {
     "pergroup128_bf16_int4_4x2048x8192x2048": ("aq_gemm_kernel", "mfma"),
     "smallm_pergroup64_fp16_int8_32x8192x8192": ("aq_smallm_kernel", "hbm"),
     "w8a8_bf16_8192x4096x8192": ("qm_gemm_kernel", "mfma"),
+    "perchannel_bf16_fp8e4m3_4096x4096x4096": ("aq_gemm_kernel", "mfma"),
+    "smallm_perchannel_bf16_fp8e4m3_32x8192x8192": ("aq_smallm_kernel", "hbm"),
 }
 CACHE_BYTES = 256 << 20
 
@@ -84,7 +86,10 @@ def make_runner(case, torch, dev, sets):
         ws = None
         for s in range(sets):
             # extra sets are copies of the same values at other addresses
-            b = dict(x1=to_dev(case.x1, act, torch, dev), x2=to_dev(case.x2, "raw", torch, dev),
+            x2 = to_dev(case.x2, "raw", torch, dev)
+            if case.weight == "fp8e4m3":
+                x2 = x2.view(torch.float8_e4m3fn)
+            b = dict(x1=to_dev(case.x1, act, torch, dev), x2=x2,
                      scale=to_dev(case.scale, act, torch, dev), offset=to_dev(case.offset, act, torch, dev),
                      bias=to_dev(case.bias, act, torch, dev), x3=to_dev(case.x3, act, torch, dev))
             b["out"] = torch.empty(case.out_shape, dtype=b["x1"].dtype, device=dev)

@@ -39,14 +39,17 @@
 extern "C" {
 #endif
 
-/* Element types.  WQ_I4 is a packed signed 4-bit type: see wq_tensor. */
+/* Element types.  WQ_I4 is a packed signed 4-bit type: see wq_tensor.  WQ_F8E4M3 is
+ * FLOAT8_E4M3FN, one byte per element: sign, 4-bit exponent of bias 7, 3-bit mantissa,
+ * no infinities, S.1111.111 the only NaN (largest finite value 448). */
 typedef enum wq_dtype {
   WQ_F16 = 1,
   WQ_BF16 = 2,
   WQ_F32 = 3,
   WQ_I8 = 4,
   WQ_I4 = 5,
-  WQ_I32 = 6
+  WQ_I32 = 6,
+  WQ_F8E4M3 = 7
 } wq_dtype;
 
 /*
@@ -82,9 +85,14 @@ typedef struct wq_tensor {
  * Arguments (guide, "aclnnWeightQuantMatmulAllReduceGetWorkspaceSize 参数详解" and
  * "约束说明 / 形状与范围约束" (shape constraints)):
  *   x1               required; WQ_F16 or WQ_BF16; (m, k) or (b, s, k); m = b*s in [1, 2^31-1].
- *   x2               required; WQ_I8 or WQ_I4; (k, n); k in [0, 65535], n in [1, 65535].
- *                    Alignment (guide, 950 format/alignment rules): int8 needs k and n
- *                    multiples of 32, int4 multiples of 64 (k = 0 is allowed).
+ *   x2               required; WQ_I8, WQ_I4 or WQ_F8E4M3; (k, n); k in [0, 65535],
+ *                    n in [1, 65535].  Alignment (guide, 950 format/alignment rules): int8
+ *                    needs k and n multiples of 32, int4 multiples of 64 (k = 0 is allowed);
+ *                    FLOAT8_E4M3FN, one byte per element like int8, multiples of 32.
+ *                    WQ_F8E4M3 weights (guide, 支持矩阵 (support matrix), 950 row, and the
+ *                    note under the 950 dtype table): per-channel scale only, no
+ *                    antiquant_offset (it must be NULL), antiquant_group_size 0.  Their
+ *                    values enter the formula as decoded; a NaN code gives NaN outputs.
  *   bias             optional; x1's dtype; (n).
  *   antiquant_scale  required; x1's dtype.  Per-tensor (1); per-channel (n) or (1, n);
  *                    per-group (ceil(k / g), n) (guide, attribute notes on

@@ -29,6 +29,8 @@ def run_antiquant(case, device="cuda:0", out=None):
     act = case.act
     x1 = dev_tensor(case.x1, act, device)
     x2 = dev_tensor(case.x2, "raw", device)
+    if case.weight == "fp8e4m3":
+        x2 = x2.view(torch_mod().float8_e4m3fn)
     args = dict(antiquant_offset=dev_tensor(case.offset, act, device),
                 bias=dev_tensor(case.bias, act, device), x3=dev_tensor(case.x3, act, device),
                 antiquant_group_size=case.group_size, x2_int4=case.weight == "int4", out=out)

@@ -82,6 +82,27 @@ AQ_CASES = [
                                       group_size=128, with_bias=False)),
     ("maxn_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(40, 64), n=65504, mode="channel")),
     ("maxn_smallm_pertensor_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(8, 64), n=65504, mode="tensor")),
+    # FLOAT8_E4M3FN weights: per-channel, no offset; codes uniform over the finite patterns
+    # (zeros of both signs, subnormals, +-448), scales of the size an fp8 weight needs
+    ("perchannel_bf16_f8_ragged", dict(act="bf16", weight="fp8e4m3", x1_shape=(600, 288), n=544, mode="channel",
+                                       with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("perchannel_fp16_f8_1xn", dict(act="fp16", weight="fp8e4m3", x1_shape=(257, 320), n=288, mode="channel",
+                                    channel_2d=True, with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("perchannel_fp16_f8_3d_nobias", dict(act="fp16", weight="fp8e4m3", x1_shape=(3, 70, 512), n=96,
+                                          mode="channel", with_offset=False, with_bias=False,
+                                          scale_dist=("uniform", 2e-4, 1e-3))),
+    ("perchannel_bf16_f8_longk", dict(act="bf16", weight="fp8e4m3", x1_shape=(256, 4096), n=256, mode="channel",
+                                      with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("smallm_m1_perchannel_bf16_f8", dict(act="bf16", weight="fp8e4m3", x1_shape=(1, 512), n=256, mode="channel",
+                                          with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("smallm_m32_perchannel_fp16_f8", dict(act="fp16", weight="fp8e4m3", x1_shape=(32, 2048), n=640,
+                                           mode="channel", with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("smallm_m7_perchannel_fp16_f8_k96", dict(act="fp16", weight="fp8e4m3", x1_shape=(7, 96), n=64, mode="channel",
+                                              with_offset=False, with_x3=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("maxk_perchannel_bf16_f8", dict(act="bf16", weight="fp8e4m3", x1_shape=(96, 65504), n=128, mode="channel",
+                                     with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("maxk_smallm_perchannel_fp16_f8", dict(act="fp16", weight="fp8e4m3", x1_shape=(3, 65504), n=64,
+                                            mode="channel", with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
 ]
 
 
@@ -117,6 +138,33 @@ def test_empty_k(act):
     case0 = workloads.make_antiquant(seed=8, act=act, weight="int8", x1_shape=(32, 0), n=128, mode="channel",
                                      with_bias=False, with_x3=False)
     assert np.all(to_f64(run_antiquant(case0)) == 0)
+
+
+@pytest.mark.parametrize("m", [4, 40])
+def test_fp8_nan_code(m):
+    """FLOAT8_E4M3FN has one NaN pattern per sign (S.1111.111).  Its decoded value enters the
+    formula like any other, so its output column is NaN on every row; the other columns
+    match the oracle.  Both the small-m (m <= 32) and the tiled path."""
+    _announce(f"fp8_nan_code_m{m}")
+    case = workloads.make_antiquant(seed=31 + m, act="bf16", weight="fp8e4m3", x1_shape=(m, 256), n=128,
+                                    mode="channel", with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))
+    case.x2[5, 7] = 0x7F
+    case.x2[200, 100] = 0xFF
+    got = to_f64(run_antiquant(case)).reshape(m, case.n)
+    ref = ref_antiquant(case).reshape(m, case.n)
+    nan_cols = [7, 100]
+    assert np.isnan(ref[:, nan_cols]).all()
+    assert np.isnan(got[:, nan_cols]).all()
+    keep = np.setdiff1d(np.arange(case.n), nan_cols)
+    r = oracle.compare(got[:, keep], ref[:, keep], case.act)
+    assert r["ok"], r
+
+
+def test_fp8_empty_k():
+    _announce("fp8_empty_k")
+    case = workloads.make_antiquant(seed=9, act="fp16", weight="fp8e4m3", x1_shape=(32, 0), n=128,
+                                    mode="channel", with_offset=False)
+    assert oracle.compare(to_f64(run_antiquant(case)), ref_antiquant(case), "fp16")["ok"]
 
 
 def test_determinism():
@@ -243,6 +291,7 @@ W8A8_CASES = [
     ("w8a8_bf16dq", dict(out="bf16", x1_shape=(257, 320), n=288, dequant_dtype="bf16")),
     ("w8a8_m1", dict(out="bf16", x1_shape=(1, 128), n=64)),
     ("w8a8_3d_m3", dict(out="fp16", x1_shape=(3, 1, 256), n=96)),
+    ("w8a8_fp16_pt_3d", dict(out="fp16", x1_shape=(2, 130, 384), n=320)),
     ("w8a8_maxk", dict(out="bf16", x1_shape=(64, 65504), n=64)),
 ]
 

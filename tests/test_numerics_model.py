@@ -7,7 +7,8 @@ is reduced):
 * naive    -- restore W = (x2 + offset) * scale and round it to the activation dtype
               before the product (what a straight dequantise-then-GEMM would feed the
               matrix cores);
-* factored -- feed the exact integer codes, accumulate in fp32 per group, apply scale
+* factored -- feed the exact weight codes (integers, or FLOAT8_E4M3FN values, which are
+              exact in fp16 and bf16 too), accumulate in fp32 per group, apply scale
               and offset in fp32: out = sum_g s_g * (P_g + off_g * S_g) + bias + x3,
               with P_g = x1_g @ codes_g and S_g the row sums of x1 over the group.
 
@@ -66,6 +67,8 @@ CASES = [
     ("perchannel_bf16_int8_4096x4096x4096", 128, 256),
     ("pergroup128_bf16_int4_4x2048x8192x2048", 128, 256),
     ("smallm_pergroup64_fp16_int8_32x8192x8192", 32, 512),
+    ("perchannel_bf16_fp8e4m3_4096x4096x4096", 128, 256),
+    ("smallm_perchannel_bf16_fp8e4m3_32x8192x8192", 32, 512),
 ]
 
 
@@ -85,7 +88,10 @@ def test_factored_identity_and_rounding(name, m, n):
                                case.group_size, act=case.act, weight=case.weight)
     ref = ref.reshape(m, n)
     x1 = oracle.decode(case.x1, case.act).reshape(m, -1)
-    codes = (oracle.unpack_int4(case.x2) if case.weight == "int4" else case.x2).astype(np.float64)
+    if case.weight == "fp8e4m3":
+        codes = oracle.decode_fp8e4m3(case.x2)
+    else:
+        codes = (oracle.unpack_int4(case.x2) if case.weight == "int4" else case.x2).astype(np.float64)
     s, o, g = _params(case)
     extra = np.zeros((m, n))
     if case.bias is not None:

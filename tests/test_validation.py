@@ -16,7 +16,8 @@ from weight_quantized_gemm_amd import make_desc
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 FAKE = 0x10000
-DT = {"fp16": W.WQ_F16, "bf16": W.WQ_BF16, "int8": W.WQ_I8, "int4": W.WQ_I4}
+DT = {"fp16": W.WQ_F16, "bf16": W.WQ_BF16, "int8": W.WQ_I8, "int4": W.WQ_I4,
+      "fp8e4m3": W.WQ_F8E4M3}
 OK, NULLPTR, INVALID = W.WQ_OK, W.WQ_ERR_PARAM_NULLPTR, W.WQ_ERR_PARAM_INVALID
 
 
@@ -133,6 +134,38 @@ def test_shapes_and_ranges(wqlib):
     assert aq(wqlib, x1, D([64, 128], W.WQ_I4), sc, out) == OK
     assert aq(wqlib, x1, D([64, 96], W.WQ_I4), D([96], f16), D([32, 96], f16)) == INVALID
     assert aq(wqlib, D([32, 96], f16), D([96, 128], W.WQ_I4), sc, out) == INVALID
+
+
+def test_fp8_weight_rules(wqlib):
+    """FLOAT8_E4M3FN weights (guide, support matrix 950 row and the note under the 950
+    dtype table): per-channel scale only, no offset; one byte per element, so k and n
+    are multiples of 32 as for int8."""
+    for act in ("fp16", "bf16"):
+        a = DT[act]
+        x1, x2, sc, out = base(act=act, w="fp8e4m3")
+        assert aq(wqlib, x1, x2, sc, out) == OK                                     # (n)
+        assert aq(wqlib, x1, x2, D([1, 128], a), out, bias=D([128], a), x3=D([32, 128], a)) == OK
+        assert aq(wqlib, x1, x2, D([1], a), out) == INVALID                         # per-tensor
+        assert aq(wqlib, x1, x2, D([2, 128], a), out, g=32) == INVALID              # per-group
+        assert aq(wqlib, x1, x2, sc, out, offset=D([128], a)) == INVALID            # offset
+        # the same shapes with int8 weights are all accepted
+        x2i = D([64, 128], W.WQ_I8)
+        assert aq(wqlib, x1, x2i, D([1], a), out) == OK
+        assert aq(wqlib, x1, x2i, D([2, 128], a), out, g=32) == OK
+        assert aq(wqlib, x1, x2i, sc, out, offset=D([128], a)) == OK
+    f16 = W.WQ_F16
+    x1, x2, sc, out = base(w="fp8e4m3")
+    assert aq(wqlib, D([32, 96], f16), D([96, 128], W.WQ_F8E4M3), sc, out) == OK   # k % 32
+    assert aq(wqlib, D([32, 48], f16), D([48, 128], W.WQ_F8E4M3), sc, out) == INVALID
+    assert aq(wqlib, x1, D([64, 112], W.WQ_F8E4M3), D([112], f16), D([32, 112], f16)) == INVALID
+    # an offset with fp8 weights is refused whatever its shape; a null data pointer in it is
+    # still a null-pointer error, as those are checked first
+    assert aq(wqlib, x1, x2, sc, out, offset=D([7], f16)) == INVALID
+    assert aq(wqlib, x1, x2, sc, out, offset=D([128], f16, 0)) == NULLPTR
+    # empty K keeps the per-channel rule
+    x1e, x2e = D([32, 0], f16, 0), D([0, 128], W.WQ_F8E4M3, 0)
+    assert aq(wqlib, x1e, x2e, D([128], f16), D([32, 128], f16)) == OK
+    assert aq(wqlib, x1e, x2e, D([0, 128], f16, 0), D([32, 128], f16), g=64) == INVALID
 
 
 def test_empty_k(wqlib):

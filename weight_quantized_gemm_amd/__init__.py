@@ -22,13 +22,13 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
-__all__ = ["WQ_F16", "WQ_BF16", "WQ_F32", "WQ_I8", "WQ_I4", "WQ_I32", "WQ_OK",
+__all__ = ["WQ_F16", "WQ_BF16", "WQ_F32", "WQ_I8", "WQ_I4", "WQ_I32", "WQ_F8E4M3", "WQ_OK",
            "WQ_ERR_PARAM_NULLPTR", "WQ_ERR_PARAM_INVALID", "WQ_ERR_RUNTIME", "WqTensor",
            "WqError", "lib", "library_path", "make_desc", "antiquant_matmul",
            "antiquant_workspace_size", "quant_matmul", "quant_workspace_size", "AntiquantMatmul",
            "QuantMatmul", "profile_next_call", "EXPORTS"]
 
-WQ_F16, WQ_BF16, WQ_F32, WQ_I8, WQ_I4, WQ_I32 = 1, 2, 3, 4, 5, 6
+WQ_F16, WQ_BF16, WQ_F32, WQ_I8, WQ_I4, WQ_I32, WQ_F8E4M3 = 1, 2, 3, 4, 5, 6, 7
 WQ_OK, WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID, WQ_ERR_RUNTIME = 0, 161001, 161002, 561001
 
 EXPORTS = ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul",
@@ -115,7 +115,7 @@ def _torch():
 def _dtype_code(t) -> int:
     torch = _torch()
     m = {torch.float16: WQ_F16, torch.bfloat16: WQ_BF16, torch.float32: WQ_F32,
-         torch.int8: WQ_I8, torch.int32: WQ_I32}
+         torch.int8: WQ_I8, torch.int32: WQ_I32, torch.float8_e4m3fn: WQ_F8E4M3}
     if t.dtype not in m:
         raise ValueError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
@@ -217,8 +217,9 @@ def antiquant_matmul(x1, x2, antiquant_scale, antiquant_offset=None, bias=None, 
     """out = x1 @ ((x2 + antiquant_offset) * antiquant_scale) + bias + x3 on x1's device.
 
     x1: fp16/bf16 (m, k) or (b, s, k); x2: int8 (k, n), or with ``x2_int4`` a uint8 (k, n/2)
-    tensor of packed signed nibbles (even column in the low nibble); scale/offset: (1),
-    (n), (1, n) or (ceil(k/g), n) for group size g.  Returns the output tensor."""
+    tensor of packed signed nibbles (even column in the low nibble), or float8_e4m3fn (k, n)
+    with a per-channel scale and no offset; scale/offset: (1), (n), (1, n) or (ceil(k/g), n)
+    for group size g.  Returns the output tensor."""
     return AntiquantMatmul(x1, x2, antiquant_scale, antiquant_offset, bias, x3, antiquant_group_size,
                            x2_int4=x2_int4, out=out, workspace=workspace)(stream)
 

@@ -10,7 +10,8 @@
 //   P_g[m,n] = sum_{i in group g} x1[m,i] * (x2[i,n] + C),   S_g[m] = sum_{i in g} x1[m,i]
 //
 // C is the constant bias of the fed weight images (136 for bf16/int4, 0 otherwise).  The
-// matrix cores see only exact 16-bit images of the integer codes and x1; scale and offset
+// matrix cores see only exact 16-bit images of the weight codes (int8, int4 or
+// FLOAT8_E4M3FN, all exact in fp16 and bf16) and x1; scale and offset
 // are applied in fp32 on the accumulators, per group at each group end, or once in the
 // epilogue for per-tensor / per-channel parameters.  S_g is summed in-kernel from the x1
 // fragments (v_dot2 against ones).  Per-group scale and offset rows travel with the
@@ -21,11 +22,15 @@
 // BK = 64.  Operands travel global -> LDS by direct-to-LDS buffer loads
 // (no registers, out-of-range lanes read zero) through 3 LDS stages, one barrier per
 // k-step.  x1 tiles are row-major with a 16-byte-chunk XOR swizzle and are read as MFMA A
-// fragments by ds_read_b128.  Weight tiles stay raw (int8 or packed int4, n-contiguous,
+// fragments by ds_read_b128.  Weight tiles stay raw (one-byte codes or packed int4, n-contiguous,
 // 32-byte-pair XOR swizzle); B fragments come from ds_read_b64_tr_b8 (8 consecutive k of
 // one column per lane) and are turned into exact 16-bit images in registers.  The
 // epilogue stages fp32 results through LDS so that x3, bias and the output move in
 // 16-byte row-contiguous accesses.
+//
+// This header holds the kernel templates; aq_gemm_int8.hip, aq_gemm_int4.hip and
+// aq_gemm_fp8.hip instantiate them, one weight format per translation unit.
+#pragma once
 #include "wq_kernels.h"
 #include "wq_pipeline.h"
 
@@ -119,8 +124,9 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
 
 // The kernel body, specialised on the wave's column index WNI in the GM x GN wave grid:
 // column offsets and the per-channel row-sum block become compile-time constants.
-template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED, int WNI>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, int WNI>
 __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int wave) {
+  constexpr bool W4 = WF == kWInt4;
   using T = Tile<W4, GM, GN, WM, WN, GROUPED>;
   constexpr int BN = T::BN, RB = T::RB, WC = T::WCols;
   const int lane = threadIdx.x & 63;
@@ -378,7 +384,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
 #pragma unroll
       for (int j = 0; j < T::Reads; ++j) {
         if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
-        else bfr[j] = i8x8_to_act<BF16>(cur.raw[j]);
+        else bfr[j] = w8x8_to_act<BF16, WF>(cur.raw[j]);
       }
       // Per-group: a group's first 16-k step (group starts fall on multiples of 32, so on
       // steps 0 and 2) starts its accumulators from zero through the MFMA's own operand
@@ -499,7 +505,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   }
 }
 
-template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED>
 __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
@@ -507,7 +513,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #define WQ_WAVE_COLUMN(c)                                                      \
   if constexpr (GN > c) {                                                     \
     if (wn == c) {                                                            \
-      aq_gemm_body<BF16, W4, GM, GN, WM, WN, GROUPED, c>(a, smem, wave);       \
+      aq_gemm_body<BF16, WF, GM, GN, WM, WN, GROUPED, c>(a, smem, wave);       \
       return;                                                                 \
     }                                                                         \
   }
@@ -516,15 +522,15 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #undef WQ_WAVE_COLUMN
 }
 
-template <bool BF16, bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED>
 hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   static_assert(GN <= 8, "wave grids have at most 8 columns");
-  using T = Tile<W4, GM, GN, WM, WN, GROUPED>;
+  using T = Tile<WF == kWInt4, GM, GN, WM, WN, GROUPED>;
   AqArgs a = a0;
   a.tiles_m = (int)((a.m + T::BM - 1) / T::BM);
   a.tiles_n = (a.n + T::BN - 1) / T::BN;
   const size_t lds = (size_t)T::Total;
-  auto kern = aq_gemm_kernel<BF16, W4, GM, GN, WM, WN, GROUPED>;
+  auto kern = aq_gemm_kernel<BF16, WF, GM, GN, WM, WN, GROUPED>;
   hipError_t e = raise_lds_limit((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
@@ -533,8 +539,6 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return profile_end(stream);
 }
-
-}  // namespace
 
 // Tile configurations (wave grid GM x GN, blocks per wave WM x WN).  The matrix cores and
 // the VALU hardly overlap on gfx950, and one wave per SIMD leaves LDS latency exposed, so
@@ -546,32 +550,31 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
 //                             2: 1x4 of 256x64   3: 2x2 of 128x128   4: 4x2 of 64x128
 //   per-group:                0: 2x4 waves of 64x64 (128x256)   1: 4x2 of 64x64 (256x128)
 //                             2: 2x2 of 128x64 (256x128)        3: 8x1 of 32x64 (int8)
-template <bool BF16, bool W4>
+template <bool BF16, int WF>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
-  if (a.grouped) {
-    switch (a.tile) {
-      case 1: return launch_one<BF16, W4, 4, 2, 2, 2, true>(a, stream);
-      case 2: return launch_one<BF16, W4, 2, 2, 4, 2, true>(a, stream);
-      case 3:
-        if constexpr (!W4) return launch_one<BF16, W4, 8, 1, 1, 2, true>(a, stream);
-        else return launch_one<BF16, W4, 2, 4, 2, 2, true>(a, stream);
-      default: return launch_one<BF16, W4, 2, 4, 2, 2, true>(a, stream);
+  constexpr bool W4 = WF == kWInt4;
+  if constexpr (WF != kWFp8) {  // FLOAT8_E4M3FN weights come per-channel only
+    if (a.grouped) {
+      switch (a.tile) {
+        case 1: return launch_one<BF16, WF, 4, 2, 2, 2, true>(a, stream);
+        case 2: return launch_one<BF16, WF, 2, 2, 4, 2, true>(a, stream);
+        case 3:
+          if constexpr (!W4) return launch_one<BF16, WF, 8, 1, 1, 2, true>(a, stream);
+          else return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
+        default: return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
+      }
     }
   }
   switch (a.tile) {
     case 1:
-      if constexpr (!W4) return launch_one<BF16, W4, 1, 8, 8, 1, false>(a, stream);
-      else return launch_one<BF16, W4, 2, 4, 4, 2, false>(a, stream);
-    case 2: return launch_one<BF16, W4, 1, 4, 8, 2, false>(a, stream);
-    case 3: return launch_one<BF16, W4, 2, 2, 4, 4, false>(a, stream);
-    case 4: return launch_one<BF16, W4, 4, 2, 2, 4, false>(a, stream);
-    default: return launch_one<BF16, W4, 2, 4, 4, 2, false>(a, stream);
+      if constexpr (!W4) return launch_one<BF16, WF, 1, 8, 8, 1, false>(a, stream);
+      else return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
+    case 2: return launch_one<BF16, WF, 1, 4, 8, 2, false>(a, stream);
+    case 3: return launch_one<BF16, WF, 2, 2, 4, 4, false>(a, stream);
+    case 4: return launch_one<BF16, WF, 4, 2, 2, 4, false>(a, stream);
+    default: return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
   }
 }
 
-hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream) {
-  if (a.bf16) return a.w4 ? launch_mode<true, true>(a, stream) : launch_mode<true, false>(a, stream);
-  return a.w4 ? launch_mode<false, true>(a, stream) : launch_mode<false, false>(a, stream);
-}
-
+}  // namespace
 }  // namespace wq

@@ -3,7 +3,7 @@
 //
 //   out = x1 @ ((x2 + offset) * scale) + bias + x3
 // ("CANN ops-transformer ... aclnnWeightQuantMatmulAllReduce 完全指南", section 计算公式),
-// evaluated in the same factored form as the large-m kernel (aq_gemm.hip).
+// evaluated in the same factored form as the large-m kernel (aq_gemm.h).
 //
 // Work split: a workgroup owns a 128-column slab of x2 and a contiguous k range (split-k).
 // Its 8 waves (two per SIMD, so that one wave's LDS, matrix-core and VALU latencies hide
@@ -48,8 +48,9 @@ struct SmTile {
   static_assert(Lds <= 160 * 1024, "one workgroup per CU");
 };
 
-template <bool BF16, bool W4, bool GROUPED>
+template <bool BF16, int WF, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) {
+  constexpr bool W4 = WF == kWInt4;
   using T = SmTile<W4, GROUPED>;
   constexpr int RB = T::RB;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
           acc[2 * p] = mfma32x32x16<BF16>(af[kk], ev, acc[2 * p]);
           acc[2 * p + 1] = mfma32x32x16<BF16>(af[kk], od, acc[2 * p + 1]);
         } else {
-          acc[p] = mfma32x32x16<BF16>(af[kk], i8x8_to_act<BF16>(braw[kk][p]), acc[p]);
+          acc[p] = mfma32x32x16<BF16>(af[kk], w8x8_to_act<BF16, WF>(braw[kk][p]), acc[p]);
         }
       }
 #pragma unroll
@@ -361,11 +362,11 @@ __global__ __launch_bounds__(256) void aq_smallm_finish(const AqArgs a) {
   }
 }
 
-template <bool BF16, bool W4, bool GROUPED>
+template <bool BF16, int WF, bool GROUPED>
 hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
-  using T = SmTile<W4, GROUPED>;
+  using T = SmTile<WF == kWInt4, GROUPED>;
   const int slabs = (a.n + kSlab - 1) / kSlab;
-  auto kern = aq_smallm_kernel<BF16, W4, GROUPED>;
+  auto kern = aq_smallm_kernel<BF16, WF, GROUPED>;
   hipError_t e = raise_lds_limit((const void*)kern, T::Lds);
   if (e != hipSuccess) return e;
   if ((e = profile_begin(stream)) != hipSuccess) return e;
@@ -395,12 +396,14 @@ SmallmPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped) {
 }
 
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream) {
+  // FLOAT8_E4M3FN weights come per-channel only
+  if (a.f8) return a.bf16 ? launch_sm<true, kWFp8, false>(a, stream) : launch_sm<false, kWFp8, false>(a, stream);
   if (a.bf16) {
-    if (a.w4) return a.grouped ? launch_sm<true, true, true>(a, stream) : launch_sm<true, true, false>(a, stream);
-    return a.grouped ? launch_sm<true, false, true>(a, stream) : launch_sm<true, false, false>(a, stream);
+    if (a.w4) return a.grouped ? launch_sm<true, kWInt4, true>(a, stream) : launch_sm<true, kWInt4, false>(a, stream);
+    return a.grouped ? launch_sm<true, kWInt8, true>(a, stream) : launch_sm<true, kWInt8, false>(a, stream);
   }
-  if (a.w4) return a.grouped ? launch_sm<false, true, true>(a, stream) : launch_sm<false, true, false>(a, stream);
-  return a.grouped ? launch_sm<false, false, true>(a, stream) : launch_sm<false, false, false>(a, stream);
+  if (a.w4) return a.grouped ? launch_sm<false, kWInt4, true>(a, stream) : launch_sm<false, kWInt4, false>(a, stream);
+  return a.grouped ? launch_sm<false, kWInt8, true>(a, stream) : launch_sm<false, kWInt8, false>(a, stream);
 }
 
 }  // namespace wq

@@ -136,7 +136,7 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.x3 = p.x3; a.out = p.out;
   a.m = p.m; a.k = (int32_t)p.k; a.n = (int32_t)p.n;
   a.group = (int32_t)p.group; a.groups = (int32_t)p.groups;
-  a.bf16 = p.act == WQ_BF16; a.w4 = p.w4;
+  a.bf16 = p.act == WQ_BF16; a.w4 = p.w4; a.f8 = p.f8;
   a.grouped = p.mode == wq::QuantMode::kGroup;
   a.per_tensor = p.mode == wq::QuantMode::kTensor;
   a.code_bias = wq::code_bias(p);

@@ -48,6 +48,9 @@ __device__ __forceinline__ uint16_t f32_to_act(float f) {
 }
 
 // ----------------------------------------------------------------------------- code images
+// Weight storage formats (a kernel template parameter).
+enum WFmt : int { kWInt8 = 0, kWInt4 = 1, kWFp8 = 2 };
+
 // Every int8 and int4 weight code is exact in fp16 and in bf16.  The conversions below turn
 // packed codes into 16-bit floating images, two per dword, in the byte order of the input
 // (consecutive k after a tr8 transpose read).  bf16 images of int4 codes are biased by a
@@ -87,6 +90,33 @@ __device__ __forceinline__ u32x4_t i8x8_to_act(u32x2_t d) {
     i8x4_to_f16(d[1], o[2], o[3]);
   }
   return u32x4_t{o[0], o[1], o[2], o[3]};
+}
+
+// 8 FLOAT8_E4M3FN codes of one column, consecutive k -> an MFMA B fragment.  E4M3FN
+// values have 3 mantissa bits and magnitudes from 2^-9 to 448, so each is exact in bf16 and
+// in fp16; gfx950 converts two codes (one half of a dword) per instruction, here with a unit
+// scale, which leaves the values unchanged.
+template <bool BF16>
+__device__ __forceinline__ u32x4_t f8x8_to_act(u32x2_t d) {
+  uint32_t o[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if constexpr (BF16) {
+      o[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[h], 1.0f, false));
+      o[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[h], 1.0f, true));
+    } else {
+      o[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[h], 1.0f, false));
+      o[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[h], 1.0f, true));
+    }
+  }
+  return u32x4_t{o[0], o[1], o[2], o[3]};
+}
+
+// 8 one-byte codes (int8 or FLOAT8_E4M3FN) of one column -> an MFMA B fragment.
+template <bool BF16, int WF>
+__device__ __forceinline__ u32x4_t w8x8_to_act(u32x2_t d) {
+  if constexpr (WF == kWFp8) return f8x8_to_act<BF16>(d);
+  else return i8x8_to_act<BF16>(d);
 }
 
 // 8 bytes of packed int4 (two adjacent columns, consecutive k: a tr8 read of a packed

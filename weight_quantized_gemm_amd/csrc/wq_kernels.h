@@ -25,7 +25,7 @@ struct AqArgs {
   int32_t tiles_m, tiles_n;
   int32_t tile;          // tile configuration index (0 = default)
   float code_bias;       // C: the fed weight image is code + C
-  bool bf16, w4, grouped, per_tensor;
+  bool bf16, w4, f8, grouped, per_tensor;  // f8: FLOAT8_E4M3FN weights
 };
 
 // W8A8 matmul.
@@ -53,7 +53,14 @@ hipError_t raise_lds_limit(const void* kernel, int bytes);
 hipError_t profile_begin(hipStream_t stream);
 hipError_t profile_end(hipStream_t stream);
 
-hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream);
+// large-m kernels, one translation unit per weight format
+hipError_t launch_aq_gemm_int8(const AqArgs& a, hipStream_t stream);
+hipError_t launch_aq_gemm_int4(const AqArgs& a, hipStream_t stream);
+hipError_t launch_aq_gemm_fp8(const AqArgs& a, hipStream_t stream);
+inline hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream) {
+  if (a.f8) return launch_aq_gemm_fp8(a, stream);
+  return a.w4 ? launch_aq_gemm_int4(a, stream) : launch_aq_gemm_int8(a, stream);
+}
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream);  // k == 0
 hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);

@@ -13,6 +13,7 @@ struct AntiquantProblem {
   int64_t m = 0, k = 0, n = 0;
   int32_t act = WQ_F16;      // WQ_F16 | WQ_BF16 (x1, scale, offset, bias, x3, output)
   bool w4 = false;           // x2 is packed int4
+  bool f8 = false;           // x2 is FLOAT8_E4M3FN (per-channel, no offset)
   QuantMode mode = QuantMode::kTensor;
   int64_t group = 0;         // group size along k (per-group); k for tensor/channel
   int64_t groups = 1;        // ceil(k / group)

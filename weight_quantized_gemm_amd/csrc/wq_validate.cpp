@@ -13,7 +13,10 @@
 //  * shapes and ranges -- guide, 形状与范围约束 and 空 tensor 支持度 (empty tensors);
 //    W8A8 -- aclnnQuantMatmulAllReduceV2, Constraints;
 //  * alignment -- guide, 产品相关的格式与对齐约束 (950: int8 needs n, k multiples of 32,
-//    int4 multiples of 64).
+//    int4 multiples of 64).  The text is silent on FLOAT8_E4M3FN; being one byte per
+//    element like int8, it takes int8's multiple of 32;
+//  * FLOAT8_E4M3FN weights -- guide, 支持矩阵 (950 row) and the note under the 950 dtype
+//    table: per-channel only and no antiquantOffset.
 #include <climits>
 #include <cstddef>
 
@@ -83,9 +86,11 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
   // 2. dtypes
   const int32_t act = x1->dtype;
   if (act != WQ_F16 && act != WQ_BF16) return WQ_ERR_PARAM_INVALID;
-  if (x2->dtype != WQ_I8 && x2->dtype != WQ_I4) return WQ_ERR_PARAM_INVALID;
+  if (x2->dtype != WQ_I8 && x2->dtype != WQ_I4 && x2->dtype != WQ_F8E4M3) return WQ_ERR_PARAM_INVALID;
   for (const wq_tensor* t : {scale, output, offset, bias, x3})
     if (t && t->dtype != act) return WQ_ERR_PARAM_INVALID;
+  const bool f8 = x2->dtype == WQ_F8E4M3;
+  if (f8 && offset) return WQ_ERR_PARAM_INVALID;  // fp8 weights take no offset
 
   // 3. attributes (the group size rule needs k, the last dimension of x1)
   for (const wq_tensor* t : {x1, x2, scale, output, offset, bias, x3})
@@ -97,6 +102,7 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
     if (group_size % 32 != 0 || group_size < 32 || group_size > hi) return WQ_ERR_PARAM_INVALID;
   }
   if (group_size < 0) return WQ_ERR_PARAM_INVALID;
+  if (f8 && group_size != 0) return WQ_ERR_PARAM_INVALID;  // fp8 weights: per-channel only
 
   // 4. shapes
   if (x1->ndim != 2 && x1->ndim != 3) return WQ_ERR_PARAM_INVALID;
@@ -142,6 +148,7 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
     return WQ_ERR_PARAM_INVALID;
   }
   if (offset && !same_shape(offset, scale)) return WQ_ERR_PARAM_INVALID;
+  if (f8 && mode != QuantMode::kChannel) return WQ_ERR_PARAM_INVALID;
 
   // layout: row-major contiguous only; no output aliasing
   for (const wq_tensor* t : {x1, x2, scale, output, offset, bias, x3})
@@ -150,7 +157,7 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
     if (aliases(output->data, t)) return WQ_ERR_PARAM_INVALID;
 
   if (p) {
-    p->m = m; p->k = k; p->n = n; p->act = act; p->w4 = w4; p->mode = mode;
+    p->m = m; p->k = k; p->n = n; p->act = act; p->w4 = w4; p->f8 = f8; p->mode = mode;
     p->group = group; p->groups = groups;
     p->x1 = x1->data; p->x2 = x2->data; p->scale = scale->data;
     p->offset = offset ? offset->data : nullptr;

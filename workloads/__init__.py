@@ -14,6 +14,9 @@ Storage conventions
 * int4  -> ``numpy.uint8`` of shape (k, n/2): two signed two's-complement nibbles per
   byte along n, the even column in the low nibble.
 * int8 / int32 / fp32 -> the matching numpy dtype.
+* fp8e4m3 (FLOAT8_E4M3FN) -> ``numpy.uint8`` bit patterns.  Weight codes are drawn
+  uniformly over the 254 finite patterns (every pattern except S.1111.111, the NaN), so a
+  case covers zeros of both signs, subnormals and the largest magnitude 448.
 
 Draw order (one ``numpy.random.Generator(PCG64(seed))`` per case):
 anti-quant: x1, x2, antiquant_scale, antiquant_offset, bias, x3;
@@ -67,9 +70,9 @@ class AntiquantCase:
     """One anti-quant problem, every array in its storage format."""
     name: str
     act: str                      # "fp16" | "bf16"
-    weight: str                   # "int8" | "int4"
+    weight: str                   # "int8" | "int4" | "fp8e4m3"
     x1: np.ndarray                # (m, k) or (b, s, k)
-    x2: np.ndarray                # int8 (k, n) or packed uint8 (k, n/2)
+    x2: np.ndarray                # int8 (k, n), packed uint8 (k, n/2) or fp8 bits uint8 (k, n)
     n: int
     scale: np.ndarray             # (1,), (n,), (1, n) or (ceil(k/g), n)
     offset: Optional[np.ndarray]
@@ -154,13 +157,16 @@ def make_antiquant(*, seed: int, act: str, weight: str, x1_shape, n: int, mode: 
                    x3_dist=("normal", 0.0, 0.1), with_x3=True,
                    x1_dist=("normal", 0.0, 1.0), channel_2d=False, name="") -> AntiquantCase:
     """Draw one anti-quant case.  ``mode`` is "tensor", "channel" or "group"."""
-    assert act in ACT_DTYPES and weight in ("int8", "int4")
+    assert act in ACT_DTYPES and weight in ("int8", "int4", "fp8e4m3")
     rng = np.random.Generator(np.random.PCG64(seed))
     x1_shape = tuple(int(d) for d in x1_shape)
     k = x1_shape[-1]
     x1 = encode(_dist(rng, x1_dist, x1_shape), act)
     if weight == "int8":
         x2 = rng.integers(-128, 127, size=(k, n), endpoint=True, dtype=np.int8)
+    elif weight == "fp8e4m3":
+        r = rng.integers(0, 253, size=(k, n), endpoint=True, dtype=np.int16)
+        x2 = (r + (r >= 0x7F)).astype(np.uint8)   # 0..0x7E, 0x80..0xFE: no NaN pattern
     else:
         x2 = pack_int4(rng.integers(-8, 7, size=(k, n), endpoint=True, dtype=np.int8))
     if mode == "tensor":
@@ -201,8 +207,8 @@ def make_w8a8(*, seed: int, out: str, x1_shape, n: int, dequant: str = "channel"
 
 
 # --------------------------------------------------------------------------- named workloads
-# The five workloads the library is measured on, named by what they are.  The seed of the
-# i-th (1-based) is 1000 + i.
+# The workloads the library is measured on, named by what they are.  The seed of the i-th
+# (1-based) is 1000 + i.
 WORKLOADS = {
     "tiny_pertensor_fp16_int8_16x256x256": dict(
         kind="antiquant", seed=1001, act="fp16", weight="int8", x1_shape=(16, 256), n=256,
@@ -223,6 +229,16 @@ WORKLOADS = {
     "w8a8_bf16_8192x4096x8192": dict(
         kind="w8a8", seed=1005, out="bf16", x1_shape=(8192, 4096), n=8192, dequant="channel",
         dequant_dtype="fp32"),
+    # FLOAT8_E4M3FN weights (per-channel, no offset) on the shapes of the second and the
+    # fourth workload
+    "perchannel_bf16_fp8e4m3_4096x4096x4096": dict(
+        kind="antiquant", seed=1006, act="bf16", weight="fp8e4m3", x1_shape=(4096, 4096), n=4096,
+        mode="channel", scale_dist=("uniform", 2e-4, 1e-3), with_offset=False,
+        bias_dist=("normal", 0.0, 0.1), x3_dist=("normal", 0.0, 0.1)),
+    "smallm_perchannel_bf16_fp8e4m3_32x8192x8192": dict(
+        kind="antiquant", seed=1007, act="bf16", weight="fp8e4m3", x1_shape=(32, 8192), n=8192,
+        mode="channel", scale_dist=("uniform", 2e-4, 1e-3), with_offset=False,
+        bias_dist=("normal", 0.0, 0.1), with_x3=False),
 }
 
 
