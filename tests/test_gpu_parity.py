@@ -82,6 +82,18 @@ AQ_CASES = [
                                       group_size=128, with_bias=False)),
     ("maxn_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(40, 64), n=65504, mode="channel")),
     ("maxn_smallm_pertensor_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(8, 64), n=65504, mode="tensor")),
+    # m >= 1024: several row tiles share each weight tile (ragged m and n tiles; k not a
+    # multiple of 64; the largest k and n at this m)
+    ("largem_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(1100, 288), n=544, mode="channel")),
+    ("largem_pertensor_fp16_i4", dict(act="fp16", weight="int4", x1_shape=(1030, 256), n=320, mode="tensor")),
+    ("largem_perchannel_fp16_i8_3d_nooff", dict(act="fp16", weight="int8", x1_shape=(2, 600, 384), n=256,
+                                                mode="channel", channel_2d=True, with_offset=False)),
+    ("largem_perchannel_bf16_i4_nox3", dict(act="bf16", weight="int4", x1_shape=(1280, 640), n=192, mode="channel",
+                                            with_x3=False, with_bias=False)),
+    ("largem_maxk_perchannel_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(1024, 65504), n=64,
+                                            mode="channel")),
+    ("largem_maxn_pertensor_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(1024, 64), n=65504,
+                                           mode="tensor")),
     # FLOAT8_E4M3FN weights: per-channel, no offset; codes uniform over the finite patterns
     # (zeros of both signs, subnormals, +-448), scales of the size an fp8 weight needs
     ("perchannel_bf16_f8_ragged", dict(act="bf16", weight="fp8e4m3", x1_shape=(600, 288), n=544, mode="channel",
@@ -101,6 +113,11 @@ AQ_CASES = [
                                               with_offset=False, with_x3=False, scale_dist=("uniform", 2e-4, 1e-3))),
     ("maxk_perchannel_bf16_f8", dict(act="bf16", weight="fp8e4m3", x1_shape=(96, 65504), n=128, mode="channel",
                                      with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("largem_perchannel_bf16_f8", dict(act="bf16", weight="fp8e4m3", x1_shape=(1500, 512), n=96, mode="channel",
+                                       with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("largem_perchannel_fp16_f8_1xn", dict(act="fp16", weight="fp8e4m3", x1_shape=(1060, 320), n=288,
+                                           mode="channel", channel_2d=True, with_offset=False,
+                                           scale_dist=("uniform", 2e-4, 1e-3))),
     ("maxk_smallm_perchannel_fp16_f8", dict(act="fp16", weight="fp8e4m3", x1_shape=(3, 65504), n=64,
                                             mode="channel", with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
 ]
@@ -140,11 +157,12 @@ def test_empty_k(act):
     assert np.all(to_f64(run_antiquant(case0)) == 0)
 
 
-@pytest.mark.parametrize("m", [4, 40])
+@pytest.mark.parametrize("m", [4, 40, 1100])
 def test_fp8_nan_code(m):
     """FLOAT8_E4M3FN has one NaN pattern per sign (S.1111.111).  Its decoded value enters the
     formula like any other, so its output column is NaN on every row; the other columns
-    match the oracle.  Both the small-m (m <= 32) and the tiled path."""
+    match the oracle.  The small-m path (m <= 32) and the tiled path, with one and with
+    several row tiles."""
     _announce(f"fp8_nan_code_m{m}")
     case = workloads.make_antiquant(seed=31 + m, act="bf16", weight="fp8e4m3", x1_shape=(m, 256), n=128,
                                     mode="channel", with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))

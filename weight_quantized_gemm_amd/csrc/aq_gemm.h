@@ -546,10 +546,10 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
 // x1 tile (16-bit) costs more load bandwidth per MFMA than the packed weights, and the
 // per-group accumulators (current group + folded total) leave room for 64x64 wave tiles
 // only.  Index 0 is the default of each mode; the others are kept for tuning.
-//   per-tensor / per-channel: 0: 2x4 waves of 128x64 (256x256)   1: 1x8 of 256x32
-//                             2: 1x4 of 256x64   3: 2x2 of 128x128   4: 4x2 of 64x128
+//   per-tensor / per-channel: 0: 2x4 waves of 128x64 (256x256)   1: 1x8 of 256x32 (int8)
+//                             2: 4x2 of 64x128
 //   per-group:                0: 2x4 waves of 64x64 (128x256)   1: 4x2 of 64x64 (256x128)
-//                             2: 2x2 of 128x64 (256x128)        3: 8x1 of 32x64 (int8)
+//                             2: 8x1 of 32x64 (int8)
 template <bool BF16, int WF>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   constexpr bool W4 = WF == kWInt4;
@@ -557,8 +557,7 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
     if (a.grouped) {
       switch (a.tile) {
         case 1: return launch_one<BF16, WF, 4, 2, 2, 2, true>(a, stream);
-        case 2: return launch_one<BF16, WF, 2, 2, 4, 2, true>(a, stream);
-        case 3:
+        case 2:
           if constexpr (!W4) return launch_one<BF16, WF, 8, 1, 1, 2, true>(a, stream);
           else return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
         default: return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
@@ -569,9 +568,7 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
     case 1:
       if constexpr (!W4) return launch_one<BF16, WF, 1, 8, 8, 1, false>(a, stream);
       else return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
-    case 2: return launch_one<BF16, WF, 1, 4, 8, 2, false>(a, stream);
-    case 3: return launch_one<BF16, WF, 2, 2, 4, 4, false>(a, stream);
-    case 4: return launch_one<BF16, WF, 4, 2, 2, 4, false>(a, stream);
+    case 2: return launch_one<BF16, WF, 4, 2, 2, 4, false>(a, stream);
     default: return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
   }
 }
