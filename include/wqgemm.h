@@ -58,12 +58,16 @@ typedef enum wq_dtype {
  *   dtype   a wq_dtype.
  *   ndim    1, 2 or 3.
  *   shape   logical shape; entries past ndim are ignored.
- *   stride  element strides of the logical shape.  This version accepts row-major
- *           contiguous tensors only (stride[ndim-1] == 1, stride[i] == stride[i+1]*shape[i+1]);
- *           anything else is WQ_ERR_PARAM_INVALID.
- * WQ_I4 weights: logical shape (k, n); storage is k rows of n/2 bytes; each byte holds two
- * signed two's-complement nibbles along n, bits 0-3 = even column, bits 4-7 = odd column.
- * Strides of a WQ_I4 tensor are given in logical elements (row stride n).
+ *   stride  element strides of the logical shape.  Tensors must be row-major contiguous
+ *           (stride[ndim-1] == 1, stride[i] == stride[i+1]*shape[i+1]; strides of extents 1
+ *           are ignored), with one exception: the weight x2 (and, per-group, the anti-quant
+ *           scale and offset with it) may be the transpose of a row-major tensor, i.e. logical
+ *           shape (k, n) with strides (1, k).  Anything else is WQ_ERR_PARAM_INVALID.
+ * WQ_I4 weights: logical shape (k, n); two signed two's-complement nibbles per byte along the
+ * storage's contiguous axis, the even index in bits 0-3.  Row-major: k rows of n/2 bytes,
+ * nibbles along n.  Transposed: n rows of k/2 bytes, nibbles along k (this library's choice;
+ * the pages fix no int4 packing).  Strides of a WQ_I4 tensor are given in logical elements
+ * ((n, 1) row-major, (1, k) transposed).
  * An optional input is absent when its descriptor pointer is NULL.
  */
 typedef struct wq_tensor {
@@ -93,11 +97,15 @@ typedef struct wq_tensor {
  *                    note under the 950 dtype table): per-channel scale only, no
  *                    antiquant_offset (it must be NULL), antiquant_group_size 0.  Their
  *                    values enter the formula as decoded; a NaN code gives NaN outputs.
+ *                    x2 may be transposed (strides (1, k): storage (n, k), or (n, k/2)
+ *                    bytes for int4) (guide, 参数说明 and its notes on contiguity).
  *   bias             optional; x1's dtype; (n).
  *   antiquant_scale  required; x1's dtype.  Per-tensor (1); per-channel (n) or (1, n);
  *                    per-group (ceil(k / g), n) (guide, attribute notes on
- *                    IsAntiquantScaleShapeValid).
- *   antiquant_offset optional; x1's dtype; the scale's shape.  Absent means 0.
+ *                    IsAntiquantScaleShapeValid).  Per-group with a transposed x2, scale and
+ *                    offset are transposed too (strides (1, ceil(k / g))); per-group with a
+ *                    row-major x2 they are row-major (guide, 参数说明).
+ *   antiquant_offset optional; x1's dtype; the scale's shape and layout.  Absent means 0.
  *   x3               optional; x1's dtype; the output's shape.
  *   antiquant_group_size  0 = not per-group; otherwise a multiple of 32 in
  *                    [32, min(k - 1, INT32_MAX)].  Not checked when k == 0.
@@ -120,9 +128,10 @@ int wq_antiquant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor*
  * WQ_ERR_PARAM_INVALID.  Returns WQ_ERR_RUNTIME if a launch fails.
 
  *
- * Workspace contents: none are expected on entry; the small-m path (m <= 32) with its
+ * Workspace contents: none are expected on entry.  The small-m path (m <= 32) with its
  * k split over several workgroups keeps the fp32 partial sums there until a finishing
- * kernel of the same call has added them.
+ * kernel of the same call has added them; per-group scale and offset given transposed are
+ * copied there, row-major, before the product.
  */
 int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
                         const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,
@@ -133,7 +142,10 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
  * Workspace size of wq_quant_matmul (the W8A8 sibling).
  * Arguments (aclnnQuantMatmulAllReduceV2, "Parameters" table and "Constraints"):
  *   x1              required; WQ_I8; (m, k) or (b, s, k); m in [1, 2^31-1]; k in [1, 65535].
- *   x2              required; WQ_I8; (k, n); n in [1, 65535]; k and n multiples of 32.
+ *   x2              required; WQ_I8; (k, n); k and n multiples of 32.  Row-major with n in
+ *                   [1, 65535], or transposed (strides (1, k): storage (n, k)) with n in
+ *                   [1, 2^23] (Parameters table: only the last two axes may be swapped;
+ *                   Constraints: n may exceed 65535 only when x2 is transposed).
  *   bias            optional; WQ_I32; (n).  Added to the int32 accumulator before scaling.
  *   x3              optional; the output's dtype and shape.
  *   dequant_scale   required; WQ_F32 or WQ_BF16; (1), (n) or (1, n).

@@ -53,20 +53,28 @@ def expand_params(p: np.ndarray, mode: str, k: int, n: int, group_size: int) -> 
 
 
 def ref_antiquant(x1, x2, scale, offset=None, bias=None, x3=None, group_size: int = 0, *,
-                  act: str, weight: str, n: int | None = None) -> np.ndarray:
+                  act: str, weight: str, n: int | None = None,
+                  x2_transposed: bool = False) -> np.ndarray:
     """fp64 result of the anti-quant matmul, unrounded, in the output's shape.
 
     Inputs are stored arrays: x1/scale/offset/bias/x3 in ``act`` ("fp16" -> float16,
     "bf16" -> uint16 bit patterns); x2 int8 (k, n), packed int4 uint8 (k, n/2), or
     FLOAT8_E4M3FN bit patterns uint8 (k, n) for weight="fp8e4m3".
     None means an absent optional input: offset 0, bias 0, x3 0 ([guide] shape
-    constraints: those inputs may be empty)."""
+    constraints: those inputs may be empty).
+
+    ``x2_transposed``: x2 is stored as the transpose, (n, k) (int4: (n, k/2) bytes, two
+    nibbles per byte along k, the even k in the low nibble), and per-group scale and offset
+    are stored transposed with it, (groups, n) -> (n, groups) ([guide] 参数说明: in the
+    per-group case they are transposed together with x2).  The logical operands, and so
+    the result, are those of the untransposed call."""
     x1f = decode(x1, act)
     lead = x1f.shape[:-1]
     k = x1f.shape[-1]
     m = int(np.prod(lead))
     a = x1f.reshape(m, k)
     if weight == "int4":
+        # the packing runs along the storage's contiguous axis in either layout
         codes = unpack_int4(x2).astype(np.float64)
     elif weight == "fp8e4m3":
         # FLOAT8_E4M3FN weights ([guide] "支持矩阵", 950 series): the stored values enter
@@ -75,6 +83,8 @@ def ref_antiquant(x1, x2, scale, offset=None, bias=None, x3=None, group_size: in
     else:
         assert x2.dtype == np.int8
         codes = x2.astype(np.float64)
+    if x2_transposed:
+        codes = codes.T
     assert codes.shape[0] == k
     n_ = codes.shape[1]
     if n is not None:
@@ -83,10 +93,14 @@ def ref_antiquant(x1, x2, scale, offset=None, bias=None, x3=None, group_size: in
 
     y = np.zeros((m, n), dtype=np.float64)
     if k > 0:
-        mode = resolve_mode(scale.shape, group_size, n)
-        s_full = expand_params(decode(scale, act), mode, k, n, group_size)
-        o_full = (np.zeros((k, n)) if offset is None
-                  else expand_params(decode(offset, act), mode, k, n, group_size))
+        sp, op = scale, offset
+        if x2_transposed and group_size != 0:
+            sp = scale.T
+            op = None if offset is None else offset.T
+        mode = resolve_mode(sp.shape, group_size, n)
+        s_full = expand_params(decode(sp, act), mode, k, n, group_size)
+        o_full = (np.zeros((k, n)) if op is None
+                  else expand_params(decode(op, act), mode, k, n, group_size))
         w = (codes + o_full) * s_full          # add first, then multiply
         y = a @ w
     # k == 0: the product is empty and the output is bias + x3 ([guide] "空 tensor 支持度").

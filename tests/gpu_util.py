@@ -31,10 +31,18 @@ def run_antiquant(case, device="cuda:0", out=None):
     x2 = dev_tensor(case.x2, "raw", device)
     if case.weight == "fp8e4m3":
         x2 = x2.view(torch_mod().float8_e4m3fn)
-    args = dict(antiquant_offset=dev_tensor(case.offset, act, device),
+    scale = dev_tensor(case.scale, act, device)
+    offset = dev_tensor(case.offset, act, device)
+    if case.x2_transposed:
+        # transposed storage is handed over as the (k, n) transpose view, as a caller would
+        x2 = x2.t()
+        if case.group_size:
+            scale = scale.t()
+            offset = None if offset is None else offset.t()
+    args = dict(antiquant_offset=offset,
                 bias=dev_tensor(case.bias, act, device), x3=dev_tensor(case.x3, act, device),
                 antiquant_group_size=case.group_size, x2_int4=case.weight == "int4", out=out)
-    y = W.antiquant_matmul(x1, x2, dev_tensor(case.scale, act, device), **args)
+    y = W.antiquant_matmul(x1, x2, scale, **args)
     return y
 
 
@@ -44,7 +52,7 @@ def ref_antiquant(case, rows=None):
     else:
         c = sample_rows(case, rows)
     return oracle.ref_antiquant(c.x1, c.x2, c.scale, c.offset, c.bias, c.x3, c.group_size,
-                                act=c.act, weight=c.weight)
+                                act=c.act, weight=c.weight, x2_transposed=c.x2_transposed)
 
 
 def sample_rows(case, rows):
@@ -64,6 +72,8 @@ def run_w8a8(case, device="cuda:0", with_acc=True):
     torch = torch_mod()
     x1 = dev_tensor(case.x1, "raw", device)
     x2 = dev_tensor(case.x2, "raw", device)
+    if case.x2_transposed:
+        x2 = x2.t()
     dq = dev_tensor(case.dequant_scale, case.dequant_dtype, device)
     pt = dev_tensor(case.pertoken_scale, "fp32", device)
     bias = dev_tensor(case.bias, "raw", device)
@@ -77,7 +87,7 @@ def run_w8a8(case, device="cuda:0", with_acc=True):
 def ref_w8a8(case, rows=None):
     c = case if rows is None else sample_rows(case, rows)
     return oracle.ref_w8a8(c.x1, c.x2, c.dequant_scale, c.pertoken_scale, c.bias, c.x3,
-                           dequant_dtype=c.dequant_dtype, out=c.out)
+                           dequant_dtype=c.dequant_dtype, out=c.out, x2_transposed=c.x2_transposed)
 
 
 def sampled_rows(m, count=48, seed=0):

@@ -106,6 +106,62 @@ def pin_bruteforce_w8a8(ref_w8a8):
     assert np.all(np.abs(got - want) <= 1e-12 * np.maximum(1.0, np.abs(want)))
 
 
+# ------------------------------------------------------------------ transposed x2
+def transposed_storage(stored, logical, weight):
+    """The same logical operands stored transposed: x2 as (n, k) (int4: (n, k/2) bytes,
+    nibbles along k), per-group scale and offset as (n, groups)."""
+    st = dict(stored)
+    codes = np.array(logical["codes"], dtype=np.int64)
+    if weight == "int4":
+        st["x2"] = pack_int4(np.ascontiguousarray(codes.T).astype(np.int8))
+    else:
+        st["x2"] = np.ascontiguousarray(stored["x2"].T)
+    if logical["mode"] == "group":
+        st["scale"] = np.ascontiguousarray(stored["scale"].T)
+        if stored["offset"] is not None:
+            st["offset"] = np.ascontiguousarray(stored["offset"].T)
+    return st
+
+
+def pin_bruteforce_transposed(ref_antiquant):
+    """Every tiny case again with x2 (and per-group parameters) stored transposed, against
+    the same exact brute force on the logical values."""
+    for seed, act, weight, lead, k, n, mode, g in TINY_CASES:
+        st, lg = tiny_antiquant_case(seed, act, weight, lead, k, n, mode, g)
+        tt = transposed_storage(st, lg, weight)
+        got = ref_antiquant(tt["x1"], tt["x2"], tt["scale"], tt["offset"], tt["bias"], tt["x3"],
+                            g, act=act, weight=weight, x2_transposed=True)
+        want = bruteforce.antiquant(lg["x1"], lg["codes"], lg["scale"], lg["offset"], lg["bias"],
+                                    lg["x3"], mode, g)
+        want = np.array([[float(v) for v in row] for row in want]).reshape(got.shape)
+        assert np.all(np.abs(got - want) <= 1e-12 * np.maximum(1.0, np.abs(want))), seed
+
+
+def pin_int4_kpacked(ref_antiquant):
+    """Transposed int4 storage written by hand: one column (n = 1) of k = 4 codes packed
+    along k, bytes 0x21, 0xF8 -> codes 1, 2, -8, -1; with x1 = (1, 10, 100, 1000) and unit
+    scale the output is 1 + 20 - 800 - 1000 = -1779."""
+    x1 = np.array([[1, 10, 100, 1000]], dtype=np.float16)
+    x2 = np.array([[0x21, 0xF8]], dtype=np.uint8)
+    y = ref_antiquant(x1, x2, np.ones(1, np.float16), None, None, None, 0, act="fp16",
+                      weight="int4", x2_transposed=True)
+    assert y.tolist() == [[-1779.0]], y
+
+
+def pin_bruteforce_w8a8_transposed(ref_w8a8):
+    rng = np.random.default_rng(12)
+    m, k, n = 4, 96, 3
+    x1 = rng.integers(-128, 128, size=(m, k)).astype(np.int8)
+    x2 = rng.integers(-128, 128, size=(k, n)).astype(np.int8)
+    dqv = dyadic(rng, (1,), 20, -14, -10)
+    got, acc = ref_w8a8(x1, np.ascontiguousarray(x2.T), dqv.astype(np.float32), None, None, None,
+                        dequant_dtype="fp32", out="fp16", x2_transposed=True)
+    wacc, wout = bruteforce.w8a8(x1.tolist(), x2.tolist(), None, [Fraction(float(dqv[0]))], None, None)
+    assert np.array_equal(acc, np.array(wacc, dtype=np.int64))
+    want = np.array([[float(v) for v in r] for r in wout])
+    assert np.all(np.abs(got - want) <= 1e-12 * np.maximum(1.0, np.abs(want)))
+
+
 # ------------------------------------------------------------------ FLOAT8_E4M3FN weights
 # bit pattern -> value, worked by hand from the format (sign | 4-bit exponent, bias 7 |
 # 3-bit mantissa; exponent 0 subnormal m/8 * 2^-6; S.1111.111 NaN)

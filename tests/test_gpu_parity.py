@@ -94,6 +94,34 @@ AQ_CASES = [
                                             mode="channel")),
     ("largem_maxn_pertensor_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(1024, 64), n=65504,
                                            mode="tensor")),
+    # x2 stored transposed, (n, k) (int4 packed along k), handed over as its (k, n) transpose
+    # view; per-group scale and offset transposed with it
+    ("xt_perchannel_bf16_i8_ragged", dict(act="bf16", weight="int8", x1_shape=(600, 288), n=544, mode="channel",
+                                          x2_transposed=True)),
+    ("xt_pergroup128_fp16_i4_3d", dict(act="fp16", weight="int4", x1_shape=(2, 150, 512), n=320, mode="group",
+                                       group_size=128, x2_transposed=True)),
+    ("xt_pergroup96_bf16_i8_partial", dict(act="bf16", weight="int8", x1_shape=(280, 320), n=160, mode="group",
+                                           group_size=96, x2_transposed=True)),
+    ("xt_pertensor_bf16_i4_nooff", dict(act="bf16", weight="int4", x1_shape=(260, 256), n=192, mode="tensor",
+                                        with_offset=False, x2_transposed=True)),
+    ("xt_perchannel_fp16_f8", dict(act="fp16", weight="fp8e4m3", x1_shape=(257, 320), n=288, mode="channel",
+                                   with_offset=False, scale_dist=("uniform", 2e-4, 1e-3), x2_transposed=True)),
+    ("xt_largem_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(1100, 288), n=544,
+                                          mode="channel", x2_transposed=True)),
+    ("xt_smallm_pergroup64_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(32, 1024), n=384, mode="group",
+                                          group_size=64, offset_dist=("uniform", -4, 4), with_x3=False,
+                                          x2_transposed=True)),
+    ("xt_smallm_m3_pergroup128_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(3, 1024), n=256, mode="group",
+                                              group_size=128, x2_transposed=True)),
+    ("xt_smallm_m8_pergroup64_bf16_i8_k96", dict(act="bf16", weight="int8", x1_shape=(8, 96), n=64, mode="group",
+                                                 group_size=64, x2_transposed=True)),
+    ("xt_smallm_m1_perchannel_bf16_f8", dict(act="bf16", weight="fp8e4m3", x1_shape=(1, 512), n=256,
+                                             mode="channel", with_offset=False,
+                                             scale_dist=("uniform", 2e-4, 1e-3), x2_transposed=True)),
+    ("xt_maxk_smallm_pergroup32_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(3, 65504), n=64,
+                                               mode="group", group_size=32, x2_transposed=True)),
+    ("xt_maxn_perchannel_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(40, 64), n=65472, mode="channel",
+                                        x2_transposed=True)),
     # FLOAT8_E4M3FN weights: per-channel, no offset; codes uniform over the finite patterns
     # (zeros of both signs, subnormals, +-448), scales of the size an fp8 weight needs
     ("perchannel_bf16_f8_ragged", dict(act="bf16", weight="fp8e4m3", x1_shape=(600, 288), n=544, mode="channel",
@@ -311,6 +339,11 @@ W8A8_CASES = [
     ("w8a8_3d_m3", dict(out="fp16", x1_shape=(3, 1, 256), n=96)),
     ("w8a8_fp16_pt_3d", dict(out="fp16", x1_shape=(2, 130, 384), n=320)),
     ("w8a8_maxk", dict(out="bf16", x1_shape=(64, 65504), n=64)),
+    ("w8a8_xt_ragged_bf16", dict(out="bf16", x1_shape=(600, 288), n=544, x2_transposed=True)),
+    ("w8a8_xt_fp16_tensor_3d", dict(out="fp16", x1_shape=(2, 70, 256), n=96, dequant="tensor",
+                                    with_pertoken=False, x2_transposed=True)),
+    # n beyond 65535, allowed with a transposed x2 only
+    ("w8a8_xt_n70016", dict(out="bf16", x1_shape=(40, 64), n=70016, x2_transposed=True)),
 ]
 
 

@@ -166,3 +166,43 @@ def test_fp8_decode_mutants(kind, monkeypatch):
     # through the formula too: the brute-force pin sees the mutant via the oracle
     monkeypatch.setattr(AQ, "decode_fp8e4m3", bad)
     assert caught([P.pin_bruteforce_fp8], oracle.ref_antiquant), kind
+
+
+# ---------------------------------------------------------------- transposed x2
+def _transposed_mutant(kind):
+    """An oracle that turns transposed storage into row-major storage the wrong way, then
+    runs the real oracle on it."""
+    from workloads import pack_int4
+
+    def ref(x1, x2, scale, offset=None, bias=None, x3=None, group_size=0, *, act, weight, n=None,
+            x2_transposed=False):
+        if x2_transposed:
+            k = x1.shape[-1]
+            if weight == "int4":
+                codes = ST.unpack_int4(x2)                       # (n, k)
+                codes = codes.reshape(k, -1) if kind == "reshape" else codes.T
+                x2 = pack_int4(np.ascontiguousarray(codes).astype(np.int8))
+            else:
+                x2 = x2.reshape(k, -1) if kind == "reshape" else np.ascontiguousarray(x2.T)
+            if group_size:
+                # "params_kept": the parameters are not transposed back, only re-viewed
+                fix = (lambda p: p.reshape(-1, x2.shape[1] * (2 if weight == "int4" else 1))) \
+                    if kind in ("reshape", "params_kept") else (lambda p: np.ascontiguousarray(p.T))
+                scale = fix(scale)
+                offset = None if offset is None else fix(offset)
+        return AQ.ref_antiquant(x1, x2, scale, offset, bias, x3, group_size, act=act, weight=weight, n=n)
+    return ref
+
+
+@pytest.mark.parametrize("kind", ["reshape", "params_kept"])
+def test_transposed_mutants(kind):
+    bad = _transposed_mutant(kind)
+    assert caught([P.pin_bruteforce_transposed, P.pin_int4_kpacked], bad), kind
+
+
+def test_transposed_w8a8_mutant():
+    def bad(x1, x2, dq, pt=None, bias=None, x3=None, *, dequant_dtype="fp32", out="bf16", x2_transposed=False):
+        if x2_transposed:
+            x2 = x2.reshape(x1.shape[-1], -1)                   # re-viewed, not transposed
+        return W8.ref_w8a8(x1, x2, dq, pt, bias, x3, dequant_dtype=dequant_dtype, out=out)
+    assert caught([P.pin_bruteforce_w8a8_transposed], bad)

@@ -64,3 +64,15 @@ def test_fp8_decode():
 
 def test_bruteforce_fp8():
     P.pin_bruteforce_fp8(oracle.ref_antiquant)
+
+
+def test_bruteforce_transposed():
+    P.pin_bruteforce_transposed(oracle.ref_antiquant)
+
+
+def test_int4_kpacked():
+    P.pin_int4_kpacked(oracle.ref_antiquant)
+
+
+def test_bruteforce_w8a8_transposed():
+    P.pin_bruteforce_w8a8_transposed(oracle.ref_w8a8)

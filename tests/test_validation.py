@@ -168,6 +168,43 @@ def test_fp8_weight_rules(wqlib):
     assert aq(wqlib, x1e, x2e, D([0, 128], f16, 0), D([32, 128], f16), g=64) == INVALID
 
 
+def test_transposed_x2(wqlib):
+    """x2 may be the transpose of a row-major (n, k) tensor; per-group scale and offset go
+    with it (guide, 参数说明); W8A8 likewise (Parameters table), and only then may n exceed
+    65535 (Constraints)."""
+    f16, bf16 = W.WQ_F16, W.WQ_BF16
+    k, n = 64, 128
+    x1 = D([32, k], f16, FAKE + 0x100000)
+    out = D([32, n], f16, FAKE + 0x400000)
+    for wd in (W.WQ_I8, W.WQ_I4, W.WQ_F8E4M3):
+        xt = D([k, n], wd, None, [1, k])
+        assert aq(wqlib, x1, xt, D([n], f16), out) == OK
+        assert aq(wqlib, x1, xt, D([1, n], f16), out) == OK
+    xt = D([k, n], W.WQ_I8, None, [1, k])
+    assert aq(wqlib, x1, xt, D([1], f16), out, offset=D([1], f16)) == OK          # per-tensor
+    # per-group: parameters transposed with x2, and only then
+    gt, gr = D([2, n], f16, None, [1, 2]), D([2, n], f16)
+    assert aq(wqlib, x1, xt, gt, out, offset=D([2, n], f16, None, [1, 2]), g=32) == OK
+    assert aq(wqlib, x1, xt, gr, out, g=32) == INVALID
+    assert aq(wqlib, x1, xt, gt, out, offset=D([2, n], f16), g=32) == INVALID
+    xr = D([k, n], W.WQ_I8)
+    assert aq(wqlib, x1, xr, gt, out, g=32) == INVALID
+    assert aq(wqlib, x1, xr, gr, out, g=32) == OK
+    # other strided layouts stay invalid
+    assert aq(wqlib, x1, D([k, n], W.WQ_I8, None, [2 * n, 1]), D([n], f16), out) == INVALID
+    assert aq(wqlib, x1, D([k, n], W.WQ_I8, None, [1, 2 * k]), D([n], f16), out) == INVALID
+    # alignment still applies to the logical (k, n)
+    assert aq(wqlib, x1, D([k, 96], W.WQ_I4, None, [1, k]), D([96], f16), D([32, 96], f16)) == INVALID
+    # W8A8
+    i8 = W.WQ_I8
+    q1 = D([16, k], i8, FAKE + 0x100000)
+    assert qm(wqlib, q1, D([k, n], i8, None, [1, k]), D([n], W.WQ_F32), D([16, n], bf16)) == OK
+    big = 70016
+    assert qm(wqlib, q1, D([k, big], i8, None, [1, k]), D([1], W.WQ_F32), D([16, big], bf16)) == OK
+    assert qm(wqlib, q1, D([k, big], i8), D([1], W.WQ_F32), D([16, big], bf16)) == INVALID
+    assert qm(wqlib, q1, D([k, n], i8, None, [2 * n, 1]), D([n], W.WQ_F32), D([16, n], bf16)) == INVALID
+
+
 def test_empty_k(wqlib):
     f16 = W.WQ_F16
     x1, x2 = D([32, 0], f16, 0), D([0, 128], W.WQ_I8, 0)
@@ -178,8 +215,8 @@ def test_empty_k(wqlib):
 def test_layout_and_alias(wqlib):
     f16 = W.WQ_F16
     x1, x2, sc, out = base()
-    # a transposed (non-contiguous) x2 is not accepted in this version
-    assert aq(wqlib, x1, D([64, 128], W.WQ_I8, None, [1, 64]), sc, out) == INVALID
+    # a padded (non-contiguous) x2 is not accepted; its transpose is (test_transposed_x2)
+    assert aq(wqlib, x1, D([64, 128], W.WQ_I8, None, [256, 1]), sc, out) == INVALID
     # the output may not alias an input
     assert aq(wqlib, x1, x2, sc, D([32, 128], f16, FAKE + 0x100000)) == INVALID
 

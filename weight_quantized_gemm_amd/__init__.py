@@ -127,10 +127,14 @@ def _desc(t, int4: bool = False):
     if int4:
         torch = _torch()
         if t.dtype not in (torch.uint8, torch.int8) or t.dim() != 2:
-            raise ValueError("packed int4 weights are a 2-D uint8/int8 tensor of shape (k, n/2)")
-        k, half = t.shape
-        st = [t.stride(0) * 2, 1] if t.stride(1) == 1 else [t.stride(0) * 2, t.stride(1) * 2]
-        return make_desc([k, 2 * half], WQ_I4, t.data_ptr(), st)
+            raise ValueError("packed int4 weights are a 2-D uint8/int8 tensor: (k, n/2) bytes, or "
+                             "the (k/2, n) transpose view of an (n, k/2) tensor")
+        a, b = t.shape
+        if t.stride(0) == 1 and t.stride(1) == a and a > 1 and b > 1:
+            # transpose view of row-major (n, k/2) storage: logical (k, n), nibbles along k
+            return make_desc([2 * a, b], WQ_I4, t.data_ptr(), [1, 2 * a])
+        # row-major (k, n/2) storage (strides in logical elements; the library checks them)
+        return make_desc([a, 2 * b], WQ_I4, t.data_ptr(), [t.stride(0) * 2, t.stride(1)])
     return make_desc(list(t.shape), _dtype_code(t), t.data_ptr(), list(t.stride()))
 
 
@@ -170,8 +174,18 @@ def antiquant_workspace_size(x1, x2, antiquant_scale, antiquant_offset=None, bia
     return ws.value
 
 
+def _is_t_view(t) -> bool:
+    """The transpose view of a row-major 2-D tensor (strides (1, rows))."""
+    return t.dim() == 2 and t.shape[0] > 1 and t.shape[1] > 1 and t.stride(0) == 1 and t.stride(1) == t.shape[0]
+
+
+def _weight_n(x2, x2_int4: bool) -> int:
+    """Output columns n of a weight tensor (row-major int4 storage packs two columns a byte)."""
+    return x2.shape[1] * (2 if x2_int4 and not _is_t_view(x2) else 1)
+
+
 def _out_desc_like(x1, x2, x2_int4):
-    n = x2.shape[1] * (2 if x2_int4 else 1)
+    n = _weight_n(x2, x2_int4)
     return make_desc(list(x1.shape[:-1]) + [n], _dtype_code(x1), 0x1)
 
 
@@ -186,7 +200,7 @@ class AntiquantMatmul:
     def __init__(self, x1, x2, antiquant_scale, antiquant_offset=None, bias=None, x3=None,
                  antiquant_group_size: int = 0, *, x2_int4: bool = False, out=None, workspace=None):
         torch = _torch()
-        n = x2.shape[1] * (2 if x2_int4 else 1)
+        n = _weight_n(x2, x2_int4)
         if out is None:
             out = torch.empty(tuple(x1.shape[:-1]) + (n,), dtype=x1.dtype, device=x1.device)
         self._descs = [_desc(x1), _desc(x2, x2_int4), _desc(bias), _desc(antiquant_scale),
@@ -219,7 +233,9 @@ def antiquant_matmul(x1, x2, antiquant_scale, antiquant_offset=None, bias=None, 
     x1: fp16/bf16 (m, k) or (b, s, k); x2: int8 (k, n), or with ``x2_int4`` a uint8 (k, n/2)
     tensor of packed signed nibbles (even column in the low nibble), or float8_e4m3fn (k, n)
     with a per-channel scale and no offset; scale/offset: (1), (n), (1, n) or (ceil(k/g), n)
-    for group size g.  Returns the output tensor."""
+    for group size g.  x2 may also be the transpose view ``w.t()`` of a row-major (n, k)
+    tensor (int4: of an (n, k/2) tensor packed along k); per-group scale and offset are then
+    transpose views too.  Returns the output tensor."""
     return AntiquantMatmul(x1, x2, antiquant_scale, antiquant_offset, bias, x3, antiquant_group_size,
                            x2_int4=x2_int4, out=out, workspace=workspace)(stream)
 

@@ -40,7 +40,8 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kArow = 128;                 // bytes per x1 row in a stage (64 x 16-bit)
 
-template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED>
+// XT: the weights are stored transposed, (n, k) (int4: (n, k/2) bytes packed along k).
+template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false>
 struct Tile {
   static constexpr int Waves = GM * GN;              // wave grid GM x GN
   static constexpr int Threads = 64 * Waves;
@@ -55,6 +56,9 @@ struct Tile {
   static constexpr int Win = 256 / RB;               // k rows per 256-byte bank window
   static constexpr int PairMask = 8 / Win - 1;       // swizzle span of 32-byte pairs
   static constexpr int RowsPerKB = 1024 / RB;        // k rows per 1 KiB DMA block
+  // transposed weights: per column a row of the stage's 64 k (64 bytes, int4 32 bytes)
+  static constexpr int RowT = W4 ? kBK / 2 : kBK;
+  static constexpr int ColsPerKB = 1024 / RowT;      // columns per 1 KiB DMA block
   static constexpr int Ablocks = Abytes / 1024;      // 1 KiB DMA blocks of x1
   static constexpr int Bblocks = Bbytes / 1024;      // DMA blocks per stage (weights)
   static constexpr int Aper = Ablocks / Waves;
@@ -63,7 +67,10 @@ struct Tile {
   static constexpr int Bwaves = Bblocks >= Waves ? Waves : Bblocks;
   static constexpr int Pwave = Waves - 1;            // issues the group-parameter loads
   static constexpr int WCols = 32 * WN;              // logical columns per wave
-  static constexpr int Reads = W4 ? WN / 2 : WN;     // tr8 reads per wave per 16-k step
+  static constexpr bool XTile = XT;
+  // B fragment reads per wave per 16-k step: tr8 reads (an int4 one feeds two blocks), or
+  // one 8-byte (int4: 4-byte) read per block from transposed weights
+  static constexpr int Reads = (W4 && !XT) ? WN / 2 : WN;
   // LDS layout: stages (x1 | weights | group parameters) | S rows (BM fp32) | per-wave
   // group-sum scratch (Waves x 32*WM fp32).  As many stages as fit (3 to 6): a deeper
   // pipeline hides more load latency where a stage is small.
@@ -78,7 +85,7 @@ struct Tile {
   static_assert(Ablocks % Waves == 0, "x1 DMA blocks split evenly over the waves");
   static_assert(Bblocks % Waves == 0 || Bblocks < Waves, "weight DMA blocks split");
   static_assert(Win >= 1 && Win <= 4, "weight row bytes 64..256");
-  static_assert(!W4 || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
+  static_assert(!W4 || XT || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
 };
 
 // Stage barrier allowing `ahead` later stages (OWN loads each) to stay in flight, for a
@@ -113,6 +120,22 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
     const int c = 2 * kk + (lane >> 5);
     f.a[i] = *(const u32x4_t*)(As + r * kArow + 16 * row_slot<kArow>(r, c));
   }
+  if constexpr (T::XTile) {
+    // column row r holds the stage's k for one column, 16-byte chunks swizzled like x1
+    // rows; lane half h = lane / 32 takes k 16 kk + 8 h .. + 7
+    constexpr int RowT = T::RowT;
+    const int c = 2 * kk + (lane >> 5);  // 8-k piece within the row
+#pragma unroll
+    for (int j = 0; j < T::Reads; ++j) {
+      const int r = wn * T::WCols + 32 * j + (lane & 31);
+      if constexpr (RowT == 64) {        // 8 bytes per piece
+        f.raw[j] = *(const u32x2_t*)(Bs + r * RowT + 16 * row_slot<RowT>(r, c >> 1) + 8 * (c & 1));
+      } else {                           // int4: 4 bytes per piece
+        f.raw[j] = u32x2_t{*(const uint32_t*)(Bs + r * RowT + 16 * row_slot<RowT>(r, c >> 2) + 4 * (c & 3)), 0u};
+      }
+    }
+    return;
+  }
   const int kr = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 1);
 #pragma unroll
   for (int j = 0; j < T::Reads; ++j) {
@@ -124,10 +147,10 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
 
 // The kernel body, specialised on the wave's column index WNI in the GM x GN wave grid:
 // column offsets and the per-channel row-sum block become compile-time constants.
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, int WNI>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT, int WNI>
 __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int wave) {
   constexpr bool W4 = WF == kWInt4;
-  using T = Tile<W4, GM, GN, WM, WN, GROUPED>;
+  using T = Tile<W4, GM, GN, WM, WN, GROUPED, XT>;
   constexpr int BN = T::BN, RB = T::RB, WC = T::WCols;
   const int lane = threadIdx.x & 63;
   const int wm = wave / GN;
@@ -138,7 +161,8 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   const int n0 = tn * BN;
   const int64_t M = a.m;
   const int K = a.k, N = a.n;
-  const int64_t x2_pitch = W4 ? (N >> 1) : N;
+  // bytes per weight row: a k row of n codes, or (transposed) a column row of k codes
+  const int64_t x2_pitch = XT ? (W4 ? (K >> 1) : K) : (W4 ? (N >> 1) : N);
   const int nk = (K + kBK - 1) / kBK;
 
   // ---------------------------------------------------------------- DMA issue
@@ -149,7 +173,9 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   // bytes of x1 from the tile's first row on that the tile may read (at most BM rows)
   const uint32_t x1_bytes = (uint32_t)((M - m0 < T::BM ? M - m0 : T::BM) * K * 2);
   const int nb0 = W4 ? n0 / 2 : n0;
-  const uint8_t* x2b = (const uint8_t*)a.x2 + nb0;
+  const uint8_t* x2b = (const uint8_t*)a.x2 + (XT ? (int64_t)n0 * x2_pitch : (int64_t)nb0);
+  // transposed weights: bytes from the tile's first column row on that the tile may read
+  const uint32_t x2t_bytes = (uint32_t)((N - n0 < BN ? N - n0 : BN) * x2_pitch);
   uint32_t a_off[T::Aper];
   int a_k[T::Aper];  // first k (within the stage) of the chunk this lane loads
 #pragma unroll
@@ -161,12 +187,22 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     a_off[j] = (uint32_t)(r * K * 2 + 16 * c);
   }
   uint32_t b_off[T::Bper];
+  int b_k[T::Bper];  // transposed weights: first k (within the stage) of the chunk this lane loads
 #pragma unroll
   for (int j = 0; j < T::Bper; ++j) {
     const int b = wave + T::Waves * j;
-    const int r = T::RowsPerKB * b + lane / (RB / 16);
-    const int p = lane % (RB / 16);
-    b_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * pair_slot<RB>(r, p >> 1) + (p & 1)));
+    if constexpr (XT) {
+      constexpr int L = T::RowT / 16;  // 16-byte chunks per column row
+      const int r = T::ColsPerKB * b + lane / L;
+      const int c = row_slot<T::RowT>(r, lane % L);
+      b_k[j] = W4 ? 32 * c : 16 * c;
+      b_off[j] = (uint32_t)(r * x2_pitch + 16 * c);
+    } else {
+      const int r = T::RowsPerKB * b + lane / (RB / 16);
+      const int p = lane % (RB / 16);
+      b_k[j] = 0;
+      b_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * pair_slot<RB>(r, p >> 1) + (p & 1)));
+    }
   }
   // per-group parameters: buffer resources over scale / offset from column n0 on
   const bool has_offset = a.offset != nullptr;
@@ -196,8 +232,13 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     r.k0 = ks * kBK;
     r.st = smem + (ks % T::Stages) * T::Stage;
     r.ra = make_rsrc32(x1b + (int64_t)r.k0 * 2, x1_bytes - (uint32_t)r.k0 * 2);
-    const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
-    r.rb = make_rsrc32(x2b + (int64_t)r.k0 * x2_pitch, (uint32_t)(rows * x2_pitch - nb0));
+    if constexpr (XT) {
+      const uint32_t kb = W4 ? (uint32_t)r.k0 / 2 : (uint32_t)r.k0;
+      r.rb = make_rsrc32(x2b + kb, x2t_bytes - kb);
+    } else {
+      const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
+      r.rb = make_rsrc32(x2b + (int64_t)r.k0 * x2_pitch, (uint32_t)(rows * x2_pitch - nb0));
+    }
     r.tail = r.k0 + kBK > K;  // only the last k-step can reach past k
     return r;
   };
@@ -210,7 +251,9 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     }
   };
   auto issue_b = [&](const StageRsrc& r, int j) {
-    dma16(r.rb, r.st + T::Abytes + 1024 * (wave + T::Waves * j), b_off[j]);
+    uint8_t* dst = r.st + T::Abytes + 1024 * (wave + T::Waves * j);
+    if (!XT || !r.tail) dma16(r.rb, dst, b_off[j]);
+    else dma16(r.rb, dst, r.k0 + b_k[j] >= K ? kOOB : b_off[j]);  // k past the end reads 0
   };
   auto issue_p = [&](const StageRsrc& r) {
     if constexpr (GROUPED) {
@@ -271,7 +314,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
 
   // logical column of lane's block j (int4: block 2p + e covers byte pair p, parity e)
   auto block_col = [&](int j) -> int {
-    if constexpr (W4) return n0 + wn * WC + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
+    if constexpr (W4 && !XT) return n0 + wn * WC + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
     else return n0 + wn * WC + 32 * j + (lane & 31);
   };
 
@@ -383,7 +426,8 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       u32x4_t bfr[WN];
 #pragma unroll
       for (int j = 0; j < T::Reads; ++j) {
-        if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
+        if constexpr (W4 && XT) bfr[j] = i4x8_k_to_act<BF16>(cur.raw[j][0]);
+        else if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
         else bfr[j] = w8x8_to_act<BF16, WF>(cur.raw[j]);
       }
       // Per-group: a group's first 16-k step (group starts fall on multiples of 32, so on
@@ -505,7 +549,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   }
 }
 
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT>
 __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
@@ -513,7 +557,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #define WQ_WAVE_COLUMN(c)                                                      \
   if constexpr (GN > c) {                                                     \
     if (wn == c) {                                                            \
-      aq_gemm_body<BF16, WF, GM, GN, WM, WN, GROUPED, c>(a, smem, wave);       \
+      aq_gemm_body<BF16, WF, GM, GN, WM, WN, GROUPED, XT, c>(a, smem, wave);   \
       return;                                                                 \
     }                                                                         \
   }
@@ -522,15 +566,15 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #undef WQ_WAVE_COLUMN
 }
 
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false>
 hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   static_assert(GN <= 8, "wave grids have at most 8 columns");
-  using T = Tile<WF == kWInt4, GM, GN, WM, WN, GROUPED>;
+  using T = Tile<WF == kWInt4, GM, GN, WM, WN, GROUPED, XT>;
   AqArgs a = a0;
   a.tiles_m = (int)((a.m + T::BM - 1) / T::BM);
   a.tiles_n = (a.n + T::BN - 1) / T::BN;
   const size_t lds = (size_t)T::Total;
-  auto kern = aq_gemm_kernel<BF16, WF, GM, GN, WM, WN, GROUPED>;
+  auto kern = aq_gemm_kernel<BF16, WF, GM, GN, WM, WN, GROUPED, XT>;
   hipError_t e = raise_lds_limit((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
@@ -553,6 +597,12 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
 template <bool BF16, int WF>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   constexpr bool W4 = WF == kWInt4;
+  if (a.x2t) {  // transposed weights: the default tile of each mode
+    if constexpr (WF != kWFp8) {
+      if (a.grouped) return launch_one<BF16, WF, 2, 4, 2, 2, true, true>(a, stream);
+    }
+    return launch_one<BF16, WF, 2, 4, 4, 2, false, true>(a, stream);
+  }
   if constexpr (WF != kWFp8) {  // FLOAT8_E4M3FN weights come per-channel only
     if (a.grouped) {
       switch (a.tile) {

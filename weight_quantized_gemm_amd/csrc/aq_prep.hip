@@ -1,5 +1,8 @@
-// The empty-K case of the anti-quant matmul, out = bias + x3 ("CANN ops-transformer ...
-// aclnnWeightQuantMatmulAllReduce 完全指南", section 空 tensor 支持度 (empty tensors)).
+// Small passes around the anti-quant matmul:
+//  * the empty-K case, out = bias + x3 ("CANN ops-transformer ... aclnnWeightQuantMatmulAllReduce
+//    完全指南", section 空 tensor 支持度 (empty tensors));
+//  * per-group scale and offset stored transposed with a transposed x2 (section 参数说明):
+//    copied to the row-major (groups, n) layout the GEMM kernels read, in the workspace.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -21,7 +24,32 @@ __global__ __launch_bounds__(256) void bias_x3_kernel(const uint16_t* __restrict
   }
 }
 
+// dst (rows, cols) = transpose of src (cols, rows), 16-bit elements, through a 64 x 64 LDS
+// tile (rows = groups, cols = n): reads and writes move along the contiguous axis.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ src,
+                                                          uint16_t* __restrict__ dst, int rows, int cols) {
+  __shared__ uint16_t tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {  // src row c0 + i, element r0 + tx
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) tile[i][tx] = src[(int64_t)c * rows + r];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {  // dst row r0 + i, element c0 + tx
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) dst[(int64_t)r * cols + c] = tile[tx][i];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_transpose16(const void* src, void* dst, int rows, int cols, hipStream_t stream) {
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, (const uint16_t*)src, (uint16_t*)dst,
+                     rows, cols);
+  return hipGetLastError();
+}
 
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream) {
   const int64_t total = a.m * a.n;

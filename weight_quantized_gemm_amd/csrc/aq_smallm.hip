@@ -33,6 +33,9 @@ constexpr int kRows = 64;     // k rows per block, a wave's unit of work
 template <bool W4, bool GROUPED>
 struct SmTile {
   static constexpr int RB = W4 ? kSlab / 2 : kSlab;   // weight bytes per k row
+  // transposed weights: per column a row of the block's 64 k (int4: 32 bytes)
+  static constexpr int RowT = W4 ? kRows / 2 : kRows;
+  static constexpr int ColsPerKB = 1024 / RowT;
   static constexpr int Wbytes = kRows * RB;           // 8 or 4 KiB
   static constexpr int Xbytes = 32 * kRows * 2;       // 4 KiB of x1 (32 rows x 64 k)
   static constexpr int Pbytes = GROUPED ? 1024 : 0;   // scale / offset rows of the block's groups
@@ -48,7 +51,8 @@ struct SmTile {
   static_assert(Lds <= 160 * 1024, "one workgroup per CU");
 };
 
-template <bool BF16, int WF, bool GROUPED>
+// XT: the weights are stored transposed, (n, k) (int4: (n, k/2) bytes packed along k).
+template <bool BF16, int WF, bool GROUPED, bool XT>
 __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) {
   constexpr bool W4 = WF == kWInt4;
   using T = SmTile<W4, GROUPED>;
@@ -65,17 +69,28 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   const int nb = wave < nblocks ? (nblocks - wave + kWaves - 1) / kWaves : 0;
   auto block_k0 = [&](int t) { return kbeg + (wave + kWaves * t) * kRows; };
 
-  const int64_t x2_pitch = W4 ? (N >> 1) : N;
+  // bytes per weight row: a k row of n codes, or (transposed) a column row of k codes
+  const int64_t x2_pitch = XT ? (W4 ? (K >> 1) : K) : (W4 ? (N >> 1) : N);
   const int nb0 = W4 ? n0 / 2 : n0;
   uint8_t* const st = smem + wave * T::Stage;  // the wave's one LDS stage
 
   // per-lane DMA offsets inside a block
   uint32_t w_off[T::WDma];
+  int w_k[T::WDma];  // transposed weights: first k (within the block) of this lane's chunk
 #pragma unroll
   for (int j = 0; j < T::WDma; ++j) {
-    const int r = (1024 / RB) * j + lane / (RB / 16);
-    const int p = lane % (RB / 16);
-    w_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * pair_slot<RB>(r, p >> 1) + (p & 1)));
+    if constexpr (XT) {
+      constexpr int L = T::RowT / 16;
+      const int r = T::ColsPerKB * j + lane / L;
+      const int c = row_slot<T::RowT>(r, lane % L);
+      w_k[j] = W4 ? 32 * c : 16 * c;
+      w_off[j] = (uint32_t)(r * x2_pitch + 16 * c);
+    } else {
+      const int r = (1024 / RB) * j + lane / (RB / 16);
+      const int p = lane % (RB / 16);
+      w_k[j] = 0;
+      w_off[j] = (uint32_t)(r * x2_pitch + 16 * (2 * pair_slot<RB>(r, p >> 1) + (p & 1)));
+    }
   }
   uint32_t x_off[T::XDma];
   int x_k[T::XDma];  // first k (within the block) of the x1 chunk this lane loads
@@ -95,10 +110,20 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   }
   auto issue = [&](int t) {
     const int k0 = block_k0(t);
-    const u32x4_t rw = make_rsrc((const uint8_t*)a.x2 + (int64_t)k0 * x2_pitch + nb0,
-                                 (int64_t)(kend - k0) * x2_pitch - nb0);
+    if constexpr (XT) {
+      // the slab's column rows from k0 on; k >= kend (the split's end) is masked per chunk
+      const int64_t kb = W4 ? k0 / 2 : k0;
+      const int cols = N - n0 < kSlab ? N - n0 : kSlab;
+      const u32x4_t rw = make_rsrc((const uint8_t*)a.x2 + (int64_t)n0 * x2_pitch + kb,
+                                   (int64_t)cols * x2_pitch - kb);
 #pragma unroll
-    for (int j = 0; j < T::WDma; ++j) dma16(rw, st + 1024 * j, w_off[j]);
+      for (int j = 0; j < T::WDma; ++j) dma16(rw, st + 1024 * j, k0 + w_k[j] < kend ? w_off[j] : kOOB);
+    } else {
+      const u32x4_t rw = make_rsrc((const uint8_t*)a.x2 + (int64_t)k0 * x2_pitch + nb0,
+                                   (int64_t)(kend - k0) * x2_pitch - nb0);
+#pragma unroll
+      for (int j = 0; j < T::WDma; ++j) dma16(rw, st + 1024 * j, w_off[j]);
+    }
     // rows >= m lie past the resource; k >= kend (a 32-row tail block) is masked per chunk
     const u32x4_t rx = make_rsrc((const uint8_t*)a.x1 + (int64_t)k0 * 2, (int64_t)M * K * 2 - (int64_t)k0 * 2);
 #pragma unroll
@@ -121,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   float ssum = 0.f;  // row sum of x1 (row lane % 32, k half lane / 32)
   // logical column of this lane in block j (int4: byte pair p = j >> 1, parity j & 1)
   auto block_col = [&](int j) -> int {
-    if constexpr (W4) return n0 + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
+    if constexpr (W4 && !XT) return n0 + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
     else return n0 + 32 * j + (lane & 31);
   };
   const float cbias = a.code_bias;
@@ -163,17 +188,32 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
     wave_wait<0>();
     const uint8_t* W = st;
     const uint8_t* X = st + T::Wbytes;
-    constexpr int kP = W4 ? 2 : 4;            // tr8 reads per 16-k step
+    // B fragment reads per 16-k step: tr8 reads (an int4 one feeds two column blocks), or
+    // one 8-byte (int4: 4-byte) read per block from transposed weights
+    constexpr int kP = (W4 && !XT) ? 2 : 4;
     u32x4_t af[kRows / 16];
     u32x2_t braw[kRows / 16][kP];
 #pragma unroll
     for (int kk = 0; kk < kRows / 16; ++kk) {
       const int r = lane & 31;
       af[kk] = *(const u32x4_t*)(X + r * 128 + 16 * row_slot<128>(r, 2 * kk + (lane >> 5)));
-      const int kr = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 1);
-      const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+      if constexpr (XT) {
+        constexpr int RowT = T::RowT;
+        const int c = 2 * kk + (lane >> 5);  // 8-k piece within the column row
 #pragma unroll
-      for (int p = 0; p < kP; ++p) braw[kk][p] = lds_read_tr8(W + kr * RB + 32 * pair_slot<RB>(kr, p) + sub);
+        for (int p = 0; p < kP; ++p) {
+          const int cr = 32 * p + (lane & 31);
+          if constexpr (RowT == 64)
+            braw[kk][p] = *(const u32x2_t*)(W + cr * RowT + 16 * row_slot<RowT>(cr, c >> 1) + 8 * (c & 1));
+          else
+            braw[kk][p] = u32x2_t{*(const uint32_t*)(W + cr * RowT + 16 * row_slot<RowT>(cr, c >> 2) + 4 * (c & 3)), 0u};
+        }
+      } else {
+        const int kr = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 1);
+        const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+#pragma unroll
+        for (int p = 0; p < kP; ++p) braw[kk][p] = lds_read_tr8(W + kr * RB + 32 * pair_slot<RB>(kr, p) + sub);
+      }
     }
     // the parameter rows of the block's first (e = 0) and second (e = 1) 32-row halves
     uint16_t ps[2][4], po[2][4];
@@ -198,7 +238,9 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
     for (int kk = 0; kk < kRows / 16; ++kk) {
 #pragma unroll
       for (int p = 0; p < kP; ++p) {
-        if constexpr (W4) {
+        if constexpr (W4 && XT) {
+          acc[p] = mfma32x32x16<BF16>(af[kk], i4x8_k_to_act<BF16>(braw[kk][p][0]), acc[p]);
+        } else if constexpr (W4) {
           u32x4_t ev, od;
           i4_kpairs<BF16>(braw[kk][p], ev, od);
           acc[2 * p] = mfma32x32x16<BF16>(af[kk], ev, acc[2 * p]);
@@ -366,7 +408,7 @@ template <bool BF16, int WF, bool GROUPED>
 hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
   using T = SmTile<WF == kWInt4, GROUPED>;
   const int slabs = (a.n + kSlab - 1) / kSlab;
-  auto kern = aq_smallm_kernel<BF16, WF, GROUPED>;
+  auto kern = a.x2t ? aq_smallm_kernel<BF16, WF, GROUPED, true> : aq_smallm_kernel<BF16, WF, GROUPED, false>;
   hipError_t e = raise_lds_limit((const void*)kern, T::Lds);
   if (e != hipSuccess) return e;
   if ((e = profile_begin(stream)) != hipSuccess) return e;

@@ -14,7 +14,9 @@
 // BK = 64.  x1 and x2 tiles move global -> LDS by direct-to-LDS buffer loads through a
 // 4-stage ring (three stages in flight), one barrier per k-step.  x1 rows (64 bytes) are
 // read as MFMA A fragments by 16-byte loads; x2 rows (256 bytes, n-contiguous) give B
-// fragments by two tr8 transpose reads (16 consecutive k of one column).  The epilogue
+// fragments by two tr8 transpose reads (16 consecutive k of one column).  A transposed x2
+// (stored (n, k), which the Parameters table allows) travels exactly like x1: 64-byte rows
+// of k per column, 16-byte fragment loads, no transpose.  The epilogue
 // stages the accumulators through LDS so that x3, the output and the int32 accumulator
 // move in 16-byte row-contiguous accesses.
 #include "wq_kernels.h"
@@ -32,8 +34,9 @@ constexpr int kBbytes = kBK * kRB;              // 16 KiB
 constexpr int kStage = kAbytes + kBbytes;
 constexpr int kLds = kStages * kStage;          // 128 KiB
 
-// Wave grid GM x GN with WM x WN 32x32 blocks per wave (256 x 256 per workgroup).
-template <bool OUT_BF16, int kGM, int kGN>
+// Wave grid GM x GN with WM x WN 32x32 blocks per wave (256 x 256 per workgroup); XT: x2
+// stored transposed, (n, k).
+template <bool OUT_BF16, int kGM, int kGN, bool XT>
 __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs a) {
   constexpr int kWaves = kGM * kGN;
   constexpr int kWM = 8 / kGM, kWN = 8 / kGN;
@@ -56,7 +59,9 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   // ------------------------------------------------------------------ DMA issue
   const uint8_t* x1b = (const uint8_t*)a.x1 + m0 * K;
   const int64_t x1_bytes = (M - m0) * K;
-  const uint8_t* x2b = (const uint8_t*)a.x2 + n0;
+  const uint8_t* x2b = (const uint8_t*)a.x2 + (XT ? (int64_t)n0 * K : (int64_t)n0);
+  // transposed x2: bytes from the tile's first column on that the tile may read
+  const uint32_t x2t_bytes = (uint32_t)((N - n0 < kBN ? N - n0 : kBN) * (int64_t)K);
   uint32_t a_off[kAper];
   int a_chunk[kAper];
 #pragma unroll
@@ -67,12 +72,20 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
     a_off[j] = (uint32_t)(r * K + 16 * a_chunk[j]);
   }
   uint32_t b_off[kBper];
+  int b_chunk[kBper];
 #pragma unroll
   for (int j = 0; j < kBper; ++j) {
-    const int b = wave + kWaves * j;                 // 4 rows of 256 bytes
-    const int r = 4 * b + (lane >> 4);
-    const int p = lane & 15;
-    b_off[j] = (uint32_t)(r * N + 16 * (2 * pair_slot<kRB>(r, p >> 1) + (p & 1)));
+    const int b = wave + kWaves * j;
+    if constexpr (XT) {                              // 16 columns of 64 bytes of k
+      const int r = 16 * b + (lane >> 2);
+      b_chunk[j] = row_slot<kRA>(r, lane & 3);
+      b_off[j] = (uint32_t)(r * K + 16 * b_chunk[j]);
+    } else {                                         // 4 k rows of 256 bytes
+      const int r = 4 * b + (lane >> 4);
+      const int p = lane & 15;
+      b_chunk[j] = 0;
+      b_off[j] = (uint32_t)(r * N + 16 * (2 * pair_slot<kRB>(r, p >> 1) + (p & 1)));
+    }
   }
   // A stage's loads are formed once (stage_rsrc) and issued in two halves, one behind
   // each 32-k step of the k-step that issues them, so that the texture unit is not handed
@@ -88,8 +101,12 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
     r.k0 = ks * kBK;
     r.st = smem + (ks % kStages) * kStage;
     r.ra = make_rsrc(x1b + r.k0, x1_bytes - r.k0);
-    const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
-    r.rb = make_rsrc32(x2b + (int64_t)r.k0 * N, (uint32_t)(rows * N - n0));
+    if constexpr (XT) {
+      r.rb = make_rsrc32(x2b + r.k0, x2t_bytes - (uint32_t)r.k0);
+    } else {
+      const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
+      r.rb = make_rsrc32(x2b + (int64_t)r.k0 * N, (uint32_t)(rows * N - n0));
+    }
     r.tail = r.k0 + kBK > K;
     return r;
   };
@@ -103,8 +120,12 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
       else dma16(r.ra, dst, r.k0 + 16 * a_chunk[j] >= K ? kOOB : a_off[j]);
     }
 #pragma unroll
-    for (int j = 0; j < kBper; ++j)
-      if (j % 2 == h) dma16(r.rb, r.st + kAbytes + 1024 * (wave + kWaves * j), b_off[j]);
+    for (int j = 0; j < kBper; ++j) {
+      if (j % 2 != h) continue;
+      uint8_t* dst = r.st + kAbytes + 1024 * (wave + kWaves * j);
+      if (!XT || !r.tail) dma16(r.rb, dst, b_off[j]);
+      else dma16(r.rb, dst, r.k0 + 16 * b_chunk[j] >= K ? kOOB : b_off[j]);
+    }
   };
   auto issue = [&](int ks) {
     const StageRsrc r = stage_rsrc(ks);
@@ -168,14 +189,22 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
         const int r = wm * (32 * kWM) + 32 * i + (lane & 31);
         af[i] = *(const u32x4_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + (lane >> 5)));
       }
-      const int kr = 32 * kk + 16 * (lane >> 5) + ((lane & 15) >> 1);
+      if constexpr (XT) {
 #pragma unroll
-      for (int j = 0; j < kWN; ++j) {
-        const int pair = wn * kWN + j;
-        const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-        const u32x2_t lo = lds_read_tr8(Bs + kr * kRB + 32 * pair_slot<kRB>(kr, pair) + sub);
-        const u32x2_t hi = lds_read_tr8(Bs + (kr + 8) * kRB + 32 * pair_slot<kRB>(kr + 8, pair) + sub);
-        bfr[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        for (int j = 0; j < kWN; ++j) {
+          const int r = wn * WC + 32 * j + (lane & 31);
+          bfr[j] = *(const u32x4_t*)(Bs + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + (lane >> 5)));
+        }
+      } else {
+        const int kr = 32 * kk + 16 * (lane >> 5) + ((lane & 15) >> 1);
+#pragma unroll
+        for (int j = 0; j < kWN; ++j) {
+          const int pair = wn * kWN + j;
+          const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+          const u32x2_t lo = lds_read_tr8(Bs + kr * kRB + 32 * pair_slot<kRB>(kr, pair) + sub);
+          const u32x2_t hi = lds_read_tr8(Bs + (kr + 8) * kRB + 32 * pair_slot<kRB>(kr + 8, pair) + sub);
+          bfr[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
       }
 #pragma unroll
       for (int i = 0; i < kWM; ++i)
@@ -256,9 +285,12 @@ hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   a.tiles_m = (int)((a.m + kBM - 1) / kBM);
   a.tiles_n = (a.n + kBN - 1) / kBN;
   // default: 2 x 4 waves of 128 x 64 (two per SIMD); tuning tile 1: 2 x 2 waves of 128 x 128
-  auto kern = a.tile == 1 ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2> : qm_gemm_kernel<false, 2, 2>)
-                          : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4> : qm_gemm_kernel<false, 2, 4>);
-  const int threads = a.tile == 1 ? 256 : 512;
+  // (row-major x2 only)
+  const bool t1 = a.tile == 1 && !a.x2t;
+  auto kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, true> : qm_gemm_kernel<false, 2, 4, true>)
+              : t1  ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, false> : qm_gemm_kernel<false, 2, 2, false>)
+                    : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false> : qm_gemm_kernel<false, 2, 4, false>);
+  const int threads = t1 ? 256 : 512;
   hipError_t e = raise_lds_limit((const void*)kern, kLds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;

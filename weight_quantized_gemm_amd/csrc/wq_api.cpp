@@ -30,6 +30,7 @@ struct AqPlan {
   SmallmPlan sm;
   int64_t partial_bytes = 0;
   int64_t rowsum_bytes = 0;
+  int64_t param_bytes = 0;   // per-group scale / offset given transposed: row-major copies
   int64_t workspace = 0;
 };
 
@@ -48,7 +49,8 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
       pl.rowsum_bytes = grouped ? 0 : align_up((int64_t)pl.sm.splits * p.m * (int64_t)sizeof(float));
     }
   }
-  pl.workspace = pl.partial_bytes + pl.rowsum_bytes;
+  if (p.params_t) pl.param_bytes = align_up(p.groups * p.n * 2);
+  pl.workspace = pl.partial_bytes + pl.rowsum_bytes + 2 * pl.param_bytes;
   return pl;
 }
 
@@ -136,7 +138,7 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.x3 = p.x3; a.out = p.out;
   a.m = p.m; a.k = (int32_t)p.k; a.n = (int32_t)p.n;
   a.group = (int32_t)p.group; a.groups = (int32_t)p.groups;
-  a.bf16 = p.act == WQ_BF16; a.w4 = p.w4; a.f8 = p.f8;
+  a.bf16 = p.act == WQ_BF16; a.w4 = p.w4; a.f8 = p.f8; a.x2t = p.x2t;
   a.grouped = p.mode == wq::QuantMode::kGroup;
   a.per_tensor = p.mode == wq::QuantMode::kTensor;
   a.code_bias = wq::code_bias(p);
@@ -145,6 +147,17 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.tile = wq::tile_override();
 
   hipError_t e;
+  if (pl.param_bytes) {
+    // transposed per-group parameters (n, groups) -> row-major (groups, n) copies
+    char* pb = (char*)workspace + pl.partial_bytes + pl.rowsum_bytes;
+    if ((e = wq::launch_transpose16(p.scale, pb, (int)p.groups, (int)p.n, s)) != hipSuccess) return WQ_ERR_RUNTIME;
+    a.scale = pb;
+    if (p.offset) {
+      if ((e = wq::launch_transpose16(p.offset, pb + pl.param_bytes, (int)p.groups, (int)p.n, s)) != hipSuccess)
+        return WQ_ERR_RUNTIME;
+      a.offset = pb + pl.param_bytes;
+    }
+  }
   if (pl.empty_k) {
     e = wq::launch_aq_bias_x3(a, s);
     return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
@@ -190,6 +203,7 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
   a.m = p.m; a.k = (int32_t)p.k; a.n = (int32_t)p.n;
   a.out_bf16 = p.out_dtype == WQ_BF16; a.dq_bf16 = p.dq_dtype == WQ_BF16;
   a.dq_per_tensor = p.dq_per_tensor;
+  a.x2t = p.x2t;
   a.tile = wq::tile_override();
   hipError_t e = wq::launch_qm_gemm(a, (hipStream_t)stream);
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;

@@ -148,6 +148,26 @@ __device__ __forceinline__ void i4_kpairs(u32x2_t d, u32x4_t& even, u32x4_t& odd
   odd = u32x4_t{od[0], od[1], od[2], od[3]};
 }
 
+// 4 bytes of int4 codes packed along k (8 consecutive k of one column, the even k in the low
+// nibble: a transposed int4 weight) -> an MFMA B fragment, images in k order.  Same images
+// as i4_kpairs: bf16 code + 136, fp16 the code.
+template <bool BF16>
+__device__ __forceinline__ u32x4_t i4x8_k_to_act(uint32_t d) {
+  const uint32_t mag = BF16 ? 0x43434343u : 0x64646464u;
+  const uint32_t u = d ^ 0x88888888u;                 // nibble -> code + 8 in [0, 15]
+  const uint32_t e = u & 0x0f0f0f0fu, o = (u >> 4) & 0x0f0f0f0fu;   // even k, odd k
+  const uint32_t t0 = __builtin_amdgcn_perm(o, e, 0x05010400u);    // [k0, k1, k2, k3]
+  const uint32_t t1 = __builtin_amdgcn_perm(o, e, 0x07030602u);    // [k4, k5, k6, k7]
+  uint32_t w[4] = {__builtin_amdgcn_perm(mag, t0, 0x04010400u), __builtin_amdgcn_perm(mag, t0, 0x04030402u),
+                   __builtin_amdgcn_perm(mag, t1, 0x04010400u), __builtin_amdgcn_perm(mag, t1, 0x04030402u)};
+  if constexpr (!BF16) {
+    const f16x2_t k = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, w[q]) - k);
+  }
+  return u32x4_t{w[0], w[1], w[2], w[3]};
+}
+
 // row sums: a * 1 + b * 1 + c for a dword of two 16-bit activations
 template <bool BF16>
 __device__ __forceinline__ float dot2_ones(uint32_t v, float c) {

@@ -26,6 +26,7 @@ struct AqArgs {
   int32_t tile;          // tile configuration index (0 = default)
   float code_bias;       // C: the fed weight image is code + C
   bool bf16, w4, f8, grouped, per_tensor;  // f8: FLOAT8_E4M3FN weights
+  bool x2t;              // x2 stored transposed: (n, k) (int4: (n, k/2) bytes along k)
 };
 
 // W8A8 matmul.
@@ -43,6 +44,7 @@ struct QmArgs {
   int32_t tiles_m, tiles_n;
   int32_t tile;          // tile configuration index (0 = default)
   bool out_bf16, dq_bf16, dq_per_tensor;
+  bool x2t;              // x2 stored transposed, (n, k)
 };
 
 // Raise a kernel's dynamic LDS limit; done once per (kernel, device, size) in a process.
@@ -63,6 +65,8 @@ inline hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream) {
 }
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream);  // k == 0
+// dst (rows, cols) = transpose of src (cols, rows), 16-bit elements
+hipError_t launch_transpose16(const void* src, void* dst, int rows, int cols, hipStream_t stream);
 hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);
 
 // Split-k plan of the small-m path, shared by the planner (workspace size) and the launch.

@@ -14,6 +14,8 @@ struct AntiquantProblem {
   int32_t act = WQ_F16;      // WQ_F16 | WQ_BF16 (x1, scale, offset, bias, x3, output)
   bool w4 = false;           // x2 is packed int4
   bool f8 = false;           // x2 is FLOAT8_E4M3FN (per-channel, no offset)
+  bool x2t = false;          // x2 is stored transposed: row-major (n, k) (int4: (n, k/2) bytes)
+  bool params_t = false;     // per-group scale / offset stored transposed: row-major (n, groups)
   QuantMode mode = QuantMode::kTensor;
   int64_t group = 0;         // group size along k (per-group); k for tensor/channel
   int64_t groups = 1;        // ceil(k / group)
@@ -31,6 +33,7 @@ struct QuantProblem {
   int32_t out_dtype = WQ_BF16;   // WQ_F16 | WQ_BF16 (output and x3)
   int32_t dq_dtype = WQ_F32;     // WQ_F32 | WQ_BF16
   bool dq_per_tensor = false;
+  bool x2t = false;              // x2 stored transposed: row-major (n, k)
   const void* x1 = nullptr;
   const void* x2 = nullptr;
   const void* bias = nullptr;      // int32, may be null

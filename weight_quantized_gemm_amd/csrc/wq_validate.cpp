@@ -16,7 +16,11 @@
 //    int4 multiples of 64).  The text is silent on FLOAT8_E4M3FN; being one byte per
 //    element like int8, it takes int8's multiple of 32;
 //  * FLOAT8_E4M3FN weights -- guide, 支持矩阵 (950 row) and the note under the 950 dtype
-//    table: per-channel only and no antiquantOffset.
+//    table: per-channel only and no antiquantOffset;
+//  * transposed x2 -- guide, 参数说明 (per-group: antiquantScale and antiquantOffset are
+//    transposed together with x2) and its notes on CheckContiguous; W8A8 --
+//    aclnnQuantMatmulAllReduceV2, Parameters table (x2: the last two axes may be transposed,
+//    no other non-contiguous layout) and Constraints (n may exceed 65535 only then).
 #include <climits>
 #include <cstddef>
 
@@ -27,6 +31,9 @@ namespace {
 
 constexpr int64_t kMaxM = INT32_MAX;   // m in [1, 2^31 - 1]
 constexpr int64_t kMaxKN = 65535;      // k, n in [.., 65535]
+// W8A8 with a transposed x2: n beyond 65535 (the pages give no bound; this library keeps
+// n * 256 within int32 tile arithmetic)
+constexpr int64_t kMaxNT = (int64_t)1 << 23;
 
 int64_t numel(const wq_tensor* t) {
   int64_t e = 1;
@@ -49,6 +56,14 @@ bool contiguous(const wq_tensor* t) {
     expect *= t->shape[i];
   }
   return true;
+}
+
+// The transpose of a row-major (n, k) tensor, given with its logical shape (k, n): strides
+// (1, k).  Both extents exceed 1 wherever this is asked (k and n are multiples of 32, and a
+// per-group parameter tensor has at least two rows), so the test is unambiguous.
+bool transposed2(const wq_tensor* t) {
+  return t->ndim == 2 && t->shape[0] > 1 && t->shape[1] > 1 && t->stride[0] == 1 &&
+         t->stride[1] == t->shape[0];
 }
 
 // data pointer may be NULL only for an empty tensor
@@ -150,14 +165,28 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
   if (offset && !same_shape(offset, scale)) return WQ_ERR_PARAM_INVALID;
   if (f8 && mode != QuantMode::kChannel) return WQ_ERR_PARAM_INVALID;
 
-  // layout: row-major contiguous only; no output aliasing
-  for (const wq_tensor* t : {x1, x2, scale, output, offset, bias, x3})
+  // layout: row-major contiguous, except that x2 may be the transpose of a row-major (n, k)
+  // tensor; per-group parameters then must be transposed with it (and only then).  No
+  // output aliasing.
+  const bool x2t = k > 0 && transposed2(x2);
+  if (!x2t && !contiguous(x2)) return WQ_ERR_PARAM_INVALID;
+  const bool pt = mode == QuantMode::kGroup && groups > 0 && x2t;
+  for (const wq_tensor* t : {scale, offset}) {
+    if (!t) continue;
+    if (mode == QuantMode::kGroup && groups > 0) {
+      if (pt ? !transposed2(t) : !contiguous(t)) return WQ_ERR_PARAM_INVALID;
+    } else if (!contiguous(t)) {
+      return WQ_ERR_PARAM_INVALID;
+    }
+  }
+  for (const wq_tensor* t : {x1, output, bias, x3})
     if (t && !contiguous(t)) return WQ_ERR_PARAM_INVALID;
   for (const wq_tensor* t : {x1, x2, scale, offset, bias, x3})
     if (aliases(output->data, t)) return WQ_ERR_PARAM_INVALID;
 
   if (p) {
     p->m = m; p->k = k; p->n = n; p->act = act; p->w4 = w4; p->f8 = f8; p->mode = mode;
+    p->x2t = x2t; p->params_t = pt;
     p->group = group; p->groups = groups;
     p->x1 = x1->data; p->x2 = x2->data; p->scale = scale->data;
     p->offset = offset ? offset->data : nullptr;
@@ -196,8 +225,10 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
     m *= x1->shape[i];
     if (m > kMaxM) return WQ_ERR_PARAM_INVALID;
   }
-  // the W8A8 op supports no empty tensor (Constraints, "Empty tensor support")
-  if (k < 1 || k > kMaxKN || n < 1 || n > kMaxKN) return WQ_ERR_PARAM_INVALID;
+  // the W8A8 op supports no empty tensor (Constraints, "Empty tensor support"); n may exceed
+  // 65535 only with a transposed x2 (Constraints)
+  const bool x2t = transposed2(x2);
+  if (k < 1 || k > kMaxKN || n < 1 || n > (x2t ? kMaxNT : kMaxKN)) return WQ_ERR_PARAM_INVALID;
   if (k % 32 != 0 || n % 32 != 0) return WQ_ERR_PARAM_INVALID;
 
   if (output->ndim != x1->ndim) return WQ_ERR_PARAM_INVALID;
@@ -213,7 +244,8 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
   if (pt && !shape_is(pt, 1, m)) return WQ_ERR_PARAM_INVALID;
   if (acc_out && !shape_is(acc_out, 2, m, n)) return WQ_ERR_PARAM_INVALID;
 
-  for (const wq_tensor* t : {x1, x2, dq, output, bias, x3, pt, acc_out})
+  if (!x2t && !contiguous(x2)) return WQ_ERR_PARAM_INVALID;
+  for (const wq_tensor* t : {x1, dq, output, bias, x3, pt, acc_out})
     if (t && !contiguous(t)) return WQ_ERR_PARAM_INVALID;
   for (const wq_tensor* t : {x1, x2, dq, bias, x3, pt, acc_out})
     if (aliases(output->data, t)) return WQ_ERR_PARAM_INVALID;
@@ -224,6 +256,7 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
   if (p) {
     p->m = m; p->k = k; p->n = n; p->out_dtype = output->dtype; p->dq_dtype = dq->dtype;
     p->dq_per_tensor = dq_tensor;
+    p->x2t = x2t;
     p->x1 = x1->data; p->x2 = x2->data; p->bias = bias ? bias->data : nullptr;
     p->x3 = x3 ? x3->data : nullptr; p->dq = dq->data; p->pt = pt ? pt->data : nullptr;
     p->out = output->data; p->acc_out = acc_out ? acc_out->data : nullptr;

@@ -14,6 +14,10 @@ Storage conventions
 * int4  -> ``numpy.uint8`` of shape (k, n/2): two signed two's-complement nibbles per
   byte along n, the even column in the low nibble.
 * int8 / int32 / fp32 -> the matching numpy dtype.
+* transposed weights (``x2_transposed``): x2 is stored as its transpose, (n, k) (int4:
+  (n, k/2) bytes, two nibbles per byte along k, the even k in the low nibble), and per-group
+  scale and offset as (n, groups).  The values drawn are the same as for the row-major case
+  of the same seed.
 * fp8e4m3 (FLOAT8_E4M3FN) -> ``numpy.uint8`` bit patterns.  Weight codes are drawn
   uniformly over the 254 finite patterns (every pattern except S.1111.111, the NaN), so a
   case covers zeros of both signs, subnormals and the largest magnitude 448.
@@ -79,6 +83,7 @@ class AntiquantCase:
     bias: Optional[np.ndarray]    # (n,)
     x3: Optional[np.ndarray]      # output shape
     group_size: int
+    x2_transposed: bool = False   # x2 (and per-group scale / offset) stored transposed
 
     @property
     def k(self) -> int:
@@ -109,6 +114,7 @@ class W8A8Case:
     dequant_dtype: str            # "fp32" | "bf16"
     pertoken_scale: Optional[np.ndarray]  # fp32 (m,)
     x3: Optional[np.ndarray]      # out dtype, output shape
+    x2_transposed: bool = False   # x2 stored as (n, k)
 
     @property
     def k(self) -> int:
@@ -116,7 +122,7 @@ class W8A8Case:
 
     @property
     def n(self) -> int:
-        return self.x2.shape[1]
+        return self.x2.shape[0] if self.x2_transposed else self.x2.shape[1]
 
     @property
     def m(self) -> int:
@@ -155,7 +161,8 @@ def make_antiquant(*, seed: int, act: str, weight: str, x1_shape, n: int, mode: 
                    offset_dist=("uniform", -2.0, 2.0), with_offset=True,
                    bias_dist=("normal", 0.0, 0.1), with_bias=True,
                    x3_dist=("normal", 0.0, 0.1), with_x3=True,
-                   x1_dist=("normal", 0.0, 1.0), channel_2d=False, name="") -> AntiquantCase:
+                   x1_dist=("normal", 0.0, 1.0), channel_2d=False, x2_transposed=False,
+                   name="") -> AntiquantCase:
     """Draw one anti-quant case.  ``mode`` is "tensor", "channel" or "group"."""
     assert act in ACT_DTYPES and weight in ("int8", "int4", "fp8e4m3")
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -168,7 +175,10 @@ def make_antiquant(*, seed: int, act: str, weight: str, x1_shape, n: int, mode: 
         r = rng.integers(0, 253, size=(k, n), endpoint=True, dtype=np.int16)
         x2 = (r + (r >= 0x7F)).astype(np.uint8)   # 0..0x7E, 0x80..0xFE: no NaN pattern
     else:
-        x2 = pack_int4(rng.integers(-8, 7, size=(k, n), endpoint=True, dtype=np.int8))
+        codes4 = rng.integers(-8, 7, size=(k, n), endpoint=True, dtype=np.int8)
+        x2 = pack_int4(codes4.T if x2_transposed else codes4)
+    if x2_transposed and weight != "int4":
+        x2 = np.ascontiguousarray(x2.T)
     if mode == "tensor":
         pshape = (1,)
     elif mode == "channel":
@@ -180,30 +190,35 @@ def make_antiquant(*, seed: int, act: str, weight: str, x1_shape, n: int, mode: 
         raise ValueError(mode)
     scale = encode(_dist(rng, scale_dist, pshape), act)
     offset = encode(_dist(rng, offset_dist, pshape), act) if with_offset else None
+    if x2_transposed and mode == "group":
+        scale = np.ascontiguousarray(scale.T)
+        offset = None if offset is None else np.ascontiguousarray(offset.T)
     bias = encode(_dist(rng, bias_dist, (n,)), act) if with_bias else None
     out_shape = x1_shape[:-1] + (n,)
     x3 = encode(_dist(rng, x3_dist, out_shape), act) if with_x3 else None
     return AntiquantCase(name or f"aq_{act}_{weight}_{mode}", act, weight, x1, x2, n, scale,
-                         offset, bias, x3, group_size if mode == "group" else 0)
+                         offset, bias, x3, group_size if mode == "group" else 0, x2_transposed)
 
 
 def make_w8a8(*, seed: int, out: str, x1_shape, n: int, dequant: str = "channel",
               dequant_dtype: str = "fp32", with_bias=True, with_pertoken=True, with_x3=True,
               bias_range=(-1000, 1000), dq_range=(1e-4, 1e-3), pt_range=(0.5, 2.0),
-              name="") -> W8A8Case:
+              x2_transposed=False, name="") -> W8A8Case:
     rng = np.random.Generator(np.random.PCG64(seed))
     x1_shape = tuple(int(d) for d in x1_shape)
     k = x1_shape[-1]
     m = int(np.prod(x1_shape[:-1]))
     x1 = rng.integers(-128, 127, size=x1_shape, endpoint=True, dtype=np.int8)
     x2 = rng.integers(-128, 127, size=(k, n), endpoint=True, dtype=np.int8)
+    if x2_transposed:
+        x2 = np.ascontiguousarray(x2.T)
     bias = (rng.integers(bias_range[0], bias_range[1], size=(n,), endpoint=True,
                          dtype=np.int64).astype(np.int32) if with_bias else None)
     dshape = (1,) if dequant == "tensor" else (n,)
     dq = encode(rng.uniform(dq_range[0], dq_range[1], size=dshape), dequant_dtype)
     pt = encode(rng.uniform(pt_range[0], pt_range[1], size=(m,)), "fp32") if with_pertoken else None
     x3 = encode(rng.normal(0.0, 0.1, size=x1_shape[:-1] + (n,)), out) if with_x3 else None
-    return W8A8Case(name or f"w8a8_{out}", out, x1, x2, bias, dq, dequant_dtype, pt, x3)
+    return W8A8Case(name or f"w8a8_{out}", out, x1, x2, bias, dq, dequant_dtype, pt, x3, x2_transposed)
 
 
 # --------------------------------------------------------------------------- named workloads
