@@ -163,14 +163,48 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   };
 
   // ------------------------------------------------------------------ main loop
+  // Fragments are double-buffered across the two 32-k steps, and across stages: the barrier
+  // that publishes stage ks + 1 is taken before the MFMAs of stage ks's second step, and the
+  // first fragment reads of stage ks + 1 follow it at once, so that their LDS latency and the
+  // wait for the slowest wave hide behind those MFMAs.  The barrier also tells every wave
+  // that all reads of stage ks - 1 are done: its buffer is the one the loads issued during
+  // stage ks refill.
+  constexpr int kEarly = (kAper + 1) / 2 + (kBper + 1) / 2;  // loads of a stage's first half
+  u32x4_t af[2][kWM], bfr[2][kWN];
+  auto load = [&](const uint8_t* As, int kk, int buf) {
+    const uint8_t* Bs = As + kAbytes;
+#pragma unroll
+    for (int i = 0; i < kWM; ++i) {
+      const int r = wm * (32 * kWM) + 32 * i + (lane & 31);
+      af[buf][i] = *(const u32x4_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + (lane >> 5)));
+    }
+    if constexpr (XT) {
+#pragma unroll
+      for (int j = 0; j < kWN; ++j) {
+        const int r = wn * WC + 32 * j + (lane & 31);
+        bfr[buf][j] = *(const u32x4_t*)(Bs + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + (lane >> 5)));
+      }
+    } else {
+      const int kr = 32 * kk + 16 * (lane >> 5) + ((lane & 15) >> 1);
+#pragma unroll
+      for (int j = 0; j < kWN; ++j) {
+        const int pair = wn * kWN + j;
+        const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+        const u32x2_t lo = lds_read_tr8(Bs + kr * kRB + 32 * pair_slot<kRB>(kr, pair) + sub);
+        const u32x2_t hi = lds_read_tr8(Bs + (kr + 8) * kRB + 32 * pair_slot<kRB>(kr + 8, pair) + sub);
+        bfr[buf][j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+  };
   issue(0);
   if (nk > 1) issue(1);
   if (nk > 2) issue(2);
+  // stage 0 complete; the other prologue stages may stay in flight
+  if (nk > 2) stage_barrier<2 * kDma>();
+  else if (nk > 1) stage_barrier<kDma>();
+  else stage_barrier<0>();
+  load(smem, 0, 0);
   for (int ks = 0; ks < nk; ++ks) {
-    const int ahead = min(kStages - 2, nk - 1 - ks);  // stages issued after stage ks
-    if (ahead == 2) stage_barrier<2 * kDma>();
-    else if (ahead == 1) stage_barrier<kDma>();
-    else stage_barrier<0>();
     const bool more = ks + kStages - 1 < nk;
     StageRsrc nr{};
     if (more) nr = stage_rsrc(ks + kStages - 1);
@@ -178,38 +212,30 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
       prefetch_x3(0, 0);
       if (kWM > 1) prefetch_x3(1, 1);
     }
-
     const uint8_t* As = smem + (ks % kStages) * kStage;
-    const uint8_t* Bs = As + kAbytes;
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
-      u32x4_t af[kWM], bfr[kWN];
-#pragma unroll
-      for (int i = 0; i < kWM; ++i) {
-        const int r = wm * (32 * kWM) + 32 * i + (lane & 31);
-        af[i] = *(const u32x4_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + (lane >> 5)));
-      }
-      if constexpr (XT) {
-#pragma unroll
-        for (int j = 0; j < kWN; ++j) {
-          const int r = wn * WC + 32 * j + (lane & 31);
-          bfr[j] = *(const u32x4_t*)(Bs + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + (lane >> 5)));
+      static_assert(kBK / 32 == 2, "two 32-k steps per stage");
+      if (kk == 0) {
+        load(As, 1, 1);
+      } else if (ks + 1 < nk) {
+        // stage ks + 1 complete: in flight may stay stage ks + 2 and the first-half loads
+        // of stage ks + 3
+        const bool full = ks + 2 < nk;
+        if (more) {
+          if (full) stage_barrier<kDma + kEarly>();
+          else stage_barrier<kEarly>();
+        } else {
+          if (full) stage_barrier<kDma>();
+          else stage_barrier<0>();
         }
-      } else {
-        const int kr = 32 * kk + 16 * (lane >> 5) + ((lane & 15) >> 1);
-#pragma unroll
-        for (int j = 0; j < kWN; ++j) {
-          const int pair = wn * kWN + j;
-          const int sub = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-          const u32x2_t lo = lds_read_tr8(Bs + kr * kRB + 32 * pair_slot<kRB>(kr, pair) + sub);
-          const u32x2_t hi = lds_read_tr8(Bs + (kr + 8) * kRB + 32 * pair_slot<kRB>(kr + 8, pair) + sub);
-          bfr[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        }
+        load(smem + ((ks + 1) % kStages) * kStage, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kWM; ++i)
 #pragma unroll
-        for (int j = 0; j < kWN; ++j) acc[i][j] = mfma32x32x32_i8(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < kWN; ++j) acc[i][j] = mfma32x32x32_i8(af[kk][i], bfr[kk][j], acc[i][j]);
       if (more) issue_half(nr, kk);  // behind this step's matrix-core work
     }
   }
