@@ -128,10 +128,10 @@ int wq_antiquant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor*
  * WQ_ERR_PARAM_INVALID.  Returns WQ_ERR_RUNTIME if a launch fails.
 
  *
- * Workspace contents: none are expected on entry.  The small-m path (m <= 32) with its
- * k split over several workgroups keeps the fp32 partial sums there until a finishing
- * kernel of the same call has added them; per-group scale and offset given transposed are
- * copied there, row-major, before the product.
+ * Workspace contents: none are expected on entry.  The call uses it for: the small-m path's
+ * (m <= 32) fp32 split-k partial sums, until a finishing kernel of the same call has added
+ * them; per-group scale and offset given transposed, copied row-major; and, per-group with
+ * m > 32, the fp32 row sums of x1 over each group, (groups, m), written before the product.
  */
 int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
                         const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,

@@ -13,10 +13,13 @@
 // matrix cores see only exact 16-bit images of the weight codes (int8, int4 or
 // FLOAT8_E4M3FN, all exact in fp16 and bf16) and x1; scale and offset
 // are applied in fp32 on the accumulators, per group at each group end, or once in the
-// epilogue for per-tensor / per-channel parameters.  S_g is summed in-kernel from the x1
-// fragments (v_dot2 against ones).  Per-group scale and offset rows travel with the
-// weight tile of the k-step in which their group ends, so a fold reads them from LDS and
-// never waits on a global load (which would also wait for every stage in flight).
+// epilogue for per-tensor / per-channel parameters.  Per-channel S is summed in-kernel from
+// the x1 fragments (v_dot2 against ones), each row by one wave.  Per-group S_g come from a
+// pass before the product (group_rowsums_kernel, aq_prep.hip): summed in the k-loop they
+// cost every wave of a row band the same work, about a sixth of the kernel's time.
+// Per-group scale and offset rows and the S_g rows of the tile travel with the weight tile
+// of the k-step in which their group ends, so a fold reads them from LDS and never waits on
+// a global load (which would also wait for every stage in flight).
 //
 // Pipeline: GM x GN waves, wave tile (32*WM) x (32*WN), workgroup tile (32*WM*GM) x (32*WN*GN),
 // BK = 64.  Operands travel global -> LDS by direct-to-LDS buffer loads
@@ -50,9 +53,11 @@ struct Tile {
   static constexpr int BN = 32 * WN * GN;            // logical columns
   static constexpr int RB = W4 ? BN / 2 : BN;        // weight bytes per k row
   static constexpr int Bbytes = kBK * RB;
-  // per-group scale and offset rows of the two groups a k-step can close
+  // per-group scale and offset rows of the two groups a k-step can close, then their S_g
+  // rows (BM fp32 each)
   static constexpr int Pbytes = GROUPED ? (BN > 128 ? 2048 : 1024) : 0;
-  static constexpr int Stage = Abytes + Bbytes + Pbytes;
+  static constexpr int Sbytes = GROUPED ? 2 * BM * 4 : 0;
+  static constexpr int Stage = Abytes + Bbytes + Pbytes + Sbytes;
   static constexpr int Win = 256 / RB;               // k rows per 256-byte bank window
   static constexpr int PairMask = 8 / Win - 1;       // swizzle span of 32-byte pairs
   static constexpr int RowsPerKB = 1024 / RB;        // k rows per 1 KiB DMA block
@@ -71,15 +76,14 @@ struct Tile {
   // B fragment reads per wave per 16-k step: tr8 reads (an int4 one feeds two blocks), or
   // one 8-byte (int4: 4-byte) read per block from transposed weights
   static constexpr int Reads = (W4 && !XT) ? WN / 2 : WN;
-  // LDS layout: stages (x1 | weights | group parameters) | S rows (BM fp32) | per-wave
-  // group-sum scratch (Waves x 32*WM fp32).  As many stages as fit (3 to 6): a deeper
-  // pipeline hides more load latency where a stage is small.
-  static constexpr int Extra = BM * 4 + Waves * 32 * WM * 4;
+  // LDS layout: stages (x1 | weights | group parameters | group row sums) | per-channel S
+  // rows (BM fp32).  As many stages as fit (3 to 6): a deeper pipeline hides more load
+  // latency where a stage is small.
+  static constexpr int Extra = BM * 4;
   static constexpr int FitStages = (160 * 1024 - Extra) / Stage;
   static constexpr int Stages = FitStages > 6 ? 6 : FitStages;
   static constexpr int SOff = Stages * Stage;
-  static constexpr int GOff = SOff + BM * 4;
-  static constexpr int Total = GOff + Waves * 32 * WM * 4;
+  static constexpr int Total = SOff + BM * 4;
   static_assert(Stages >= 3, "at least three stages");
   static_assert(BM == 128 || BM == 256, "x1 stage holds 128 or 256 rows");
   static_assert(Ablocks % Waves == 0, "x1 DMA blocks split evenly over the waves");
@@ -212,8 +216,10 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     rsc = make_rsrc((const uint8_t*)a.scale + 2 * (int64_t)n0, pbytes);
     rof = has_offset ? make_rsrc((const uint8_t*)a.offset + 2 * (int64_t)n0, pbytes) : rsc;
   }
-  // loads this wave issues per stage
-  constexpr int kOwnA = T::Aper, kOwnB = T::Bper, kOwnP = GROUPED ? 2 : 0;
+  // per-group: the tile's rows of the precomputed S_g, (groups, m) fp32, from row m0 on
+  const float* gsum = a.gsum;
+  // loads this wave issues per stage (the parameter wave: 2 parameter and 2 row-sum loads)
+  constexpr int kOwnA = T::Aper, kOwnB = T::Bper, kOwnP = GROUPED ? 4 : 0;
   const bool has_b = wave < T::Bwaves, has_p = GROUPED && wave == T::Pwave;
 
   // The loads of one stage, as items that can be issued separately: x1 blocks j (kind 0),
@@ -259,7 +265,22 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     if constexpr (GROUPED) {
       const int ga = min((r.k0 + 31) / a.group, a.groups - 1);
       const int gb = min((r.k0 + 63) / a.group, a.groups - 1);
-      dma_group_params<BN>(r.st + T::Abytes + T::Bbytes, rsc, rof, has_offset, ga, gb, N, lane);
+      uint8_t* pd = r.st + T::Abytes + T::Bbytes;
+      dma_group_params<BN>(pd, rsc, rof, has_offset, ga, gb, N, lane);
+      // S_g rows of ga then gb: BM fp32 each, rows past m read zero
+      const uint32_t rows_bytes = (uint32_t)((M - m0 < T::BM ? M - m0 : T::BM) * 4);
+      const u32x4_t rsa = make_rsrc32(gsum + (int64_t)ga * M + m0, rows_bytes);
+      const u32x4_t rsb = make_rsrc32(gsum + (int64_t)gb * M + m0, rows_bytes);
+      uint8_t* sd = pd + T::Pbytes;
+      if constexpr (T::BM == 128) {  // 512 bytes a row: one half-wave load each
+        const uint32_t off = 16u * (uint32_t)(lane & 31);
+        if (lane < 32) dma16(rsa, sd, off);
+        else dma16(rsb, sd, off);  // lands at sd + 512 + 16 (lane - 32)
+      } else {                       // 1 KiB a row: one full-wave load each
+        static_assert(T::BM == 256, "x1 tiles of 128 or 256 rows");
+        dma16(rsa, sd, 16u * (uint32_t)lane);
+        dma16(rsb, sd + 1024, 16u * (uint32_t)lane);
+      }
     }
   };
   // the items of 16-k step kk: x1 blocks j with j % 4 == kk, weight blocks j with
@@ -294,23 +315,21 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
 #pragma unroll
       for (int j = 0; j < WN; ++j) tot[i][j] = f32x16_t{};
   }
-  // row sums of x1 (lane half l>>5 of row 32i + l%32 of the wave's band).  Per-channel:
-  // the GN waves of a row band share its WM i-blocks, wave wn summing blocks
-  // wn*SB .. wn*SB + SB - 1.  Per-group: every wave sums all of its rows (it needs them at
-  // each group end).
-  constexpr int SB = GROUPED ? WM : (WM / GN > 0 ? WM / GN : 1);  // blocks summed per wave
+  // per-channel row sums of x1 (lane half l>>5 of row 32i + l%32 of the wave's band): the
+  // GN waves of a row band share its WM i-blocks, wave wn summing blocks
+  // wn*SB .. wn*SB + SB - 1
+  constexpr int SB = WM / GN > 0 ? WM / GN : 1;  // blocks summed per wave
   static_assert(GROUPED || WM % GN == 0 || GN % WM == 0, "row-sum split");
   float ssum[SB];
 #pragma unroll
   for (int i = 0; i < SB; ++i) ssum[i] = 0.f;
-  // the wave's first summed block (per-channel)
-  constexpr int sb0 = GROUPED ? 0 : (WM >= GN ? wn * SB : (wn < WM ? wn : WM));
+  // the wave's first summed block
+  constexpr int sb0 = WM >= GN ? wn * SB : (wn < WM ? wn : WM);
 
   const uint16_t* __restrict__ scale = (const uint16_t*)a.scale;
   const uint16_t* __restrict__ offset = (const uint16_t*)a.offset;
   const float cbias = a.code_bias;
   (void)has_offset;
-  float* gscr = (float*)(smem + T::GOff) + wave * (32 * WM);  // this wave's S_g scratch
 
   // logical column of lane's block j (int4: block 2p + e covers byte pair p, parity e)
   auto block_col = [&](int j) -> int {
@@ -319,14 +338,9 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   };
 
   // fold the group that ends at row 32 (e = 0) or 64 (e = 1) of the k-step whose
-  // parameter rows are at Ps: tot += s * acc + s * (off - C) * S_g
+  // parameter rows are at Ps (and S_g rows after them): tot += s * acc + s * (off - C) * S_g
   auto rescale = [&](const uint16_t* Ps, int e) {
-#pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const float t = ssum[i] + __shfl_xor(ssum[i], 32, 64);
-      if (lane < 32) gscr[32 * i + lane] = t;
-      ssum[i] = 0.f;  // per-group: SB == WM
-    }
+    const float* Sg = (const float*)((const uint8_t*)Ps + T::Pbytes) + e * T::BM + wm * (32 * WM);
     float s[WN], q[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
@@ -340,7 +354,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     for (int i = 0; i < WM; ++i) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const f32x4_t sr = *(const f32x4_t*)(gscr + 32 * i + 8 * rq + 4 * (lane >> 5));
+        const f32x4_t sr = *(const f32x4_t*)(Sg + 32 * i + 8 * rq + 4 * (lane >> 5));
 #pragma unroll
         for (int j = 0; j < WN; ++j)
 #pragma unroll
@@ -406,12 +420,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       Frag<WM, T::Reads>& nxt = (kk & 1) ? f0 : f1;
       if (kk < 3) load_frag<T, WM>(As, Bs, kk + 1, wm, wn, lane, nxt);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (GROUPED) {
-#pragma unroll
-        for (int i = 0; i < WM; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) ssum[i] = dot2_ones<BF16>(cur.a[i][q], ssum[i]);
-      } else {
+      if constexpr (!GROUPED) {
 #pragma unroll
         for (int t = 0; t < SB; ++t) {
           // sb0 is a constant and t an unrolled index: the block is chosen at compile time

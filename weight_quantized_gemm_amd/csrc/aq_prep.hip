@@ -2,7 +2,9 @@
 //  * the empty-K case, out = bias + x3 ("CANN ops-transformer ... aclnnWeightQuantMatmulAllReduce
 //    完全指南", section 空 tensor 支持度 (empty tensors));
 //  * per-group scale and offset stored transposed with a transposed x2 (section 参数说明):
-//    copied to the row-major (groups, n) layout the GEMM kernels read, in the workspace.
+//    copied to the row-major (groups, n) layout the GEMM kernels read, in the workspace;
+//  * per-group row sums of x1, S_g[r] = sum of x1[r, k] over the k of group g, which the
+//    factored product needs at each group end (see aq_gemm.h).
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -42,7 +44,54 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __rest
   }
 }
 
+// S[g][r] = sum of x1[r, k] over group g's k, fp32, in a fixed order.  A wave takes one row
+// at a time: lane l sums x1[r, 512 w + 8 l .. + 7] (v_dot2 against ones), four lanes add up
+// a 32-k piece, and the row's pieces land in the wave's LDS strip; then lane j adds up the
+// pieces of groups j, j + 64, ... in k order (groups are multiples of 32 long, k too).
+template <bool BF16>
+__global__ __launch_bounds__(256) void group_rowsums_kernel(const uint16_t* __restrict__ x1,
+                                                            float* __restrict__ S, int64_t m, int k,
+                                                            int g, int groups) {
+  __shared__ float piece[4][2048];  // k / 32 < 2048 pieces per row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int np = k / 32, per = g / 32;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < m; r += (int64_t)gridDim.x * 4) {
+    const uint16_t* row = x1 + r * k;
+    for (int w0 = 0; w0 < k; w0 += 512) {
+      const int kk = w0 + 8 * lane;
+      float v = 0.f;
+      if (kk < k) {
+        const u32x4_t d = *(const u32x4_t*)(row + kk);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v = dot2_ones<BF16>(d[q], v);
+      }
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      if ((lane & 3) == 0 && kk < k) piece[wave][kk / 32] = v;
+    }
+    __builtin_amdgcn_wave_barrier();  // the strip is written (one wave: LDS in order)
+    for (int gi = lane; gi < groups; gi += 64) {
+      const int p1 = min(np, (gi + 1) * per);
+      float t = 0.f;
+      for (int p = gi * per; p < p1; ++p) t += piece[wave][p];
+      S[(int64_t)gi * m + r] = t;
+    }
+    __builtin_amdgcn_wave_barrier();  // read before the next row overwrites it
+  }
+}
+
 }  // namespace
+
+hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream) {
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((a.m + 3) / 4, 16384));
+  if (a.bf16)
+    hipLaunchKernelGGL(group_rowsums_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)a.x1, a.gsum, a.m, a.k, a.group, a.groups);
+  else
+    hipLaunchKernelGGL(group_rowsums_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)a.x1, a.gsum, a.m, a.k, a.group, a.groups);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose16(const void* src, void* dst, int rows, int cols, hipStream_t stream) {
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));

@@ -31,6 +31,7 @@ struct AqPlan {
   int64_t partial_bytes = 0;
   int64_t rowsum_bytes = 0;
   int64_t param_bytes = 0;   // per-group scale / offset given transposed: row-major copies
+  int64_t gsum_bytes = 0;    // large m, per-group: row sums of x1 per group, (groups, m) fp32
   int64_t workspace = 0;
 };
 
@@ -50,7 +51,8 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
     }
   }
   if (p.params_t) pl.param_bytes = align_up(p.groups * p.n * 2);
-  pl.workspace = pl.partial_bytes + pl.rowsum_bytes + 2 * pl.param_bytes;
+  if (!pl.small_m && p.mode == QuantMode::kGroup) pl.gsum_bytes = align_up(p.groups * p.m * 4);
+  pl.workspace = pl.partial_bytes + pl.rowsum_bytes + 2 * pl.param_bytes + pl.gsum_bytes;
   return pl;
 }
 
@@ -168,7 +170,11 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
     a.rowsum_part = pl.rowsum_bytes ? (float*)(w + pl.partial_bytes) : nullptr;
     e = wq::launch_aq_smallm(a, s);
   } else {
-    e = wq::launch_aq_gemm(a, s);  // row sums are formed in-kernel; no workspace
+    if (pl.gsum_bytes) {  // per-group row sums first (the tiled kernel reads them per stage)
+      a.gsum = (float*)((char*)workspace + pl.partial_bytes + pl.rowsum_bytes + 2 * pl.param_bytes);
+      if ((e = wq::launch_group_rowsums(a, s)) != hipSuccess) return WQ_ERR_RUNTIME;
+    }
+    e = wq::launch_aq_gemm(a, s);
   }
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
 }

@@ -16,6 +16,7 @@ struct AqArgs {
   void* out;             // (m, n)
   float* partial;        // small-m path: split-k partials [splits][m][n]
   float* rowsum_part;    // small-m path, per-tensor / per-channel: row sums [splits][m]
+  float* gsum;           // large-m per-group path: row sums of x1 per group, (groups, m)
   int64_t m;
   int32_t k, n;
   int32_t group;         // group size along k (per-group); k otherwise
@@ -65,6 +66,8 @@ inline hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream) {
 }
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream);  // k == 0
+// large m, per-group: a.gsum[g][r] = sum of x1[r, k] over the k of group g (fp32, fixed order)
+hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream);
 // dst (rows, cols) = transpose of src (cols, rows), 16-bit elements
 hipError_t launch_transpose16(const void* src, void* dst, int rows, int cols, hipStream_t stream);
 hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);
