@@ -233,6 +233,23 @@ def test_workspace_sizes(wqlib):
     st = wqlib.wq_antiquant_matmul(r(x1), r(x2), None, r(sc), None, None, 64, r(out),
                                    C.c_void_p(FAKE), C.c_uint64(size.value - 1), None)
     assert st == INVALID
+    # large m, per-group: room for the row sums of x1 per group, (groups, m) fp32
+    x1, x2, sc, out = base(m=300, k=1024, n=256, scale=[8, 256])
+    assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 128,
+                                                        r(out), r(size)) == OK
+    assert size.value >= 8 * 300 * 4
+    # ... and transposed per-group parameters add two row-major copies
+    xt = D([1024, 256], W.WQ_I8, None, [1, 1024])
+    st_ = D([8, 256], W.WQ_F16, None, [1, 8])
+    size_t = C.c_uint64(0)
+    assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(xt), None, r(st_), r(D([8, 256], W.WQ_F16, None, [1, 8])),
+                                                        None, 128, r(out), r(size_t)) == OK
+    assert size_t.value >= size.value + 2 * 8 * 256 * 2
+    # per-channel large m needs none
+    x1, x2, sc, out = base(m=300, k=1024, n=256)
+    assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
+                                                        r(out), r(size)) == OK
+    assert size.value == 0
 
 
 def qm(wqlib, x1, x2, dq, out, bias=None, x3=None, pt=None, acc=None):

@@ -237,15 +237,10 @@ __device__ __forceinline__ i32x16_t mfma32x32x32_i8(const u32x4_t& a, const u32x
 }
 
 // ----------------------------------------------------------------------------- LDS reads
-// gfx950 transpose reads.  Within each group of 16 lanes:
-//  * tr16: slot j of lane L is 16-bit element (L % 4) of the 8 bytes addressed by lane
-//    4*j + L/4;
-//  * tr8:  slot j of lane L is byte (L % 8) of the 8 bytes addressed by lane 2*j + L/8.
-// With a row-major (n-contiguous) tile, lanes addressing (row k0 + j, 4 or 8 columns) give
-// every lane one column and consecutive k -- the MFMA B-operand layout.
-__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((WQ_LDS i16x4_t*)(p)));
-}
+// gfx950 transpose read: within each group of 16 lanes, slot j of lane L is byte (L % 8) of
+// the 8 bytes addressed by lane 2*j + L/8.  With a row-major (n-contiguous) tile, lanes
+// addressing (row k0 + j, 8 columns) give every lane one column and consecutive k -- the
+// MFMA B-operand layout.
 __device__ __forceinline__ u32x2_t lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((WQ_LDS i32x2_t*)(p)));
 }

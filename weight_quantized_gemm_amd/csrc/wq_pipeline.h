@@ -82,18 +82,4 @@ __device__ __forceinline__ void dma_group_params(uint8_t* dst, const u32x4_t& rs
   }
 }
 
-// Direct-to-LDS load of one group's scale and offset rows (COLS 16-bit values from column
-// n0 each) for a 32-row k block, which lies inside one group (group sizes are multiples of
-// 32): scale at +0, offset at +256 bytes.  Two loads per wave, each by a quarter of the
-// wave (lanes 0..15, then 16..31; the other lanes stay inactive and write nothing); with
-// no offset tensor the offset row reads zeros.
-template <int COLS>
-__device__ __forceinline__ void dma_group_row(uint8_t* dst, const u32x4_t& rs, const u32x4_t& ro,
-                                              bool has_offset, int g, int n, int lane) {
-  static_assert(COLS == 128, "one 256-byte row per quarter wave");
-  const uint32_t off = (uint32_t)g * (uint32_t)n * 2u + 16u * (uint32_t)(lane & 15);
-  if (lane < 16) dma16(rs, dst, off);                                            // dst + 16 lane
-  else if (lane < 32) dma16(has_offset ? ro : rs, dst, has_offset ? off : kOOB);  // dst + 256 + ...
-}
-
 }  // namespace wq
