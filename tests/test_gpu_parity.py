@@ -391,3 +391,78 @@ def test_full_size_sampled(name):
         got = to_f64(y).reshape(-1, case.n)[rows]
         r = oracle.compare(got, ref.reshape(got.shape), case.out)
         assert r["ok"], r
+
+
+# ---------------------------------------------------------------- seeded sweep
+def _sweep_antiquant(count=48, seed=4242):
+    """Random combinations of dtype, weight format, mode, layout, optional inputs and ragged
+    shapes (small-m and tiled paths), each drawn from a fixed seed."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        act = str(rng.choice(["fp16", "bf16"]))
+        weight = str(rng.choice(["int8", "int4", "fp8e4m3"], p=[0.45, 0.35, 0.2]))
+        align = 64 if weight == "int4" else 32
+        k = int(align * rng.integers(1, 25))
+        n = int(align * rng.integers(1, 13))
+        m = int(rng.choice([1, 2, 7, 31, 32, 33, 65, 100, 257, 300]))
+        mode = "channel" if weight == "fp8e4m3" else str(rng.choice(["tensor", "channel", "group"]))
+        g = 0
+        if mode == "group":
+            gs = [v for v in range(32, k, 32)]
+            if not gs:
+                mode = "channel"
+            else:
+                g = int(rng.choice(gs))
+        lead = (m,)
+        if m % 2 == 0 and m > 2 and rng.random() < 0.3:
+            lead = (2, m // 2)
+        spec = dict(act=act, weight=weight, x1_shape=lead + (k,), n=n, mode=mode, group_size=g,
+                    with_offset=weight != "fp8e4m3" and bool(rng.random() < 0.7),
+                    with_bias=bool(rng.random() < 0.6), with_x3=bool(rng.random() < 0.6),
+                    channel_2d=bool(rng.random() < 0.3), x2_transposed=bool(rng.random() < 0.3))
+        if weight == "fp8e4m3":
+            spec["scale_dist"] = ("uniform", 2e-4, 1e-3)
+        name = (f"sw{i}_{act}_{weight}_{mode}{g or ''}_m{m}k{k}n{n}"
+                f"{'_xt' if spec['x2_transposed'] else ''}")
+        out.append((name, spec))
+    return out
+
+
+SWEEP = _sweep_antiquant()
+
+
+@pytest.mark.parametrize("name,spec", SWEEP, ids=[c[0] for c in SWEEP])
+def test_sweep_antiquant(name, spec):
+    case = workloads.make_antiquant(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec)
+    check_aq(case)
+
+
+def _sweep_w8a8(count=16, seed=4343):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        k = int(32 * rng.integers(1, 33))
+        n = int(32 * rng.integers(1, 17))
+        m = int(rng.choice([1, 5, 32, 77, 256, 300]))
+        spec = dict(out=str(rng.choice(["fp16", "bf16"])), x1_shape=(m, k), n=n,
+                    dequant=str(rng.choice(["tensor", "channel"])),
+                    dequant_dtype=str(rng.choice(["fp32", "bf16"])),
+                    with_bias=bool(rng.random() < 0.7), with_pertoken=bool(rng.random() < 0.7),
+                    with_x3=bool(rng.random() < 0.6), x2_transposed=bool(rng.random() < 0.4))
+        out.append((f"sw8_{i}_m{m}k{k}n{n}{'_xt' if spec['x2_transposed'] else ''}", spec))
+    return out
+
+
+SWEEP8 = _sweep_w8a8()
+
+
+@pytest.mark.parametrize("name,spec", SWEEP8, ids=[c[0] for c in SWEEP8])
+def test_sweep_w8a8(name, spec):
+    _announce(name)
+    case = workloads.make_w8a8(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec)
+    y, acc = run_w8a8(case)
+    ref, racc = ref_w8a8(case)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), racc)
+    r = oracle.compare(to_f64(y).reshape(ref.shape), ref, case.out)
+    assert r["ok"], r
