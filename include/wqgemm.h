@@ -54,7 +54,8 @@ typedef enum wq_dtype {
 
 /*
  * Tensor descriptor (the role of the pages' aclTensor).
- *   data    device address of the first element (for an empty tensor it may be NULL).
+ *   data    device address of the first element, 16-byte aligned (for an empty tensor it
+ *           may be NULL).
  *   dtype   a wq_dtype.
  *   ndim    1, 2 or 3.
  *   shape   logical shape; entries past ndim are ignored.
@@ -123,7 +124,7 @@ int wq_antiquant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor*
 /*
  * Enqueue the anti-quant matmul on `stream` (a hipStream_t; NULL = the null stream).
  * Same arguments as above, plus the caller's device workspace of workspace_size bytes
- * (at least what the size query returned; NULL allowed when that is 0).
+ * (at least what the size query returned, 256-byte aligned; NULL allowed when that is 0).
  * Repeats every check of the size query; a workspace smaller than required is
  * WQ_ERR_PARAM_INVALID.  Returns WQ_ERR_RUNTIME if a launch fails.
 

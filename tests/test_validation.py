@@ -219,6 +219,12 @@ def test_layout_and_alias(wqlib):
     assert aq(wqlib, x1, D([64, 128], W.WQ_I8, None, [256, 1]), sc, out) == INVALID
     # the output may not alias an input
     assert aq(wqlib, x1, x2, sc, D([32, 128], f16, FAKE + 0x100000)) == INVALID
+    # every tensor starts 16-byte aligned (the kernels move 16-byte pieces)
+    assert aq(wqlib, D([32, 64], f16, FAKE + 0x900002), x2, sc, out) == INVALID
+    assert aq(wqlib, x1, x2, sc, out, bias=D([128], f16, FAKE + 0x900008)) == INVALID
+    assert aq(wqlib, x1, x2, sc, out, bias=D([128], f16, FAKE + 0x900010)) == OK
+    assert qm(wqlib, D([16, 64], W.WQ_I8, FAKE + 0x900004), D([64, 128], W.WQ_I8), D([128], W.WQ_F32),
+              D([16, 128], W.WQ_BF16)) == INVALID
 
 
 def test_workspace_sizes(wqlib):
@@ -232,6 +238,10 @@ def test_workspace_sizes(wqlib):
     # a workspace smaller than required is refused before anything is launched
     st = wqlib.wq_antiquant_matmul(r(x1), r(x2), None, r(sc), None, None, 64, r(out),
                                    C.c_void_p(FAKE), C.c_uint64(size.value - 1), None)
+    assert st == INVALID
+    # a workspace that is not 256-byte aligned is refused too, before any launch
+    st = wqlib.wq_antiquant_matmul(r(x1), r(x2), None, r(sc), None, None, 64, r(out),
+                                   C.c_void_p(FAKE + 16), C.c_uint64(size.value), None)
     assert st == INVALID
     # large m, per-group: room for the row sums of x1 per group, (groups, m) fp32
     x1, x2, sc, out = base(m=300, k=1024, n=256, scale=[8, 256])

@@ -133,6 +133,7 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   const wq::AqPlan pl = wq::plan_antiquant(p);
   if (workspace_size < (uint64_t)pl.workspace) return WQ_ERR_PARAM_INVALID;
   if (pl.workspace > 0 && !workspace) return WQ_ERR_PARAM_NULLPTR;
+  if (pl.workspace > 0 && ((uintptr_t)workspace & 255u) != 0) return WQ_ERR_PARAM_INVALID;
   hipStream_t s = (hipStream_t)stream;
 
   wq::AqArgs a{};

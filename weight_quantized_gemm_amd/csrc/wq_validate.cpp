@@ -23,6 +23,7 @@
 //    no other non-contiguous layout) and Constraints (n may exceed 65535 only then).
 #include <climits>
 #include <cstddef>
+#include <cstdint>
 
 #include "wq_problem.h"
 
@@ -83,6 +84,9 @@ bool same_shape(const wq_tensor* a, const wq_tensor* b) {
     if (a->shape[i] != b->shape[i]) return false;
   return true;
 }
+
+// The kernels move every tensor in 16-byte pieces from its first element on.
+bool aligned16(const wq_tensor* t) { return t == nullptr || ((uintptr_t)t->data & 15u) == 0; }
 
 bool aliases(const void* out, const wq_tensor* t) {
   return t != nullptr && t->data != nullptr && t->data == out;
@@ -183,6 +187,8 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
     if (t && !contiguous(t)) return WQ_ERR_PARAM_INVALID;
   for (const wq_tensor* t : {x1, x2, scale, offset, bias, x3})
     if (aliases(output->data, t)) return WQ_ERR_PARAM_INVALID;
+  for (const wq_tensor* t : {x1, x2, scale, offset, bias, x3, output})
+    if (!aligned16(t)) return WQ_ERR_PARAM_INVALID;
 
   if (p) {
     p->m = m; p->k = k; p->n = n; p->act = act; p->w4 = w4; p->f8 = f8; p->mode = mode;
@@ -249,6 +255,8 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
     if (t && !contiguous(t)) return WQ_ERR_PARAM_INVALID;
   for (const wq_tensor* t : {x1, x2, dq, bias, x3, pt, acc_out})
     if (aliases(output->data, t)) return WQ_ERR_PARAM_INVALID;
+  for (const wq_tensor* t : {x1, x2, dq, bias, x3, pt, acc_out, output})
+    if (!aligned16(t)) return WQ_ERR_PARAM_INVALID;
   if (acc_out)
     for (const wq_tensor* t : {x1, x2, dq, bias, x3, pt})
       if (aliases(acc_out->data, t)) return WQ_ERR_PARAM_INVALID;
