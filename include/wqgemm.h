@@ -129,10 +129,12 @@ int wq_antiquant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor*
  * WQ_ERR_PARAM_INVALID.  Returns WQ_ERR_RUNTIME if a launch fails.
 
  *
- * Workspace contents: none are expected on entry.  The call uses it for: the small-m path's
- * (m <= 32) fp32 split-k partial sums, until a finishing kernel of the same call has added
- * them; per-group scale and offset given transposed, copied row-major; and, per-group with
- * m > 32, the fp32 row sums of x1 over each group, (groups, m), written before the product.
+ * Workspace contents: none are expected on entry.  The call uses it for: fp32 split-k
+ * partial sums (and per-tensor / per-channel, partial row sums of x1), until a finishing
+ * kernel of the same call has added them in split order -- always at m <= 32, and at larger
+ * m when the output tiles alone would leave compute units idle; per-group scale and offset
+ * given transposed, copied row-major; and, per-group with m > 32, the fp32 row sums of x1
+ * over each group, (groups, m), written before the product.
  */
 int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
                         const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,
@@ -162,7 +164,12 @@ int wq_quant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor* x2,
                                        const wq_tensor* pertoken_scale, const wq_tensor* output,
                                        const wq_tensor* acc_out, uint64_t* workspace_size);
 
-/* Enqueue the W8A8 matmul on `stream`.  Same conventions as wq_antiquant_matmul. */
+/*
+ * Enqueue the W8A8 matmul on `stream`.  Same conventions as wq_antiquant_matmul.  The
+ * workspace (zero bytes unless the output tiles alone would leave compute units idle) holds
+ * int32 split-k partial products until a finishing kernel of the same call adds them; the
+ * sum wraps like the single-pass accumulator, so results do not depend on the split.
+ */
 int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
                     const wq_tensor* x3, const wq_tensor* dequant_scale,
                     const wq_tensor* pertoken_scale, const wq_tensor* output,

@@ -94,6 +94,26 @@ AQ_CASES = [
                                             mode="channel")),
     ("largem_maxn_pertensor_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(1024, 64), n=65504,
                                            mode="tensor")),
+    # 32 < m with few output tiles: k is split so that the workgroups fill the CUs, and a
+    # finishing kernel adds the fp32 partials (ragged m and n tiles; k with a 32-row tail;
+    # per-group splits on group boundaries, 96-wide groups in units of 192)
+    ("midm_m64_perchannel_bf16_i8_splitk", dict(act="bf16", weight="int8", x1_shape=(64, 4096), n=512,
+                                                mode="channel")),
+    ("midm_m100_pergroup96_fp16_i8_splitk", dict(act="fp16", weight="int8", x1_shape=(100, 2304), n=384,
+                                                 mode="group", group_size=96, offset_dist=("uniform", -4, 4))),
+    ("midm_m129_perchannel_fp16_i8_splitk_tail", dict(act="fp16", weight="int8", x1_shape=(129, 2080), n=256,
+                                                      mode="channel")),
+    ("midm_m200_pergroup128_bf16_i4_splitk", dict(act="bf16", weight="int4", x1_shape=(200, 2048), n=320,
+                                                  mode="group", group_size=128, with_bias=False)),
+    ("midm_m300_pertensor_bf16_i8_splitk", dict(act="bf16", weight="int8", x1_shape=(300, 1024), n=256,
+                                                mode="tensor")),
+    ("midm_m48_perchannel_bf16_f8_splitk", dict(act="bf16", weight="fp8e4m3", x1_shape=(48, 3072), n=288,
+                                                mode="channel", with_offset=False,
+                                                scale_dist=("uniform", 2e-4, 1e-3))),
+    ("midm_xt_m64_pergroup64_bf16_i8_splitk", dict(act="bf16", weight="int8", x1_shape=(64, 2048), n=256,
+                                                   mode="group", group_size=64, x2_transposed=True)),
+    ("midm_xt_m96_perchannel_fp16_i4_splitk", dict(act="fp16", weight="int4", x1_shape=(96, 2048), n=384,
+                                                   mode="channel", x2_transposed=True)),
     # x2 stored transposed, (n, k) (int4 packed along k), handed over as its (k, n) transpose
     # view; per-group scale and offset transposed with it
     ("xt_perchannel_bf16_i8_ragged", dict(act="bf16", weight="int8", x1_shape=(600, 288), n=544, mode="channel",
@@ -344,6 +364,11 @@ W8A8_CASES = [
                                     with_pertoken=False, x2_transposed=True)),
     # n beyond 65535, allowed with a transposed x2 only
     ("w8a8_xt_n70016", dict(out="bf16", x1_shape=(40, 64), n=70016, x2_transposed=True)),
+    # few output tiles: split k, int32 partials added by a finishing kernel (k with a 32-row
+    # tail; the accumulator still bit-exact)
+    ("w8a8_splitk_m64", dict(out="bf16", x1_shape=(64, 4096), n=512)),
+    ("w8a8_splitk_m300_tail_xt", dict(out="fp16", x1_shape=(300, 2080), n=320, x2_transposed=True)),
+    ("w8a8_splitk_m7_tensor", dict(out="bf16", x1_shape=(7, 3072), n=96, dequant="tensor", with_pertoken=False)),
 ]
 
 

@@ -255,11 +255,25 @@ def test_workspace_sizes(wqlib):
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(xt), None, r(st_), r(D([8, 256], W.WQ_F16, None, [1, 8])),
                                                         None, 128, r(out), r(size_t)) == OK
     assert size_t.value >= size.value + 2 * 8 * 256 * 2
-    # per-channel large m needs none
-    x1, x2, sc, out = base(m=300, k=1024, n=256)
+    # per-channel large m: none while the tiles fill the 256 CUs (16 x 16 tiles of 256)...
+    x1, x2, sc, out = base(m=4096, k=4096, n=4096)
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                         r(out), r(size)) == OK
     assert size.value == 0
+    # ... else fp32 split-k partials and row sums: 2 x 1 tiles of 256 rows want 128 splits,
+    # but a split keeps at least 512 k, so k = 1024 gives 2 splits
+    x1, x2, sc, out = base(m=300, k=1024, n=256)
+    assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
+                                                        r(out), r(size)) == OK
+    assert size.value == 2 * 300 * 256 * 4 + 2560          # partials, then row sums padded to 256
+    # W8A8: int32 partials under the same rule (tiles of 256 x 256)
+    i8 = W.WQ_I8
+    for (m, k, n), want in (((4096, 4096, 4096), 0), ((32, 8192, 8192), 8 * 32 * 8192 * 4),
+                            ((300, 1024, 256), 2 * 300 * 256 * 4)):
+        assert wqlib.wq_quant_matmul_get_workspace_size(
+            r(D([m, k], i8)), r(D([k, n], i8)), None, None, r(D([n], W.WQ_F32)), None,
+            r(D([m, n], W.WQ_BF16)), None, r(size)) == OK
+        assert size.value == want, (m, k, n, size.value)
 
 
 def qm(wqlib, x1, x2, dq, out, bias=None, x3=None, pt=None, acc=None):

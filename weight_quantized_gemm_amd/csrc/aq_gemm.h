@@ -167,7 +167,13 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   const int K = a.k, N = a.n;
   // bytes per weight row: a k row of n codes, or (transposed) a column row of k codes
   const int64_t x2_pitch = XT ? (W4 ? (K >> 1) : K) : (W4 ? (N >> 1) : N);
-  const int nk = (K + kBK - 1) / kBK;
+  // split k: this workgroup's k range.  Split starts are multiples of 64, and per-group of
+  // the group size too, so a split holds whole groups and only the last one has a tail.
+  const int split = blockIdx.y;
+  const int kbeg = split * a.kchunk;
+  const int kend = a.splits > 1 ? min(K, kbeg + a.kchunk) : K;
+  const int klen = kend - kbeg;
+  const int nk = (klen + kBK - 1) / kBK;
 
   // ---------------------------------------------------------------- DMA issue
   // x1: wave w fills 1 KiB blocks b = w + Waves*j (8 rows each); lane -> (row, physical
@@ -235,7 +241,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   };
   auto stage_rsrc = [&](int ks) {
     StageRsrc r;
-    r.k0 = ks * kBK;
+    r.k0 = kbeg + ks * kBK;
     r.st = smem + (ks % T::Stages) * T::Stage;
     r.ra = make_rsrc32(x1b + (int64_t)r.k0 * 2, x1_bytes - (uint32_t)r.k0 * 2);
     if constexpr (XT) {
@@ -377,7 +383,10 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   const int ecol = 8 * (lane % LanesPerRow);
   const int gcol = n0 + wn * WC + ecol;   // first of this lane's 8 output columns
   const bool col_ok = gcol < N;
-  const uint16_t* __restrict__ x3 = (const uint16_t*)a.x3;
+  // with split k the epilogue writes fp32 partials; x3, bias and the parameters are applied
+  // when the splits are added
+  const bool split_out = a.splits > 1;
+  const uint16_t* __restrict__ x3 = split_out ? nullptr : (const uint16_t*)a.x3;
   // bands of x3 held in registers ahead of use: one where the accumulators leave little room
   constexpr int XP = (!GROUPED && WM * WN >= 8) ? 1 : 2;
   u32x4_t xpre[XP][kPasses];
@@ -440,7 +449,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
         else bfr[j] = w8x8_to_act<BF16, WF>(cur.raw[j]);
       }
       // Per-group: a group's first 16-k step (group starts fall on multiples of 32, so on
-      // steps 0 and 2) starts its accumulators from zero through the MFMA's own operand
+      // steps 0 and 2; k is counted from the split's start, a group boundary) starts its accumulators from zero through the MFMA's own operand
       // instead of clearing them after the previous group's fold.
       bool fresh = false;
       if constexpr (GROUPED) {
@@ -462,7 +471,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       if constexpr (GROUPED) {
         if (kk & 1) {  // groups end on multiples of 32
           const int kdone = ks * kBK + kk * 16 + 16;
-          if (kdone <= K && (kdone % a.group == 0 || kdone == K))
+          if (kdone <= klen && (kdone % a.group == 0 || kdone == klen))
             rescale((const uint16_t*)(Bs + T::Bbytes), kk >> 1);
         }
       }
@@ -479,7 +488,13 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       if (lane < 32 && sb0 + t < WM) srow[wm * (32 * WM) + 32 * (sb0 + t) + lane] = v;
     }
     __syncthreads();
+    // split k: this split's row sums of the tile's rows, from the first column of tiles
+    if (split_out && tn == 0) {
+      for (int r = threadIdx.x; r < T::BM; r += T::Threads)
+        if (m0 + r < M) a.rowsum_part[(int64_t)split * M + m0 + r] = srow[r];
+    }
   }
+  float* __restrict__ part = split_out ? a.partial + (int64_t)split * M * N : nullptr;
   // Each wave stages one 32-row band of its tile at a time in its own LDS region, then
   // moves 8 consecutive columns per lane with 16-byte accesses.
   float* E = (float*)smem + wave * (32 * EP);
@@ -532,6 +547,11 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       const f32x4_t v0 = *(const f32x4_t*)(E + er * EP + ecol);
       const f32x4_t v1 = *(const f32x4_t*)(E + er * EP + ecol + 4);
       if (grow >= M || !col_ok) continue;
+      if (split_out) {
+        *(f32x4_t*)(part + grow * N + gcol) = v0;
+        *(f32x4_t*)(part + grow * N + gcol + 4) = v1;
+        continue;
+      }
       const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       float sr = 0.f;
       if constexpr (!GROUPED) sr = srow[wm * (32 * WM) + 32 * i + er];
@@ -587,10 +607,12 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   hipError_t e = raise_lds_limit((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+  const int splits = a.splits > 1 ? a.splits : 1;
   if ((e = profile_begin(stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(T::Threads), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)splits), dim3(T::Threads), lds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return profile_end(stream);
+  if ((e = profile_end(stream)) != hipSuccess) return e;
+  return splits > 1 ? launch_aq_splitk_finish(a, stream) : hipSuccess;
 }
 
 // Tile configurations (wave grid GM x GN, blocks per wave WM x WN).  The matrix cores and
@@ -606,10 +628,14 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
 template <bool BF16, int WF>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   constexpr bool W4 = WF == kWInt4;
+  // per-tensor / per-channel with m <= 128: the 2x4 waves of 64x64 (128x256), so that a
+  // short m computes fewer padding rows (aq_gemm_tile_m gives the planner the same choice)
+  const bool short_m = a.m <= 128;
   if (a.x2t) {  // transposed weights: the default tile of each mode
     if constexpr (WF != kWFp8) {
       if (a.grouped) return launch_one<BF16, WF, 2, 4, 2, 2, true, true>(a, stream);
     }
+    if (short_m) return launch_one<BF16, WF, 2, 4, 2, 2, false, true>(a, stream);
     return launch_one<BF16, WF, 2, 4, 4, 2, false, true>(a, stream);
   }
   if constexpr (WF != kWFp8) {  // FLOAT8_E4M3FN weights come per-channel only
@@ -628,7 +654,9 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
       if constexpr (!W4) return launch_one<BF16, WF, 1, 8, 8, 1, false>(a, stream);
       else return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
     case 2: return launch_one<BF16, WF, 4, 2, 2, 4, false>(a, stream);
-    default: return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
+    default:
+      if (short_m) return launch_one<BF16, WF, 2, 4, 2, 2, false>(a, stream);
+      return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
   }
 }
 

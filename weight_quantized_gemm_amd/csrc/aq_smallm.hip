@@ -354,11 +354,12 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   }
 }
 
-// Split-k finish: out = [s*P + s*(off-C)*S] (per-tensor / per-channel) or T (per-group),
-// + bias + x3, where P / T and S are the sums of the split partials in split order.  A
-// thread handles four consecutive columns of one row (n is a multiple of 32).
+// Split-k finish, for this kernel and for the large-m kernel (aq_gemm.h):
+// out = [s*P + s*(off-C)*S] (per-tensor / per-channel) or T (per-group), + bias + x3, where
+// P / T and S are the sums of the split partials in split order.  A thread handles four
+// consecutive columns of one row (n is a multiple of 32).
 template <bool BF16, bool GROUPED>
-__global__ __launch_bounds__(256) void aq_smallm_finish(const AqArgs a) {
+__global__ __launch_bounds__(256) void aq_splitk_finish(const AqArgs a) {
   const int N = a.n;
   const int64_t quads = a.m * (N / 4);
   const int64_t plane = a.m * N;
@@ -416,17 +417,23 @@ hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = profile_end(stream)) != hipSuccess) return e;
   if (a.splits == 1) return hipSuccess;  // the kernel wrote the output
-  const int64_t quads = a.m * (a.n / 4);
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((quads + 255) / 256, 8192));
-  hipLaunchKernelGGL((aq_smallm_finish<BF16, GROUPED>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_aq_splitk_finish(a, stream);
 }
 
 }  // namespace
 
-SmallmPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped) {
+hipError_t launch_aq_splitk_finish(const AqArgs& a, hipStream_t stream) {
+  const int64_t quads = a.m * (a.n / 4);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((quads + 255) / 256, 8192));
+  auto kern = a.bf16 ? (a.grouped ? aq_splitk_finish<true, true> : aq_splitk_finish<true, false>)
+                     : (a.grouped ? aq_splitk_finish<false, true> : aq_splitk_finish<false, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+SplitPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped) {
   (void)m; (void)group; (void)grouped;
-  SmallmPlan p;
+  SplitPlan p;
   const int slabs = (n + kSlab - 1) / kSlab;
   const int want = std::max(1, 256 / std::max(1, slabs));  // about one workgroup per CU
   // whole units per split, a multiple of kWaves units when the range allows (balance)

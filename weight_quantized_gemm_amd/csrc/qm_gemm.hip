@@ -19,6 +19,8 @@
 // of k per column, 16-byte fragment loads, no transpose.  The epilogue
 // stages the accumulators through LDS so that x3, the output and the int32 accumulator
 // move in 16-byte row-contiguous accesses.
+#include <algorithm>
+
 #include "wq_kernels.h"
 #include "wq_pipeline.h"
 
@@ -33,6 +35,7 @@ constexpr int kAbytes = kBM * kRA;              // 16 KiB
 constexpr int kBbytes = kBK * kRB;              // 16 KiB
 constexpr int kStage = kAbytes + kBbytes;
 constexpr int kLds = kStages * kStage;          // 128 KiB
+static_assert(kBM == kQmTileM && kBN == kQmTileN, "the planner's tile is the kernel's");
 
 // Wave grid GM x GN with WM x WN 32x32 blocks per wave (256 x 256 per workgroup); XT: x2
 // stored transposed, (n, k).
@@ -54,7 +57,12 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   const int n0 = tn * kBN;
   const int64_t M = a.m;
   const int K = a.k, N = a.n;
-  const int nk = (K + kBK - 1) / kBK;
+  // split k: this workgroup's k range (split starts are multiples of 64, so only the last
+  // split can end in a partial k-step)
+  const int split = blockIdx.y;
+  const int kbeg = split * a.kchunk;
+  const int kend = a.splits > 1 ? min(K, kbeg + a.kchunk) : K;
+  const int nk = (kend - kbeg + kBK - 1) / kBK;
 
   // ------------------------------------------------------------------ DMA issue
   const uint8_t* x1b = (const uint8_t*)a.x1 + m0 * K;
@@ -98,7 +106,7 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   };
   auto stage_rsrc = [&](int ks) {
     StageRsrc r;
-    r.k0 = ks * kBK;
+    r.k0 = kbeg + ks * kBK;
     r.st = smem + (ks % kStages) * kStage;
     r.ra = make_rsrc(x1b + r.k0, x1_bytes - r.k0);
     if constexpr (XT) {
@@ -150,7 +158,10 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   const int ecol = 8 * (lane % LanesPerRow);
   const int gcol = n0 + wn * WC + ecol;
   const bool col_ok = gcol < N;
-  const uint16_t* x3 = (const uint16_t*)a.x3;
+  // with split k the epilogue writes int32 partials; bias, scales and x3 are applied when the
+  // splits are added
+  const bool split_out = a.splits > 1;
+  const uint16_t* x3 = split_out ? nullptr : (const uint16_t*)a.x3;
   u32x4_t xpre[2][kPasses];
   auto prefetch_x3 = [&](int i, int slot) {
 #pragma unroll
@@ -274,6 +285,12 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
       const i32x4_t v0 = *(const i32x4_t*)(E + er * EP + ecol);
       const i32x4_t v1 = *(const i32x4_t*)(E + er * EP + ecol + 4);
       if (grow >= M || !col_ok) continue;
+      if (split_out) {
+        int32_t* part = a.partial + (int64_t)split * M * N + grow * N + gcol;
+        *(i32x4_t*)part = v0;
+        *(i32x4_t*)(part + 4) = v1;
+        continue;
+      }
       int32_t v[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -304,6 +321,59 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   }
 }
 
+// Split-k finish: acc = the int32 partials added in split order (two's complement wrap, so
+// the sum is the single-pass accumulator bit for bit) + bias; the optional accumulator
+// output, then out = acc * dequant_scale * pertoken_scale + x3, rounded once.  A thread
+// handles four consecutive columns of one row (n is a multiple of 32).
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void qm_splitk_finish(const QmArgs a) {
+  const int N = a.n;
+  const int64_t quads = a.m * (N / 4);
+  const int64_t plane = a.m * N;
+  const uint16_t* x3 = (const uint16_t*)a.x3;
+  uint16_t* out = (uint16_t*)a.out;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = q / (N / 4);
+    const int col = 4 * (int)(q - row * (N / 4));
+    const int64_t idx = row * N + col;
+    i32x4_t v = *(const i32x4_t*)(a.partial + idx);
+    for (int s = 1; s < a.splits; ++s) {
+      const i32x4_t p = *(const i32x4_t*)(a.partial + (int64_t)s * plane + idx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (int32_t)((uint32_t)v[e] + (uint32_t)p[e]);
+    }
+    if (a.bias) {
+      const i32x4_t b = *(const i32x4_t*)(a.bias + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (int32_t)((uint32_t)v[e] + (uint32_t)b[e]);
+    }
+    if (a.acc_out) *(i32x4_t*)(a.acc_out + idx) = v;
+    const float pt = a.pt ? a.pt[row] : 1.f;
+    u32x2_t xv{0u, 0u};
+    if (x3) xv = *(const u32x2_t*)(x3 + idx);
+    uint32_t o[2];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      float dq[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int dc = a.dq_per_tensor ? 0 : col + e + h;
+        dq[h] = a.dq_bf16 ? bf16_bits_to_f32(((const uint16_t*)a.dq)[dc]) : ((const float*)a.dq)[dc];
+      }
+      float y0 = (float)v[e] * dq[0] * pt, y1 = (float)v[e + 1] * dq[1] * pt;
+      if (x3) {
+        const uint32_t xw = xv[e >> 1];
+        y0 += OUT_BF16 ? bf16_bits_to_f32(xw & 0xffffu) : f16_bits_to_f32(xw & 0xffffu);
+        y1 += OUT_BF16 ? bf16_bits_to_f32(xw >> 16) : f16_bits_to_f32(xw >> 16);
+      }
+      o[e >> 1] = (uint32_t)(OUT_BF16 ? f32_to_bf16_rne(y0) : f32_to_f16_rne(y0)) |
+                  ((uint32_t)(OUT_BF16 ? f32_to_bf16_rne(y1) : f32_to_f16_rne(y1)) << 16);
+    }
+    *(u32x2_t*)(out + idx) = u32x2_t{o[0], o[1]};
+  }
+}
+
 }  // namespace
 
 hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
@@ -320,10 +390,17 @@ hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   hipError_t e = raise_lds_limit((const void*)kern, kLds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+  const int splits = a.splits > 1 ? a.splits : 1;
   if ((e = profile_begin(stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), (size_t)kLds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)splits), dim3(threads), (size_t)kLds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return profile_end(stream);
+  if ((e = profile_end(stream)) != hipSuccess) return e;
+  if (splits == 1) return hipSuccess;
+  const int64_t quads = a.m * (a.n / 4);
+  const int64_t fblocks = std::max<int64_t>(1, std::min<int64_t>((quads + 255) / 256, 8192));
+  hipLaunchKernelGGL(a.out_bf16 ? qm_splitk_finish<true> : qm_splitk_finish<false>, dim3((unsigned)fblocks),
+                     dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace wq

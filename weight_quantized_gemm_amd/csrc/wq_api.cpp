@@ -16,6 +16,31 @@
 #include "wq_problem.h"
 
 namespace wq {
+
+// Workgroup tile rows of the tiled kernel's default configurations (see aq_gemm.h): 128 for
+// per-group, and for per-tensor / per-channel while m fits one such tile; 256 otherwise.
+int aq_gemm_tile_m(int64_t m, bool grouped) { return (grouped || m <= 128) ? 128 : 256; }
+
+// Split k when the tiles alone would leave CUs idle: as many splits as bring the workgroups
+// (one per CU: each takes most of a CU's LDS) up to at most the CU count of an MI355X, each
+// at least 512 k long (the pipeline fill amortises), in whole units of k.
+SplitPlan gemm_split_plan(int64_t tiles, int k, int unit) {
+  constexpr int64_t kCUs = 256;
+  SplitPlan p;
+  p.kchunk = k;
+  p.splits = 1;
+  const int64_t want = kCUs / std::max<int64_t>(1, tiles);
+  if (want < 2) return p;
+  const int min_chunk = (512 + unit - 1) / unit * unit;
+  int per = (int)((k + want - 1) / want);
+  per = std::max(min_chunk, (per + unit - 1) / unit * unit);
+  const int splits = (k + per - 1) / per;
+  if (splits < 2) return p;
+  p.kchunk = per;
+  p.splits = splits;
+  return p;
+}
+
 namespace {
 
 constexpr int64_t kAlign = 256;
@@ -27,7 +52,7 @@ constexpr int64_t kSmallM = 32;
 struct AqPlan {
   bool empty_k = false;
   bool small_m = false;
-  SmallmPlan sm;
+  SplitPlan split;           // k splits of the small-m or the tiled kernel
   int64_t partial_bytes = 0;
   int64_t rowsum_bytes = 0;
   int64_t param_bytes = 0;   // per-group scale / offset given transposed: row-major copies
@@ -42,13 +67,19 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
     return pl;
   }
   pl.small_m = p.m <= kSmallM;
+  const bool grouped = p.mode == QuantMode::kGroup;
   if (pl.small_m) {
-    const bool grouped = p.mode == QuantMode::kGroup;
-    pl.sm = aq_smallm_plan(p.m, (int)p.k, (int)p.n, (int)p.group, grouped);
-    if (pl.sm.splits > 1) {
-      pl.partial_bytes = align_up((int64_t)pl.sm.splits * p.m * p.n * (int64_t)sizeof(float));
-      pl.rowsum_bytes = grouped ? 0 : align_up((int64_t)pl.sm.splits * p.m * (int64_t)sizeof(float));
-    }
+    pl.split = aq_smallm_plan(p.m, (int)p.k, (int)p.n, (int)p.group, grouped);
+  } else {
+    // per-group splits end on group boundaries (the precomputed S_g cover whole groups)
+    const int unit = grouped ? (p.group % 64 == 0 ? (int)p.group : 2 * (int)p.group) : 64;
+    const int bm = aq_gemm_tile_m(p.m, grouped);
+    const int64_t tiles = (p.m + bm - 1) / bm * ((p.n + kAqTileN - 1) / kAqTileN);
+    pl.split = gemm_split_plan(tiles, (int)p.k, unit);
+  }
+  if (pl.split.splits > 1) {
+    pl.partial_bytes = align_up((int64_t)pl.split.splits * p.m * p.n * (int64_t)sizeof(float));
+    pl.rowsum_bytes = grouped ? 0 : align_up((int64_t)pl.split.splits * p.m * (int64_t)sizeof(float));
   }
   if (p.params_t) pl.param_bytes = align_up(p.groups * p.n * 2);
   if (!pl.small_m && p.mode == QuantMode::kGroup) pl.gsum_bytes = align_up(p.groups * p.m * 4);
@@ -64,6 +95,20 @@ int tile_override() {
     return e ? std::atoi(e) : 0;
   }();
   return v;
+}
+
+// The W8A8 kernel's k splits and int32 partials.
+struct QmPlan {
+  SplitPlan split;
+  int64_t workspace = 0;
+};
+QmPlan plan_quant(const QuantProblem& p) {
+  QmPlan pl;
+  if (p.k == 0) return pl;
+  const int64_t tiles = (p.m + kQmTileM - 1) / kQmTileM * ((p.n + kQmTileN - 1) / kQmTileN);
+  pl.split = gemm_split_plan(tiles, (int)p.k, 64);
+  if (pl.split.splits > 1) pl.workspace = align_up((int64_t)pl.split.splits * p.m * p.n * (int64_t)sizeof(int32_t));
+  return pl;
 }
 
 float code_bias(const AntiquantProblem& p) {
@@ -145,8 +190,8 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.grouped = p.mode == wq::QuantMode::kGroup;
   a.per_tensor = p.mode == wq::QuantMode::kTensor;
   a.code_bias = wq::code_bias(p);
-  a.splits = pl.sm.splits;
-  a.kchunk = pl.sm.kchunk;
+  a.splits = pl.split.splits;
+  a.kchunk = pl.split.kchunk;
   a.tile = wq::tile_override();
 
   hipError_t e;
@@ -165,10 +210,12 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
     e = wq::launch_aq_bias_x3(a, s);
     return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
   }
-  if (pl.small_m) {
+  {
     char* w = (char*)workspace;
     a.partial = pl.partial_bytes ? (float*)w : nullptr;
     a.rowsum_part = pl.rowsum_bytes ? (float*)(w + pl.partial_bytes) : nullptr;
+  }
+  if (pl.small_m) {
     e = wq::launch_aq_smallm(a, s);
   } else {
     if (pl.gsum_bytes) {  // per-group row sums first (the tiled kernel reads them per stage)
@@ -185,11 +232,11 @@ int wq_quant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor* x2,
                                        const wq_tensor* dequant_scale,
                                        const wq_tensor* pertoken_scale, const wq_tensor* output,
                                        const wq_tensor* acc_out, uint64_t* workspace_size) {
-  int st = wq::validate_quant(x1, x2, bias, x3, dequant_scale, pertoken_scale, output, acc_out,
-                              nullptr);
+  wq::QuantProblem p;
+  int st = wq::validate_quant(x1, x2, bias, x3, dequant_scale, pertoken_scale, output, acc_out, &p);
   if (st != WQ_OK) return st;
   if (!workspace_size) return WQ_ERR_PARAM_NULLPTR;
-  *workspace_size = 0;
+  *workspace_size = (uint64_t)wq::plan_quant(p).workspace;
   return WQ_OK;
 }
 
@@ -198,11 +245,13 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
                     const wq_tensor* pertoken_scale, const wq_tensor* output,
                     const wq_tensor* acc_out, void* workspace, uint64_t workspace_size,
                     void* stream) {
-  (void)workspace;
-  (void)workspace_size;
   wq::QuantProblem p;
   int st = wq::validate_quant(x1, x2, bias, x3, dequant_scale, pertoken_scale, output, acc_out, &p);
   if (st != WQ_OK) return st;
+  const wq::QmPlan pl = wq::plan_quant(p);
+  if (workspace_size < (uint64_t)pl.workspace) return WQ_ERR_PARAM_INVALID;
+  if (pl.workspace > 0 && !workspace) return WQ_ERR_PARAM_NULLPTR;
+  if (pl.workspace > 0 && ((uintptr_t)workspace & 255u) != 0) return WQ_ERR_PARAM_INVALID;
   wq::QmArgs a{};
   a.x1 = (const int8_t*)p.x1; a.x2 = (const int8_t*)p.x2; a.bias = (const int32_t*)p.bias;
   a.x3 = p.x3; a.dq = p.dq; a.pt = (const float*)p.pt; a.out = p.out;
@@ -211,6 +260,9 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
   a.out_bf16 = p.out_dtype == WQ_BF16; a.dq_bf16 = p.dq_dtype == WQ_BF16;
   a.dq_per_tensor = p.dq_per_tensor;
   a.x2t = p.x2t;
+  a.splits = pl.split.splits;
+  a.kchunk = pl.split.kchunk;
+  a.partial = pl.workspace ? (int32_t*)workspace : nullptr;
   a.tile = wq::tile_override();
   hipError_t e = wq::launch_qm_gemm(a, (hipStream_t)stream);
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;

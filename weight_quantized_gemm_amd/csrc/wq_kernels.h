@@ -14,15 +14,15 @@ struct AqArgs {
   const void* bias;      // (n) or null
   const void* x3;        // (m, n) or null
   void* out;             // (m, n)
-  float* partial;        // small-m path: split-k partials [splits][m][n]
-  float* rowsum_part;    // small-m path, per-tensor / per-channel: row sums [splits][m]
+  float* partial;        // split k: partial products [splits][m][n] (per-group: folded)
+  float* rowsum_part;    // split k, per-tensor / per-channel: row sums of x1 [splits][m]
   float* gsum;           // large-m per-group path: row sums of x1 per group, (groups, m)
   int64_t m;
   int32_t k, n;
   int32_t group;         // group size along k (per-group); k otherwise
   int32_t groups;        // parameter rows (1 unless per-group)
-  int32_t splits;        // small-m path: k splits
-  int32_t kchunk;        // small-m path: k rows per split (a multiple of 64)
+  int32_t splits;        // k splits (1: the main kernel writes the output)
+  int32_t kchunk;        // k rows per split (a multiple of 64; per-group large m: of the group too)
   int32_t tiles_m, tiles_n;
   int32_t tile;          // tile configuration index (0 = default)
   float code_bias;       // C: the fed weight image is code + C
@@ -40,8 +40,11 @@ struct QmArgs {
   const float* pt;       // (m) or null
   void* out;             // (m, n) fp16 / bf16
   int32_t* acc_out;      // (m, n) or null
+  int32_t* partial;      // split k: int32 partial products [splits][m][n]
   int64_t m;
   int32_t k, n;
+  int32_t splits;        // k splits (1: the main kernel writes the output)
+  int32_t kchunk;        // k rows per split (a multiple of 64)
   int32_t tiles_m, tiles_n;
   int32_t tile;          // tile configuration index (0 = default)
   bool out_bf16, dq_bf16, dq_per_tensor;
@@ -65,6 +68,8 @@ inline hipError_t launch_aq_gemm(const AqArgs& a, hipStream_t stream) {
   return a.w4 ? launch_aq_gemm_int4(a, stream) : launch_aq_gemm_int8(a, stream);
 }
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream);
+// split k (either path): out from the a.splits partials, added in split order
+hipError_t launch_aq_splitk_finish(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream);  // k == 0
 // large m, per-group: a.gsum[g][r] = sum of x1[r, k] over the k of group g (fp32, fixed order)
 hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream);
@@ -72,11 +77,17 @@ hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream);
 hipError_t launch_transpose16(const void* src, void* dst, int rows, int cols, hipStream_t stream);
 hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);
 
-// Split-k plan of the small-m path, shared by the planner (workspace size) and the launch.
-struct SmallmPlan {
+// Split-k plans, shared by the planners (workspace sizes) and the launches.
+struct SplitPlan {
   int kchunk = 64;   // k rows per split (a multiple of 64)
   int splits = 1;
 };
-SmallmPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped);
+SplitPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped);
+// Large m: the workgroup tile the default configuration uses, and the k splits that bring
+// the workgroup count up to about one per CU when the tiles alone leave CUs idle.
+int aq_gemm_tile_m(int64_t m, bool grouped);
+constexpr int kAqTileN = 256;
+SplitPlan gemm_split_plan(int64_t tiles, int k, int unit);
+constexpr int kQmTileM = 256, kQmTileN = 256;
 
 }  // namespace wq
