@@ -49,6 +49,8 @@ DOMINANT = {
     "w8a8_bf16_8192x4096x8192": ("qm_gemm_kernel", "mfma"),
     "perchannel_bf16_fp8e4m3_4096x4096x4096": ("aq_gemm_kernel", "mfma"),
     "smallm_perchannel_bf16_fp8e4m3_32x8192x8192": ("aq_smallm_kernel", "hbm"),
+    "midm_perchannel_bf16_int8_128x8192x8192": ("aq_gemm_kernel", "hbm"),
+    "midm_w8a8_bf16_128x8192x8192": ("qm_gemm_kernel", "hbm"),
 }
 CACHE_BYTES = 256 << 20
 

@@ -357,10 +357,13 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
 // Split-k finish, for this kernel and for the large-m kernel (aq_gemm.h):
 // out = [s*P + s*(off-C)*S] (per-tensor / per-channel) or T (per-group), + bias + x3, where
 // P / T and S are the sums of the split partials in split order.  A thread handles four
-// consecutive columns of one row (n is a multiple of 32).
+// consecutive columns of one row (n is a multiple of 32).  The kernel streams the partials
+// (8 x 4 MiB at m = 128, n = 8192), so its loads are issued ahead of their use: the
+// partials four splits at a time, at clamped split indices so that no load waits behind a
+// branch, and the other operands before the first partial.
 template <bool BF16, bool GROUPED>
 __global__ __launch_bounds__(256) void aq_splitk_finish(const AqArgs a) {
-  const int N = a.n;
+  const int N = a.n, S = a.splits;
   const int64_t quads = a.m * (N / 4);
   const int64_t plane = a.m * N;
   const uint16_t* scale = (const uint16_t*)a.scale;
@@ -368,37 +371,58 @@ __global__ __launch_bounds__(256) void aq_splitk_finish(const AqArgs a) {
   const uint16_t* bias = (const uint16_t*)a.bias;
   const uint16_t* x3 = (const uint16_t*)a.x3;
   uint16_t* out = (uint16_t*)a.out;
+  auto half = [](const u32x2_t& w, int e) { return (uint16_t)(w[e >> 1] >> (16 * (e & 1))); };
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads;
        q += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = q / (N / 4);
     const int col = 4 * (int)(q - row * (N / 4));
     const int64_t idx = row * N + col;
+    const u32x2_t xv = x3 ? *(const u32x2_t*)(x3 + idx) : u32x2_t{0u, 0u};
+    const u32x2_t bv = bias ? *(const u32x2_t*)(bias + col) : u32x2_t{0u, 0u};
+    u32x2_t sv{0u, 0u}, ov{0u, 0u};
+    if constexpr (!GROUPED) {
+      if (a.per_tensor) {
+        const uint32_t s1 = scale[0], o1 = offset ? offset[0] : 0u;
+        sv = u32x2_t{s1 | (s1 << 16), s1 | (s1 << 16)};
+        ov = u32x2_t{o1 | (o1 << 16), o1 | (o1 << 16)};
+      } else {
+        sv = *(const u32x2_t*)(scale + col);
+        if (offset) ov = *(const u32x2_t*)(offset + col);
+      }
+    }
     f32x4_t v = *(const f32x4_t*)(a.partial + idx);
-    for (int s = 1; s < a.splits; ++s) {
-      const f32x4_t p = *(const f32x4_t*)(a.partial + (int64_t)s * plane + idx);
-      v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+    float srow = 0.f;
+    if constexpr (!GROUPED) srow = a.rowsum_part[row];
+    for (int s0 = 1; s0 < S; s0 += 4) {
+      f32x4_t p[4];
+      float r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sj = min(s0 + j, S - 1);
+        p[j] = *(const f32x4_t*)(a.partial + (int64_t)sj * plane + idx);
+        if constexpr (!GROUPED) r[j] = a.rowsum_part[(int64_t)sj * a.m + row];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (s0 + j < S) {
+          v[0] += p[j][0]; v[1] += p[j][1]; v[2] += p[j][2]; v[3] += p[j][3];
+          if constexpr (!GROUPED) srow += r[j];
+        }
+      }
     }
     float y[4] = {v[0], v[1], v[2], v[3]};
     if constexpr (!GROUPED) {
-      float srow = 0.f;
-      for (int s = 0; s < a.splits; ++s) srow += a.rowsum_part[(int64_t)s * a.m + row];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int pc = a.per_tensor ? 0 : col + e;
-        const float sv = act_to_f32<BF16>(scale[pc]);
-        const float ov = offset ? act_to_f32<BF16>(offset[pc]) : 0.f;
-        y[e] = fmaf(sv, y[e], sv * (ov - a.code_bias) * srow);
+        const float s = act_to_f32<BF16>(half(sv, e));
+        const float o = offset ? act_to_f32<BF16>(half(ov, e)) : 0.f;
+        y[e] = fmaf(s, y[e], s * (o - a.code_bias) * srow);
       }
     }
-    if (bias) {
-      const u32x2_t b = *(const u32x2_t*)(bias + col);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] += act_to_f32<BF16>((uint16_t)(b[e >> 1] >> (16 * (e & 1))));
-    }
-    if (x3) {
-      const u32x2_t x = *(const u32x2_t*)(x3 + idx);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] += act_to_f32<BF16>((uint16_t)(x[e >> 1] >> (16 * (e & 1))));
+    for (int e = 0; e < 4; ++e) {
+      if (bias) y[e] += act_to_f32<BF16>(half(bv, e));
+      if (x3) y[e] += act_to_f32<BF16>(half(xv, e));
     }
     *(u32x2_t*)(out + idx) = u32x2_t{(uint32_t)f32_to_act<BF16>(y[0]) | ((uint32_t)f32_to_act<BF16>(y[1]) << 16),
                                      (uint32_t)f32_to_act<BF16>(y[2]) | ((uint32_t)f32_to_act<BF16>(y[3]) << 16)};

@@ -337,21 +337,27 @@ __global__ __launch_bounds__(256) void qm_splitk_finish(const QmArgs a) {
     const int64_t row = q / (N / 4);
     const int col = 4 * (int)(q - row * (N / 4));
     const int64_t idx = row * N + col;
-    i32x4_t v = *(const i32x4_t*)(a.partial + idx);
-    for (int s = 1; s < a.splits; ++s) {
-      const i32x4_t p = *(const i32x4_t*)(a.partial + (int64_t)s * plane + idx);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (int32_t)((uint32_t)v[e] + (uint32_t)p[e]);
-    }
-    if (a.bias) {
-      const i32x4_t b = *(const i32x4_t*)(a.bias + col);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (int32_t)((uint32_t)v[e] + (uint32_t)b[e]);
-    }
-    if (a.acc_out) *(i32x4_t*)(a.acc_out + idx) = v;
+    // every operand is loaded ahead of its use; partials four splits at a time, at clamped
+    // split indices so that no load waits behind a branch
+    const i32x4_t b = a.bias ? *(const i32x4_t*)(a.bias + col) : i32x4_t{0, 0, 0, 0};
     const float pt = a.pt ? a.pt[row] : 1.f;
     u32x2_t xv{0u, 0u};
     if (x3) xv = *(const u32x2_t*)(x3 + idx);
+    i32x4_t v = *(const i32x4_t*)(a.partial + idx);
+    for (int s0 = 1; s0 < a.splits; s0 += 4) {
+      i32x4_t p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = *(const i32x4_t*)(a.partial + (int64_t)min(s0 + j, a.splits - 1) * plane + idx);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (s0 + j < a.splits) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (int32_t)((uint32_t)v[e] + (uint32_t)p[j][e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (int32_t)((uint32_t)v[e] + (uint32_t)b[e]);
+    if (a.acc_out) *(i32x4_t*)(a.acc_out + idx) = v;
     uint32_t o[2];
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {

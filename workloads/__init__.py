@@ -254,6 +254,15 @@ WORKLOADS = {
         kind="antiquant", seed=1007, act="bf16", weight="fp8e4m3", x1_shape=(32, 8192), n=8192,
         mode="channel", scale_dist=("uniform", 2e-4, 1e-3), with_offset=False,
         bias_dist=("normal", 0.0, 0.1), with_x3=False),
+    # a batch of 128 tokens on the fourth workload's weights (per-channel), and the W8A8
+    # sibling at the same shape: few output tiles, so k is split
+    "midm_perchannel_bf16_int8_128x8192x8192": dict(
+        kind="antiquant", seed=1008, act="bf16", weight="int8", x1_shape=(128, 8192), n=8192,
+        mode="channel", scale_dist=("uniform", 0.005, 0.02), offset_dist=("uniform", -2.0, 2.0),
+        bias_dist=("normal", 0.0, 0.1), x3_dist=("normal", 0.0, 0.1)),
+    "midm_w8a8_bf16_128x8192x8192": dict(
+        kind="w8a8", seed=1009, out="bf16", x1_shape=(128, 8192), n=8192, dequant="channel",
+        dequant_dtype="fp32"),
 }
 
 
