@@ -117,9 +117,12 @@ def cpu_baseline(case, name, budget_s=10.0, max_runs=20):
     """The oracle as it stands, on the host cores: the whole workload, repeated until about
     budget_s seconds of CPU work (at most max_runs runs); the rate is from the mean run."""
     import oracle
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([d.get("num_threads", 1) for d in info] or [1])
+        blas = [f"{d.get('internal_api')} {d.get('version')} ({d.get('num_threads')} threads)" for d in info]
     except Exception:  # threadpoolctl missing: report the visible cores
         threads = os.cpu_count() or 1
     times = []
@@ -137,7 +140,20 @@ def cpu_baseline(case, name, budget_s=10.0, max_runs=20):
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"the whole workload, {len(times)} runs ({sum(times):.1f} s of CPU work), fp64 NumPy/BLAS",
-            "seconds_per_run": round(dt, 3)}
+            "seconds_per_run": round(dt, 3),
+            "host": {"os_cpu_count": os.cpu_count(), "cpu_model": cpu_model(), "blas": blas}}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
 
 
 def traffic_for(kernel, name):
@@ -194,6 +210,8 @@ def bench_one(name, args, torch, dev):
     roof["kernel"] = kernel
     roof["launch_us_median"] = round(per[len(per) // 2] * 1e3, 2)
     roof["launch_us_avg"] = round(avg_launch_s * 1e6, 2)
+    roof["launch_us_min"] = round(per[0] * 1e3, 2)
+    roof["launch_us_max"] = round(per[-1] * 1e3, 2)
     value = flops / (ms_per_step / 1e3) / 1e12
     spec = workloads.WORKLOADS[name]
     line = {
@@ -214,7 +232,8 @@ def bench_one(name, args, torch, dev):
                    "x1_shape": list(case.x1.shape), "seed": spec["seed"],
                    "algorithmic_bytes": abytes, "flops": flops,
                    "hbm_gbps": round(abytes / (ms_per_step / 1e3) / 1e9, 1),
-                   "hbm_frac": round(abytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM, 4)},
+                   "hbm_frac": round(abytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM, 4),
+                   "inputs_sha256": workloads.digest(case)},
         "roofline": roof,
         "cpu_baseline": cpu_baseline(case, name) if args.cpu else None,
     }
