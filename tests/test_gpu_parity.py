@@ -282,7 +282,13 @@ def _antiquant_tensors(case):
                                               mode="group", group_size=128)),
     ("graph_largem_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(260, 256), n=320,
                                              mode="channel")),
-], ids=["graph_smallm_pergroup64_fp16_i8", "graph_largem_pergroup128_bf16_i4", "graph_largem_perchannel_bf16_i8"])
+    # split k: the finishing kernel is captured with the main kernel
+    ("graph_splitk_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(96, 2048), n=256,
+                                             mode="channel")),
+    ("graph_splitk_pergroup128_fp16_i4", dict(act="fp16", weight="int4", x1_shape=(64, 2048), n=256,
+                                              mode="group", group_size=128)),
+], ids=["graph_smallm_pergroup64_fp16_i8", "graph_largem_pergroup128_bf16_i4", "graph_largem_perchannel_bf16_i8",
+        "graph_splitk_perchannel_bf16_i8", "graph_splitk_pergroup128_fp16_i4"])
 def test_graph_replay_antiquant(name, spec):
     """A prepared call captured in a HIP graph and replayed on new inputs (copied into the
     captured buffers, with eager work and synchronisation between replays): every replay
@@ -316,13 +322,14 @@ def test_graph_replay_antiquant(name, spec):
         assert r["ok"], (case.name, r)
 
 
-def test_graph_replay_w8a8():
+@pytest.mark.parametrize("x1_shape,n", [((300, 256), 320), ((64, 2048), 256)], ids=["tiles", "splitk"])
+def test_graph_replay_w8a8(x1_shape, n):
     """The W8A8 prepared call captured and replayed on new inputs, checked like the
-    anti-quant graph test (the int32 accumulator bit-exact)."""
+    anti-quant graph test (the int32 accumulator bit-exact); the second shape splits k."""
     import torch
     import weight_quantized_gemm_amd as W
-    _announce("graph_w8a8")
-    cases = [workloads.make_w8a8(seed=950 + i, name=f"graph_w8a8_{i}", out="bf16", x1_shape=(300, 256), n=320)
+    _announce(f"graph_w8a8_{x1_shape}_{n}")
+    cases = [workloads.make_w8a8(seed=950 + i, name=f"graph_w8a8_{i}", out="bf16", x1_shape=x1_shape, n=n)
              for i in range(3)]
 
     def tensors(c):
