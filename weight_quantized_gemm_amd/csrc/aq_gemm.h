@@ -31,6 +31,12 @@
 // epilogue stages fp32 results through LDS so that x3, bias and the output move in
 // 16-byte row-contiguous accesses.
 //
+// Split k: when the output tiles alone would leave CUs idle, the grid's y index is a k
+// split; each split runs the same pipeline over its k range (whole groups, per-group) and
+// writes its fp32 tile (per-group: the folded total) and, per-tensor / per-channel, its
+// partial row sums; aq_splitk_finish adds the splits in split order and applies the
+// parameters, bias and x3.
+//
 // This header holds the kernel templates; aq_gemm_int8.hip, aq_gemm_int4.hip and
 // aq_gemm_fp8.hip instantiate them, one weight format per translation unit.
 #pragma once

@@ -18,7 +18,8 @@
 // (stored (n, k), which the Parameters table allows) travels exactly like x1: 64-byte rows
 // of k per column, 16-byte fragment loads, no transpose.  The epilogue
 // stages the accumulators through LDS so that x3, the output and the int32 accumulator
-// move in 16-byte row-contiguous accesses.
+// move in 16-byte row-contiguous accesses.  With few output tiles k is split (grid y):
+// the splits write int32 partial tiles and qm_splitk_finish adds them, in split order.
 #include <algorithm>
 
 #include "wq_kernels.h"
