@@ -28,22 +28,26 @@
 namespace wq {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBN = 256, kBK = 64;
 constexpr int kStages = 4;
 constexpr int kRA = kBK;                        // bytes per x1 row in a stage
 constexpr int kRB = kBN;                        // bytes per x2 row in a stage
-constexpr int kAbytes = kBM * kRA;              // 16 KiB
 constexpr int kBbytes = kBK * kRB;              // 16 KiB
-constexpr int kStage = kAbytes + kBbytes;
-constexpr int kLds = kStages * kStage;          // 128 KiB
-static_assert(kBM == kQmTileM && kBN == kQmTileN, "the planner's tile is the kernel's");
+static_assert(kBN == kQmTileN, "the planner's tile is the kernel's");
+// per workgroup-tile height BM (256, or 128 for m <= 128): x1 stage, stage, LDS
+template <int BM> constexpr int qm_abytes() { return BM * kRA; }          // 16 / 8 KiB
+template <int BM> constexpr int qm_stage() { return qm_abytes<BM>() + kBbytes; }
+template <int BM> constexpr int qm_lds() { return kStages * qm_stage<BM>(); }  // 128 / 96 KiB
 
-// Wave grid GM x GN with WM x WN 32x32 blocks per wave (256 x 256 per workgroup); XT: x2
+// Wave grid GM x GN with WM x WN 32x32 blocks per wave (BM x 256 per workgroup); XT: x2
 // stored transposed, (n, k).
-template <bool OUT_BF16, int kGM, int kGN, bool XT>
+template <bool OUT_BF16, int kGM, int kGN, bool XT, int BM = 256>
 __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs a) {
   constexpr int kWaves = kGM * kGN;
-  constexpr int kWM = 8 / kGM, kWN = 8 / kGN;
+  constexpr int kBM = BM;
+  constexpr int kAbytes = qm_abytes<BM>(), kStage = qm_stage<BM>();
+  constexpr int kWM = BM / 32 / kGM, kWN = 8 / kGN;
+  static_assert(kWM >= 1 && kWM * 32 * kGM == BM, "wave rows cover the tile");
   constexpr int kAper = kAbytes / 1024 / kWaves;  // DMA blocks per wave
   constexpr int kBper = kBbytes / 1024 / kWaves;
   constexpr int kDma = kAper + kBper;             // DMA loads per wave per stage
@@ -385,15 +389,23 @@ __global__ __launch_bounds__(256) void qm_splitk_finish(const QmArgs a) {
 
 hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   QmArgs a = a0;
-  a.tiles_m = (int)((a.m + kBM - 1) / kBM);
-  a.tiles_n = (a.n + kBN - 1) / kBN;
-  // default: 2 x 4 waves of 128 x 64 (two per SIMD); tuning tile 1: 2 x 2 waves of 128 x 128
-  // (row-major x2 only)
+  // default: 2 x 4 waves of 128 x 64 (two per SIMD), a 256 x 256 tile, or for m <= 128
+  // (qm_gemm_tile_m) 2 x 4 waves of 64 x 64, a 128 x 256 tile that computes fewer padding
+  // rows; tuning tile 1: 2 x 2 waves of 128 x 128 (row-major x2 only)
   const bool t1 = a.tile == 1 && !a.x2t;
-  auto kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, true> : qm_gemm_kernel<false, 2, 4, true>)
-              : t1  ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, false> : qm_gemm_kernel<false, 2, 2, false>)
-                    : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false> : qm_gemm_kernel<false, 2, 4, false>);
+  const int bm = t1 ? 256 : qm_gemm_tile_m(a.m);
+  a.tiles_m = (int)((a.m + bm - 1) / bm);
+  a.tiles_n = (a.n + kBN - 1) / kBN;
+  void (*kern)(const QmArgs);
+  if (bm == 128)
+    kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, true, 128> : qm_gemm_kernel<false, 2, 4, true, 128>)
+                 : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false, 128> : qm_gemm_kernel<false, 2, 4, false, 128>);
+  else
+    kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, true> : qm_gemm_kernel<false, 2, 4, true>)
+           : t1  ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, false> : qm_gemm_kernel<false, 2, 2, false>)
+                 : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false> : qm_gemm_kernel<false, 2, 4, false>);
   const int threads = t1 ? 256 : 512;
+  const int kLds = bm == 128 ? qm_lds<128>() : qm_lds<256>();
   hipError_t e = raise_lds_limit((const void*)kern, kLds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;

@@ -105,7 +105,8 @@ struct QmPlan {
 QmPlan plan_quant(const QuantProblem& p) {
   QmPlan pl;
   if (p.k == 0) return pl;
-  const int64_t tiles = (p.m + kQmTileM - 1) / kQmTileM * ((p.n + kQmTileN - 1) / kQmTileN);
+  const int bm = qm_gemm_tile_m(p.m);
+  const int64_t tiles = (p.m + bm - 1) / bm * ((p.n + kQmTileN - 1) / kQmTileN);
   pl.split = gemm_split_plan(tiles, (int)p.k, 64);
   if (pl.split.splits > 1) pl.workspace = align_up((int64_t)pl.split.splits * p.m * p.n * (int64_t)sizeof(int32_t));
   return pl;

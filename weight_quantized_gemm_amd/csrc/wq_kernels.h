@@ -88,6 +88,8 @@ SplitPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped);
 int aq_gemm_tile_m(int64_t m, bool grouped);
 constexpr int kAqTileN = 256;
 SplitPlan gemm_split_plan(int64_t tiles, int k, int unit);
-constexpr int kQmTileM = 256, kQmTileN = 256;
+// W8A8: the workgroup tile of the default configuration (rows 128 for m <= 128, else 256)
+inline int qm_gemm_tile_m(int64_t m) { return m <= 128 ? 128 : 256; }
+constexpr int kQmTileN = 256;
 
 }  // namespace wq
