@@ -91,7 +91,7 @@ struct Tile {
   static constexpr int SOff = Stages * Stage;
   static constexpr int Total = SOff + BM * 4;
   static_assert(Stages >= 3, "at least three stages");
-  static_assert(BM == 128 || BM == 256, "x1 stage holds 128 or 256 rows");
+  static_assert(BM == 64 || BM == 128 || BM == 256, "x1 stage holds 64, 128 or 256 rows");
   static_assert(Ablocks % Waves == 0, "x1 DMA blocks split evenly over the waves");
   static_assert(Bblocks % Waves == 0 || Bblocks < Waves, "weight DMA blocks split");
   static_assert(Win >= 1 && Win <= 4, "weight row bytes 64..256");
@@ -284,12 +284,15 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       const u32x4_t rsa = make_rsrc32(gsum + (int64_t)ga * M + m0, rows_bytes);
       const u32x4_t rsb = make_rsrc32(gsum + (int64_t)gb * M + m0, rows_bytes);
       uint8_t* sd = pd + T::Pbytes;
-      if constexpr (T::BM == 128) {  // 512 bytes a row: one half-wave load each
+      if constexpr (T::BM == 64) {  // 256 bytes a row: a quarter-wave load each
+        if (lane < 16) dma16(rsa, sd, 16u * (uint32_t)lane);
+        else if (lane < 32) dma16(rsb, sd, 16u * (uint32_t)(lane - 16));  // lands at sd + 256
+      } else if constexpr (T::BM == 128) {  // 512 bytes a row: one half-wave load each
         const uint32_t off = 16u * (uint32_t)(lane & 31);
         if (lane < 32) dma16(rsa, sd, off);
         else dma16(rsb, sd, off);  // lands at sd + 512 + 16 (lane - 32)
       } else {                       // 1 KiB a row: one full-wave load each
-        static_assert(T::BM == 256, "x1 tiles of 128 or 256 rows");
+        static_assert(T::BM == 256, "x1 tiles of 64, 128 or 256 rows");
         dma16(rsa, sd, 16u * (uint32_t)lane);
         dma16(rsb, sd + 1024, 16u * (uint32_t)lane);
       }
@@ -631,16 +634,23 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
 //                             2: 4x2 of 64x128
 //   per-group:                0: 2x4 waves of 64x64 (128x256)   1: 4x2 of 64x64 (256x128)
 //                             2: 8x1 of 32x64 (int8)
+// Index 0 at short m: 2x4 waves of 32x64 (64x256) for m <= 64, and per-tensor /
+// per-channel 2x4 waves of 64x64 (128x256) for m <= 128.
 template <bool BF16, int WF>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   constexpr bool W4 = WF == kWInt4;
-  // per-tensor / per-channel with m <= 128: the 2x4 waves of 64x64 (128x256), so that a
-  // short m computes fewer padding rows (aq_gemm_tile_m gives the planner the same choice)
-  const bool short_m = a.m <= 128;
+  // Short m computes fewer padding rows on shorter tiles (aq_gemm_tile_m gives the planner
+  // the same choice): m <= 64 takes 2x4 waves of 32x64 (64x256) in every mode, and
+  // per-tensor / per-channel with m <= 128 the 2x4 waves of 64x64 (128x256).
+  const bool tiny_m = a.m <= 64, short_m = a.m <= 128;
   if (a.x2t) {  // transposed weights: the default tile of each mode
     if constexpr (WF != kWFp8) {
-      if (a.grouped) return launch_one<BF16, WF, 2, 4, 2, 2, true, true>(a, stream);
+      if (a.grouped) {
+        if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true, true>(a, stream);
+        return launch_one<BF16, WF, 2, 4, 2, 2, true, true>(a, stream);
+      }
     }
+    if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, false, true>(a, stream);
     if (short_m) return launch_one<BF16, WF, 2, 4, 2, 2, false, true>(a, stream);
     return launch_one<BF16, WF, 2, 4, 4, 2, false, true>(a, stream);
   }
@@ -651,7 +661,9 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
         case 2:
           if constexpr (!W4) return launch_one<BF16, WF, 8, 1, 1, 2, true>(a, stream);
           else return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
-        default: return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
+        default:
+          if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true>(a, stream);
+          return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
       }
     }
   }
@@ -661,6 +673,7 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
       else return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
     case 2: return launch_one<BF16, WF, 4, 2, 2, 4, false>(a, stream);
     default:
+      if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, false>(a, stream);
       if (short_m) return launch_one<BF16, WF, 2, 4, 2, 2, false>(a, stream);
       return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
   }

@@ -17,9 +17,13 @@
 
 namespace wq {
 
-// Workgroup tile rows of the tiled kernel's default configurations (see aq_gemm.h): 128 for
-// per-group, and for per-tensor / per-channel while m fits one such tile; 256 otherwise.
-int aq_gemm_tile_m(int64_t m, bool grouped) { return (grouped || m <= 128) ? 128 : 256; }
+// Workgroup tile rows of the tiled kernel's default configurations (see aq_gemm.h): 64 for
+// m <= 64; 128 for per-group, and for per-tensor / per-channel while m fits one such tile;
+// 256 otherwise.
+int aq_gemm_tile_m(int64_t m, bool grouped) {
+  if (m <= 64) return 64;
+  return (grouped || m <= 128) ? 128 : 256;
+}
 
 // Split k when the tiles alone would leave CUs idle: as many splits as bring the workgroups
 // (one per CU: each takes most of a CU's LDS) up to at most the CU count of an MI355X, each
