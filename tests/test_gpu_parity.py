@@ -114,6 +114,16 @@ AQ_CASES = [
                                                    mode="group", group_size=64, x2_transposed=True)),
     ("midm_xt_m96_perchannel_fp16_i4_splitk", dict(act="fp16", weight="int4", x1_shape=(96, 2048), n=384,
                                                    mode="channel", x2_transposed=True)),
+    # m <= 64: the 64-row tile (per-group row sums as quarter-wave loads)
+    ("midm_m40_pergroup96_bf16_i8_xt_splitk", dict(act="bf16", weight="int8", x1_shape=(40, 2304), n=320,
+                                                   mode="group", group_size=96, x2_transposed=True)),
+    ("midm_m50_pertensor_fp16_i8_splitk", dict(act="fp16", weight="int8", x1_shape=(50, 1600), n=224,
+                                               mode="tensor", with_x3=False)),
+    ("midm_m64_pergroup64_fp16_i4_splitk", dict(act="fp16", weight="int4", x1_shape=(2, 32, 2048), n=256,
+                                                mode="group", group_size=64, with_bias=False)),
+    ("midm_m57_perchannel_bf16_f8_nosplit", dict(act="bf16", weight="fp8e4m3", x1_shape=(57, 256), n=96,
+                                                 mode="channel", with_offset=False,
+                                                 scale_dist=("uniform", 2e-4, 1e-3))),
     # x2 stored transposed, (n, k) (int4 packed along k), handed over as its (k, n) transpose
     # view; per-group scale and offset transposed with it
     ("xt_perchannel_bf16_i8_ragged", dict(act="bf16", weight="int8", x1_shape=(600, 288), n=544, mode="channel",
