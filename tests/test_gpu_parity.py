@@ -436,7 +436,7 @@ def test_full_size_sampled(name):
 
 
 # ---------------------------------------------------------------- seeded sweep
-def _sweep_antiquant(count=48, seed=4242):
+def _sweep_antiquant(count=48, seed=4242, ms=(1, 2, 7, 31, 32, 33, 65, 100, 257, 300), kmax=24, prefix="sw"):
     """Random combinations of dtype, weight format, mode, layout, optional inputs and ragged
     shapes (small-m and tiled paths), each drawn from a fixed seed."""
     rng = np.random.default_rng(seed)
@@ -445,9 +445,9 @@ def _sweep_antiquant(count=48, seed=4242):
         act = str(rng.choice(["fp16", "bf16"]))
         weight = str(rng.choice(["int8", "int4", "fp8e4m3"], p=[0.45, 0.35, 0.2]))
         align = 64 if weight == "int4" else 32
-        k = int(align * rng.integers(1, 25))
+        k = int(align * rng.integers(1, kmax + 1))
         n = int(align * rng.integers(1, 13))
-        m = int(rng.choice([1, 2, 7, 31, 32, 33, 65, 100, 257, 300]))
+        m = int(rng.choice(list(ms)))
         mode = "channel" if weight == "fp8e4m3" else str(rng.choice(["tensor", "channel", "group"]))
         g = 0
         if mode == "group":
@@ -465,13 +465,16 @@ def _sweep_antiquant(count=48, seed=4242):
                     channel_2d=bool(rng.random() < 0.3), x2_transposed=bool(rng.random() < 0.3))
         if weight == "fp8e4m3":
             spec["scale_dist"] = ("uniform", 2e-4, 1e-3)
-        name = (f"sw{i}_{act}_{weight}_{mode}{g or ''}_m{m}k{k}n{n}"
+        name = (f"{prefix}{i}_{act}_{weight}_{mode}{g or ''}_m{m}k{k}n{n}"
                 f"{'_xt' if spec['x2_transposed'] else ''}")
         out.append((name, spec))
     return out
 
 
 SWEEP = _sweep_antiquant()
+# m from 33 to 200 with k up to 96 blocks of 32 (64 for int4): most of these split k, on
+# the 64-, 128- and 256-row tiles
+SWEEP += _sweep_antiquant(count=32, seed=4747, ms=(33, 47, 64, 65, 96, 128, 129, 200), kmax=96, prefix="swk")
 
 
 @pytest.mark.parametrize("name,spec", SWEEP, ids=[c[0] for c in SWEEP])
