@@ -27,9 +27,14 @@ __global__ __launch_bounds__(256) void bias_x3_kernel(const uint16_t* __restrict
 }
 
 // dst (rows, cols) = transpose of src (cols, rows), 16-bit elements, through a 64 x 64 LDS
-// tile (rows = groups, cols = n): reads and writes move along the contiguous axis.
-__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ src,
-                                                          uint16_t* __restrict__ dst, int rows, int cols) {
+// tile (rows = groups, cols = n): reads and writes move along the contiguous axis.  Grid z
+// picks one of two tensors (scale, then offset), so both are copied by one launch.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ src0,
+                                                          uint16_t* __restrict__ dst0,
+                                                          const uint16_t* __restrict__ src1,
+                                                          uint16_t* __restrict__ dst1, int rows, int cols) {
+  const uint16_t* __restrict__ src = blockIdx.z ? src1 : src0;
+  uint16_t* __restrict__ dst = blockIdx.z ? dst1 : dst0;
   __shared__ uint16_t tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -105,10 +110,11 @@ hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_transpose16(const void* src, void* dst, int rows, int cols, hipStream_t stream) {
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
-  hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, (const uint16_t*)src, (uint16_t*)dst,
-                     rows, cols);
+hipError_t launch_transpose16(const void* src0, void* dst0, const void* src1, void* dst1, int rows,
+                              int cols, hipStream_t stream) {
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64), src1 ? 2u : 1u);
+  hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, (const uint16_t*)src0, (uint16_t*)dst0,
+                     (const uint16_t*)src1, (uint16_t*)dst1, rows, cols);
   return hipGetLastError();
 }
 

@@ -202,14 +202,13 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   hipError_t e;
   if (pl.param_bytes) {
     // transposed per-group parameters (n, groups) -> row-major (groups, n) copies
+    // (scale and offset in one launch)
     char* pb = (char*)workspace + pl.partial_bytes + pl.rowsum_bytes;
-    if ((e = wq::launch_transpose16(p.scale, pb, (int)p.groups, (int)p.n, s)) != hipSuccess) return WQ_ERR_RUNTIME;
+    char* po = p.offset ? pb + pl.param_bytes : nullptr;
+    if ((e = wq::launch_transpose16(p.scale, pb, p.offset, po, (int)p.groups, (int)p.n, s)) != hipSuccess)
+      return WQ_ERR_RUNTIME;
     a.scale = pb;
-    if (p.offset) {
-      if ((e = wq::launch_transpose16(p.offset, pb + pl.param_bytes, (int)p.groups, (int)p.n, s)) != hipSuccess)
-        return WQ_ERR_RUNTIME;
-      a.offset = pb + pl.param_bytes;
-    }
+    if (p.offset) a.offset = po;
   }
   if (pl.empty_k) {
     e = wq::launch_aq_bias_x3(a, s);

@@ -73,8 +73,10 @@ hipError_t launch_aq_splitk_finish(const AqArgs& a, hipStream_t stream);
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream);  // k == 0
 // large m, per-group: a.gsum[g][r] = sum of x1[r, k] over the k of group g (fp32, fixed order)
 hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream);
-// dst (rows, cols) = transpose of src (cols, rows), 16-bit elements
-hipError_t launch_transpose16(const void* src, void* dst, int rows, int cols, hipStream_t stream);
+// dst0 (rows, cols) = transpose of src0 (cols, rows), 16-bit elements, and the same for
+// src1 / dst1 in the same launch unless src1 is null
+hipError_t launch_transpose16(const void* src0, void* dst0, const void* src1, void* dst1, int rows,
+                              int cols, hipStream_t stream);
 hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);
 
 // Split-k plans, shared by the planners (workspace sizes) and the launches.
