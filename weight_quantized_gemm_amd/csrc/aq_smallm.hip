@@ -175,8 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
         for (int e = 0; e < 4; ++e)
           tot[j][4 * rq + e] = fmaf(s[j], acc[j][4 * rq + e], fmaf(q[j], sr[e], tot[j][4 * rq + e]));
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x16_t{};
+    // acc is not cleared: the next MFMA of each column block starts from a zero operand
   };
 
   // ------------------------------------------------------------------ stream
@@ -236,19 +235,29 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
     const int k0 = block_k0(t);
 #pragma unroll
     for (int kk = 0; kk < kRows / 16; ++kk) {
+      // zero: start each column block's accumulator from a zero operand
+      auto step = [&](bool zero) {
 #pragma unroll
-      for (int p = 0; p < kP; ++p) {
-        if constexpr (W4 && XT) {
-          acc[p] = mfma32x32x16<BF16>(af[kk], i4x8_k_to_act<BF16>(braw[kk][p][0]), acc[p]);
-        } else if constexpr (W4) {
-          u32x4_t ev, od;
-          i4_kpairs<BF16>(braw[kk][p], ev, od);
-          acc[2 * p] = mfma32x32x16<BF16>(af[kk], ev, acc[2 * p]);
-          acc[2 * p + 1] = mfma32x32x16<BF16>(af[kk], od, acc[2 * p + 1]);
-        } else {
-          acc[p] = mfma32x32x16<BF16>(af[kk], w8x8_to_act<BF16, WF>(braw[kk][p]), acc[p]);
+        for (int p = 0; p < kP; ++p) {
+          if constexpr (W4 && XT) {
+            acc[p] = mfma32x32x16<BF16>(af[kk], i4x8_k_to_act<BF16>(braw[kk][p][0]), zero ? f32x16_t{} : acc[p]);
+          } else if constexpr (W4) {
+            u32x4_t ev, od;
+            i4_kpairs<BF16>(braw[kk][p], ev, od);
+            acc[2 * p] = mfma32x32x16<BF16>(af[kk], ev, zero ? f32x16_t{} : acc[2 * p]);
+            acc[2 * p + 1] = mfma32x32x16<BF16>(af[kk], od, zero ? f32x16_t{} : acc[2 * p + 1]);
+          } else {
+            acc[p] = mfma32x32x16<BF16>(af[kk], w8x8_to_act<BF16, WF>(braw[kk][p]), zero ? f32x16_t{} : acc[p]);
+          }
         }
-      }
+      };
+      // Per-group: a fold leaves the accumulators spent, so the MFMAs after one start from
+      // zero: at kk = 0 always (a block ends in a fold, and the first starts from zero), at
+      // kk = 2 after a fold at kk = 1.  The condition is uniform: one of two code paths runs.
+      bool fresh = false;
+      if constexpr (GROUPED) fresh = kk == 0 || (kk == 2 && ((k0 + 32) % a.group == 0 || k0 + 32 >= kend));
+      if (fresh) step(true);
+      else step(false);
 #pragma unroll
       for (int q = 0; q < 4; ++q) ssum = dot2_ones<BF16>(af[kk][q], ssum);
       if constexpr (GROUPED) {
