@@ -367,6 +367,42 @@ def test_graph_replay_w8a8(x1_shape, n):
         assert r["ok"], (c.name, r)
 
 
+@pytest.mark.parametrize("name,spec", [
+    ("stream_splitk_pergroup128_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(200, 2048), n=256, mode="group",
+                                               group_size=128)),
+    ("stream_smallm_perchannel_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(16, 4096), n=512,
+                                              mode="channel")),
+], ids=["stream_splitk_pergroup128_bf16_i4", "stream_smallm_perchannel_fp16_i8"])
+def test_side_stream(name, spec):
+    """Calls enqueued on a non-default stream (default priority, created by torch) run every
+    kernel they launch -- row-sum pass, main kernel, split-k finish -- on that stream: read
+    after synchronising only that stream, the results equal calls on the default stream
+    bit for bit (anti-quant, then a split W8A8 call)."""
+    import torch
+    import weight_quantized_gemm_amd as W
+    _announce(name)
+    case = workloads.make_antiquant(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec)
+    t = _antiquant_tensors(case)
+    int4 = spec["weight"] == "int4"
+    args = (t["x1"], t["x2"], t["scale"], t["offset"], t["bias"], t["x3"], case.group_size)
+    ref = W.AntiquantMatmul(*args, x2_int4=int4)()
+    side_call = W.AntiquantMatmul(*args, x2_int4=int4)
+    q = workloads.make_w8a8(seed=77, name="stream_w8a8", out="bf16", x1_shape=(64, 2048), n=256)
+    qa = (dev_tensor(q.x1, "raw"), dev_tensor(q.x2, "raw"), dev_tensor(q.dequant_scale, q.dequant_dtype),
+          dev_tensor(q.pertoken_scale, "fp32"), dev_tensor(q.bias, "raw"), dev_tensor(q.x3, q.out))
+    qref = W.QuantMatmul(*qa)()
+    q_side = W.QuantMatmul(*qa)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side_call(stream=side)
+    q_side(stream=side)
+    side.synchronize()
+    assert torch.equal(side_call.out.view(torch.int16), ref.view(torch.int16)), name
+    assert torch.equal(q_side.out.view(torch.int16), qref.view(torch.int16))
+    r = oracle.compare(to_f64(side_call.out).reshape(case.out_shape), ref_antiquant(case), case.act)
+    assert r["ok"], (name, r)
+
+
 W8A8_CASES = [
     ("w8a8_ragged_bf16", dict(out="bf16", x1_shape=(600, 288), n=544)),
     ("w8a8_fp16_tensor_nopt", dict(out="fp16", x1_shape=(300, 256), n=256, dequant="tensor",
