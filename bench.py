@@ -10,9 +10,9 @@ timed steps read their operands from HBM, not from a warm cache.
 
 Each input set gets a prepared call (descriptors and workspace settled once), so the host
 enqueues steps faster than the device runs them.  The timed region covers exactly the
-timed steps, bracketed by device synchronisation; inside it, the library's profiling hook
-records a pair of HIP events on the launch stream around each step's main kernel, which
-gives that kernel's average launch duration for the roofline.
+timed steps, bracketed by device synchronisation.  As many steps again follow it, each with
+the library's profiling hook recording a pair of HIP events on the launch stream around the
+step's main kernel, which gives that kernel's average launch duration for the roofline.
 
 Output: one JSON line (the headline workload), with the roofline of the dominant kernel
 and the CPU oracle's rate on the host as a baseline.  ``--all`` prints one line per
@@ -187,10 +187,16 @@ def bench_one(name, args, torch, dev):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        W.profile_next_call(*evs[i])
         calls[(args.warmup + i) % sets](sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Kernel durations: as many steps again, each with the profiling hook's two events around
+    # its main kernel.  They run outside the timed region because the event records are
+    # work of their own on the stream.
+    for i in range(args.steps):
+        W.profile_next_call(*evs[i])
+        calls[(args.warmup + args.steps + i) % sets](sh)
+    torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in evs)          # ms, main kernel per step
     ev_total = sum(per)
     ms_per_step = wall * 1e3 / args.steps
