@@ -458,8 +458,9 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
         else bfr[j] = w8x8_to_act<BF16, WF>(cur.raw[j]);
       }
       // Per-group: a group's first 16-k step (group starts fall on multiples of 32, so on
-      // steps 0 and 2; k is counted from the split's start, a group boundary) starts its accumulators from zero through the MFMA's own operand
-      // instead of clearing them after the previous group's fold.
+      // steps 0 and 2; k is counted from the split's start, a group boundary) starts its
+      // accumulators from zero through the MFMA's own operand instead of clearing them
+      // after the previous group's fold.
       bool fresh = false;
       if constexpr (GROUPED) {
         if (kk % 2 == 0) fresh = (ks * kBK + kk * 16) % a.group == 0;
