@@ -49,30 +49,34 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __rest
   }
 }
 
-// S[g][r] = sum of x1[r, k] over group g's k, fp32, in a fixed order.  A wave takes one row
-// at a time: lane l sums x1[r, 512 w + 8 l .. + 7] (v_dot2 against ones), four lanes add up
-// a 32-k piece, and the row's pieces land in the wave's LDS strip; then lane j adds up the
-// pieces of groups j, j + 64, ... in k order (groups are multiples of 32 long, k too).  The
-// pass streams x1 (128 MiB at m = k = 8192), so each lane keeps four 16-byte loads in
-// flight: the row is read 2048 k at a time.
+// S[g][r] = sum of x1[r, k] over group g's k, fp32, in a fixed order.  The work items are
+// (row, chunk) pairs, a chunk being gpc whole groups (about 2048 k), so that short m still
+// spreads over many waves.  A wave takes one item at a time: lane l sums x1[r, kb + 512 w +
+// 8 l .. + 7] (v_dot2 against ones), four lanes add up a 32-k piece, and the chunk's pieces
+// land in the wave's LDS strip; then lane j adds up the pieces of the chunk's group j in k
+// order (groups are multiples of 32 long, k too).  Each lane keeps four 16-byte loads in
+// flight: the chunk is read 2048 k at a time.
 template <bool BF16>
 __global__ __launch_bounds__(256) void group_rowsums_kernel(const uint16_t* __restrict__ x1,
                                                             float* __restrict__ S, int64_t m, int k,
-                                                            int g, int groups) {
-  // each wave's strip holds its row's k / 32 pieces (dynamic LDS: 4 strips of np floats),
-  // so that short rows leave room for more workgroups per CU
+                                                            int g, int groups, int gpc, int nchunks) {
+  // each wave's strip holds one chunk's pieces (dynamic LDS: 4 strips of np floats)
   extern __shared__ float pieces[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int np = k / 32, per = g / 32;
+  const int per = g / 32, np = gpc * per;
   float* piece = pieces + wave * np;
-  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < m; r += (int64_t)gridDim.x * 4) {
+  const int64_t items = m * nchunks;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < items; it += (int64_t)gridDim.x * 4) {
+    const int64_t r = it / nchunks;
+    const int c = (int)(it - r * nchunks);
+    const int kb = c * gpc * g, ke = min(k, kb + gpc * g);
     const uint16_t* row = x1 + r * k;
-    for (int w0 = 0; w0 < k; w0 += 2048) {
+    for (int w0 = kb; w0 < ke; w0 += 2048) {
       u32x4_t d[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int kk = w0 + 512 * u + 8 * lane;
-        d[u] = kk < k ? *(const u32x4_t*)(row + kk) : u32x4_t{0u, 0u, 0u, 0u};
+        d[u] = kk < ke ? *(const u32x4_t*)(row + kk) : u32x4_t{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -82,31 +86,39 @@ __global__ __launch_bounds__(256) void group_rowsums_kernel(const uint16_t* __re
         for (int q = 0; q < 4; ++q) v = dot2_ones<BF16>(d[u][q], v);
         v += __shfl_xor(v, 1, 64);
         v += __shfl_xor(v, 2, 64);
-        if ((lane & 3) == 0 && kk < k) piece[kk / 32] = v;
+        if ((lane & 3) == 0 && kk < ke) piece[(kk - kb) / 32] = v;
       }
     }
     __builtin_amdgcn_wave_barrier();  // the strip is written (one wave: LDS in order)
-    for (int gi = lane; gi < groups; gi += 64) {
-      const int p1 = min(np, (gi + 1) * per);
+    const int nloc = (ke - kb) / 32;  // pieces in this chunk
+    for (int j = lane; j < gpc; j += 64) {
+      const int gi = c * gpc + j;
+      if (gi >= groups) break;
+      const int p1 = min(nloc, (j + 1) * per);
       float t = 0.f;
-      for (int p = gi * per; p < p1; ++p) t += piece[p];
+      for (int p = j * per; p < p1; ++p) t += piece[p];
       S[(int64_t)gi * m + r] = t;
     }
-    __builtin_amdgcn_wave_barrier();  // read before the next row overwrites it
+    __builtin_amdgcn_wave_barrier();  // read before the next item overwrites it
   }
 }
 
 }  // namespace
 
 hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream) {
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((a.m + 3) / 4, 16384));
-  const size_t lds = (size_t)4 * (size_t)(a.k / 32) * sizeof(float);  // <= 32 KiB (k <= 65535)
+  // chunks of gpc whole groups, about 2048 k (one group when groups are longer)
+  const int gpc = std::max(1, 2048 / a.group);
+  const int nchunks = (a.groups + gpc - 1) / gpc;
+  const int64_t items = a.m * nchunks;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((items + 3) / 4, 16384));
+  // 4 strips of a chunk's pieces: <= 4 x 2047 floats (a group is shorter than k <= 65535)
+  const size_t lds = (size_t)4 * (size_t)(gpc * (a.group / 32)) * sizeof(float);
   if (a.bf16)
     hipLaunchKernelGGL(group_rowsums_kernel<true>, dim3((unsigned)blocks), dim3(256), lds, stream,
-                       (const uint16_t*)a.x1, a.gsum, a.m, a.k, a.group, a.groups);
+                       (const uint16_t*)a.x1, a.gsum, a.m, a.k, a.group, a.groups, gpc, nchunks);
   else
     hipLaunchKernelGGL(group_rowsums_kernel<false>, dim3((unsigned)blocks), dim3(256), lds, stream,
-                       (const uint16_t*)a.x1, a.gsum, a.m, a.k, a.group, a.groups);
+                       (const uint16_t*)a.x1, a.gsum, a.m, a.k, a.group, a.groups, gpc, nchunks);
   return hipGetLastError();
 }
 
