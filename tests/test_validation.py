@@ -261,26 +261,26 @@ def test_workspace_sizes(wqlib):
                                                         r(out), r(size)) == OK
     assert size.value == 0
     # ... else fp32 split-k partials and row sums: 2 x 1 tiles of 256 rows want 128 splits,
-    # but a split keeps at least 512 k, so k = 1024 gives 2 splits
+    # but a split keeps at least 256 k, so k = 1024 gives 4 splits
     x1, x2, sc, out = base(m=300, k=1024, n=256)
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                         r(out), r(size)) == OK
-    assert size.value == 2 * 300 * 256 * 4 + 2560          # partials, then row sums padded to 256
+    assert size.value == 4 * 300 * 256 * 4 + 4864          # partials, then row sums padded to 256
     # per-group splits hold whole groups: g = 96 gives units of 192 and splits of at least
-    # 576; 3 tiles of 128 rows want 85 splits, k = 2304 takes 4; then the row sums per group
+    # 384; 3 tiles of 128 rows want 85 splits, k = 2304 takes 6; then the row sums per group
     x1, x2, sc, out = base(m=300, k=2304, n=256, scale=[24, 256])
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 96,
                                                         r(out), r(size)) == OK
-    assert size.value == 4 * 300 * 256 * 4 + 28928          # partials, (24, 300) fp32 padded
-    # m <= 64 counts tiles of 64 rows: one tile, k = 1024 split in two
+    assert size.value == 6 * 300 * 256 * 4 + 28928          # partials, (24, 300) fp32 padded
+    # m <= 64 counts tiles of 64 rows: one tile, k = 1024 split in four
     x1, x2, sc, out = base(m=64, k=1024, n=256)
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                         r(out), r(size)) == OK
-    assert size.value == 2 * 64 * 256 * 4 + 512
+    assert size.value == 4 * 64 * 256 * 4 + 1024
     # W8A8: int32 partials under the same rule (tiles of 256 x 256, 128 x 256 for m <= 128)
     i8 = W.WQ_I8
     for (m, k, n), want in (((4096, 4096, 4096), 0), ((32, 8192, 8192), 8 * 32 * 8192 * 4),
-                            ((300, 1024, 256), 2 * 300 * 256 * 4)):
+                            ((300, 1024, 256), 4 * 300 * 256 * 4)):
         assert wqlib.wq_quant_matmul_get_workspace_size(
             r(D([m, k], i8)), r(D([k, n], i8)), None, None, r(D([n], W.WQ_F32)), None,
             r(D([m, n], W.WQ_BF16)), None, r(size)) == OK

@@ -27,7 +27,7 @@ int aq_gemm_tile_m(int64_t m, bool grouped) {
 
 // Split k when the tiles alone would leave CUs idle: as many splits as bring the workgroups
 // (one per CU: each takes most of a CU's LDS) up to at most the CU count of an MI355X, each
-// at least 512 k long (the pipeline fill amortises), in whole units of k.
+// at least 256 k long (4 k-steps; 512 was up to 20% slower on short k), in whole units of k.
 SplitPlan gemm_split_plan(int64_t tiles, int k, int unit) {
   constexpr int64_t kCUs = 256;
   SplitPlan p;
@@ -35,7 +35,7 @@ SplitPlan gemm_split_plan(int64_t tiles, int k, int unit) {
   p.splits = 1;
   const int64_t want = kCUs / std::max<int64_t>(1, tiles);
   if (want < 2) return p;
-  const int min_chunk = (512 + unit - 1) / unit * unit;
+  const int min_chunk = (256 + unit - 1) / unit * unit;
   int per = (int)((k + want - 1) / want);
   per = std::max(min_chunk, (per + unit - 1) / unit * unit);
   const int splits = (k + per - 1) / per;
