@@ -124,6 +124,19 @@ AQ_CASES = [
     ("midm_m57_perchannel_bf16_f8_nosplit", dict(act="bf16", weight="fp8e4m3", x1_shape=(57, 256), n=96,
                                                  mode="channel", with_offset=False,
                                                  scale_dist=("uniform", 2e-4, 1e-3))),
+    # m > 128 whose 256-row tiles would split k into chunks of at most 512: several 128-row
+    # tiles (ragged last row tile), per-tensor / per-channel, every weight type, both x2 layouts
+    ("midm_m160_perchannel_bf16_i8_rows128", dict(act="bf16", weight="int8", x1_shape=(160, 2048), n=512,
+                                                  mode="channel")),
+    ("midm_m256_pertensor_fp16_i4_rows128", dict(act="fp16", weight="int4", x1_shape=(4, 64, 1024), n=768,
+                                                 mode="tensor")),
+    ("midm_m333_perchannel_bf16_f8_rows128", dict(act="bf16", weight="fp8e4m3", x1_shape=(333, 1536), n=320,
+                                                  mode="channel", with_offset=False,
+                                                  scale_dist=("uniform", 2e-4, 1e-3))),
+    ("midm_xt_m390_perchannel_fp16_i8_rows128", dict(act="fp16", weight="int8", x1_shape=(390, 1024), n=640,
+                                                     mode="channel", x2_transposed=True, with_bias=False)),
+    ("midm_xt_m201_pertensor_bf16_i4_rows128", dict(act="bf16", weight="int4", x1_shape=(201, 4096), n=256,
+                                                    mode="tensor", x2_transposed=True)),
     # x2 stored transposed, (n, k) (int4 packed along k), handed over as its (k, n) transpose
     # view; per-group scale and offset transposed with it
     ("xt_perchannel_bf16_i8_ragged", dict(act="bf16", weight="int8", x1_shape=(600, 288), n=544, mode="channel",
@@ -422,6 +435,9 @@ W8A8_CASES = [
     ("w8a8_splitk_m64", dict(out="bf16", x1_shape=(64, 4096), n=512)),
     ("w8a8_splitk_m300_tail_xt", dict(out="fp16", x1_shape=(300, 2080), n=320, x2_transposed=True)),
     ("w8a8_splitk_m7_tensor", dict(out="bf16", x1_shape=(7, 3072), n=96, dequant="tensor", with_pertoken=False)),
+    # m > 128 with 256-row tiles that would split k into chunks of at most 512: 128-row tiles
+    ("w8a8_rows128_m200_3d", dict(out="bf16", x1_shape=(2, 100, 2048), n=768)),
+    ("w8a8_rows128_m256_xt", dict(out="fp16", x1_shape=(256, 1536), n=512, x2_transposed=True)),
 ]
 
 

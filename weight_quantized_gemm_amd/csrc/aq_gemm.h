@@ -635,15 +635,16 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
 //                             2: 4x2 of 64x128
 //   per-group:                0: 2x4 waves of 64x64 (128x256)   1: 4x2 of 64x64 (256x128)
 //                             2: 8x1 of 32x64 (int8)
-// Index 0 at short m: 2x4 waves of 32x64 (64x256) for m <= 64, and per-tensor /
-// per-channel 2x4 waves of 64x64 (128x256) for m <= 128.
+// Index 0 with the planner's shorter tiles: 2x4 waves of 32x64 (64x256) at 64 rows, and
+// per-tensor / per-channel 2x4 waves of 64x64 (128x256) at 128 rows.
 template <bool BF16, int WF>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   constexpr bool W4 = WF == kWInt4;
-  // Short m computes fewer padding rows on shorter tiles (aq_gemm_tile_m gives the planner
-  // the same choice): m <= 64 takes 2x4 waves of 32x64 (64x256) in every mode, and
-  // per-tensor / per-channel with m <= 128 the 2x4 waves of 64x64 (128x256).
-  const bool tiny_m = a.m <= 64, short_m = a.m <= 128;
+  // Short m computes fewer padding rows on shorter tiles, and short split chunks run on more
+  // workgroups; the planner's tile rows (aq_gemm_tile_m) select them: 64 rows take 2x4 waves
+  // of 32x64 (64x256) in every mode, and 128 rows per-tensor / per-channel the 2x4 waves of
+  // 64x64 (128x256).
+  const bool tiny_m = a.bm == 64, short_m = a.bm == 128;
   if (a.x2t) {  // transposed weights: the default tile of each mode
     if constexpr (WF != kWFp8) {
       if (a.grouped) {

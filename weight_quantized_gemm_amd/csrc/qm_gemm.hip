@@ -389,11 +389,11 @@ __global__ __launch_bounds__(256) void qm_splitk_finish(const QmArgs a) {
 
 hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   QmArgs a = a0;
-  // default: 2 x 4 waves of 128 x 64 (two per SIMD), a 256 x 256 tile, or for m <= 128
-  // (qm_gemm_tile_m) 2 x 4 waves of 64 x 64, a 128 x 256 tile that computes fewer padding
-  // rows; tuning tile 1: 2 x 2 waves of 128 x 128 (row-major x2 only)
+  // default: 2 x 4 waves of 128 x 64 (two per SIMD), a 256 x 256 tile, or with the
+  // planner's 128 tile rows (qm_gemm_tile_m: short m, or short split chunks) 2 x 4 waves of
+  // 64 x 64, a 128 x 256 tile; tuning tile 1: 2 x 2 waves of 128 x 128 (row-major x2 only)
   const bool t1 = a.tile == 1 && !a.x2t;
-  const int bm = t1 ? 256 : qm_gemm_tile_m(a.m);
+  const int bm = t1 ? 256 : a.bm;
   a.tiles_m = (int)((a.m + bm - 1) / bm);
   a.tiles_n = (a.n + kBN - 1) / kBN;
   void (*kern)(const QmArgs);

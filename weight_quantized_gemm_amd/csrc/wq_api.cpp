@@ -18,11 +18,18 @@
 namespace wq {
 
 // Workgroup tile rows of the tiled kernel's default configurations (see aq_gemm.h): 64 for
-// m <= 64; 128 for per-group, and for per-tensor / per-channel while m fits one such tile;
-// 256 otherwise.
-int aq_gemm_tile_m(int64_t m, bool grouped) {
+// m <= 64; 128 for per-group, and for per-tensor / per-channel while m fits one such tile
+// or while 256-row tiles would split k into chunks of at most 512; 256 otherwise.  Such
+// short chunks cost 256-row workgroups more in pipeline fill and drain than 128-row tiles
+// lose by reading each x2 tile from twice as many workgroups (measured 6-30% faster at
+// m = 144..256 with k * n up to 2048 x 8192); with chunks of 1024 and more the 256-row
+// tiles are ahead by up to 7%.
+int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped) {
   if (m <= 64) return 64;
-  return (grouped || m <= 128) ? 128 : 256;
+  if (grouped || m <= 128) return 128;
+  const int64_t tiles = (m + 255) / 256 * ((n + kAqTileN - 1) / kAqTileN);
+  const SplitPlan s = gemm_split_plan(tiles, k, 64);
+  return (s.splits > 1 && s.kchunk <= 512) ? 128 : 256;
 }
 
 // Split k when the tiles alone would leave CUs idle: as many splits as bring the workgroups
@@ -45,6 +52,16 @@ SplitPlan gemm_split_plan(int64_t tiles, int k, int unit) {
   return p;
 }
 
+// Tile rows of the W8A8 kernel's default configuration: 128 while m fits one such tile, or
+// while 256-row tiles would split k into chunks of at most 512 (the rule and its reason are
+// aq_gemm_tile_m's); 256 otherwise.
+int qm_gemm_tile_m(int64_t m, int k, int n) {
+  if (m <= 128) return 128;
+  const int64_t tiles = (m + 255) / 256 * ((n + kQmTileN - 1) / kQmTileN);
+  const SplitPlan s = gemm_split_plan(tiles, k, 64);
+  return (s.splits > 1 && s.kchunk <= 512) ? 128 : 256;
+}
+
 namespace {
 
 constexpr int64_t kAlign = 256;
@@ -57,6 +74,7 @@ struct AqPlan {
   bool empty_k = false;
   bool small_m = false;
   SplitPlan split;           // k splits of the small-m or the tiled kernel
+  int bm = 0;                // tiled kernel: tile rows (aq_gemm_tile_m)
   int64_t partial_bytes = 0;
   int64_t rowsum_bytes = 0;
   int64_t param_bytes = 0;   // per-group scale / offset given transposed: row-major copies
@@ -77,8 +95,8 @@ AqPlan plan_antiquant(const AntiquantProblem& p) {
   } else {
     // per-group splits end on group boundaries (the precomputed S_g cover whole groups)
     const int unit = grouped ? (p.group % 64 == 0 ? (int)p.group : 2 * (int)p.group) : 64;
-    const int bm = aq_gemm_tile_m(p.m, grouped);
-    const int64_t tiles = (p.m + bm - 1) / bm * ((p.n + kAqTileN - 1) / kAqTileN);
+    pl.bm = aq_gemm_tile_m(p.m, (int)p.k, (int)p.n, grouped);
+    const int64_t tiles = (p.m + pl.bm - 1) / pl.bm * ((p.n + kAqTileN - 1) / kAqTileN);
     pl.split = gemm_split_plan(tiles, (int)p.k, unit);
   }
   if (pl.split.splits > 1) {
@@ -104,13 +122,14 @@ int tile_override() {
 // The W8A8 kernel's k splits and int32 partials.
 struct QmPlan {
   SplitPlan split;
+  int bm = 128;
   int64_t workspace = 0;
 };
 QmPlan plan_quant(const QuantProblem& p) {
   QmPlan pl;
   if (p.k == 0) return pl;
-  const int bm = qm_gemm_tile_m(p.m);
-  const int64_t tiles = (p.m + bm - 1) / bm * ((p.n + kQmTileN - 1) / kQmTileN);
+  pl.bm = qm_gemm_tile_m(p.m, (int)p.k, (int)p.n);
+  const int64_t tiles = (p.m + pl.bm - 1) / pl.bm * ((p.n + kQmTileN - 1) / kQmTileN);
   pl.split = gemm_split_plan(tiles, (int)p.k, 64);
   if (pl.split.splits > 1) pl.workspace = align_up((int64_t)pl.split.splits * p.m * p.n * (int64_t)sizeof(int32_t));
   return pl;
@@ -198,6 +217,7 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.splits = pl.split.splits;
   a.kchunk = pl.split.kchunk;
   a.tile = wq::tile_override();
+  a.bm = pl.bm;
 
   hipError_t e;
   if (pl.param_bytes) {
@@ -268,6 +288,7 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
   a.kchunk = pl.split.kchunk;
   a.partial = pl.workspace ? (int32_t*)workspace : nullptr;
   a.tile = wq::tile_override();
+  a.bm = pl.bm;
   hipError_t e = wq::launch_qm_gemm(a, (hipStream_t)stream);
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
 }

@@ -25,6 +25,7 @@ struct AqArgs {
   int32_t kchunk;        // k rows per split (a multiple of 64; per-group large m: of the group too)
   int32_t tiles_m, tiles_n;
   int32_t tile;          // tile configuration index (0 = default)
+  int32_t bm;            // tile rows of the default configuration (aq_gemm_tile_m)
   float code_bias;       // C: the fed weight image is code + C
   bool bf16, w4, f8, grouped, per_tensor;  // f8: FLOAT8_E4M3FN weights
   bool x2t;              // x2 stored transposed: (n, k) (int4: (n, k/2) bytes along k)
@@ -47,6 +48,7 @@ struct QmArgs {
   int32_t kchunk;        // k rows per split (a multiple of 64)
   int32_t tiles_m, tiles_n;
   int32_t tile;          // tile configuration index (0 = default)
+  int32_t bm;            // tile rows of the default configuration (qm_gemm_tile_m)
   bool out_bf16, dq_bf16, dq_per_tensor;
   bool x2t;              // x2 stored transposed, (n, k)
 };
@@ -87,11 +89,11 @@ struct SplitPlan {
 SplitPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped);
 // Large m: the workgroup tile the default configuration uses, and the k splits that bring
 // the workgroup count up to about one per CU when the tiles alone leave CUs idle.
-int aq_gemm_tile_m(int64_t m, bool grouped);
+int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped);
 constexpr int kAqTileN = 256;
 SplitPlan gemm_split_plan(int64_t tiles, int k, int unit);
 // W8A8: the workgroup tile of the default configuration (rows 128 for m <= 128, else 256)
-inline int qm_gemm_tile_m(int64_t m) { return m <= 128 ? 128 : 256; }
+int qm_gemm_tile_m(int64_t m, int k, int n);
 constexpr int kQmTileN = 256;
 
 }  // namespace wq
