@@ -260,8 +260,9 @@ def test_workspace_sizes(wqlib):
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                         r(out), r(size)) == OK
     assert size.value == 0
-    # ... else fp32 split-k partials and row sums: 2 x 1 tiles of 256 rows want 128 splits,
-    # but a split keeps at least 256 k, so k = 1024 gives 4 splits
+    # ... else fp32 split-k partials and row sums: 256-row tiles would split k = 1024 into
+    # chunks of 256, so the tiles are 128 rows (3 x 1 want 85 splits), but a split keeps at
+    # least 256 k, so k = 1024 gives 4 splits
     x1, x2, sc, out = base(m=300, k=1024, n=256)
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                         r(out), r(size)) == OK
@@ -277,10 +278,21 @@ def test_workspace_sizes(wqlib):
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                         r(out), r(size)) == OK
     assert size.value == 4 * 64 * 256 * 4 + 1024
-    # W8A8: int32 partials under the same rule (tiles of 256 x 256, 128 x 256 for m <= 128)
+    # beyond m = 128 the 256-row tiles stay where their split chunks would be over 512 long:
+    # 256 x 16384 x 4096 has 16 such tiles, chunks of 1024, 16 splits (128-row tiles would
+    # have taken 8); 512 x 4096 x 4096 would split 32 tiles into chunks of 512, so it takes
+    # 64 tiles of 128 rows, chunks of 1024, 4 splits (256-row tiles would have taken 8)
+    for (m, k, n), splits in (((256, 16384, 4096), 16), ((512, 4096, 4096), 4)):
+        x1, x2, sc, out = base(m=m, k=k, n=n)
+        assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
+                                                            r(out), r(size)) == OK
+        assert size.value == splits * m * n * 4 + splits * m * 4, (m, k, n, size.value)
+    # W8A8: int32 partials under the same rules (tiles of 256 x 256, or 128 x 256)
     i8 = W.WQ_I8
     for (m, k, n), want in (((4096, 4096, 4096), 0), ((32, 8192, 8192), 8 * 32 * 8192 * 4),
-                            ((300, 1024, 256), 4 * 300 * 256 * 4)):
+                            ((300, 1024, 256), 4 * 300 * 256 * 4),
+                            ((256, 16384, 4096), 16 * 256 * 4096 * 4),
+                            ((512, 4096, 4096), 4 * 512 * 4096 * 4)):
         assert wqlib.wq_quant_matmul_get_workspace_size(
             r(D([m, k], i8)), r(D([k, n], i8)), None, None, r(D([n], W.WQ_F32)), None,
             r(D([m, n], W.WQ_BF16)), None, r(size)) == OK

@@ -34,7 +34,8 @@ constexpr int kRA = kBK;                        // bytes per x1 row in a stage
 constexpr int kRB = kBN;                        // bytes per x2 row in a stage
 constexpr int kBbytes = kBK * kRB;              // 16 KiB
 static_assert(kBN == kQmTileN, "the planner's tile is the kernel's");
-// per workgroup-tile height BM (256, or 128 for m <= 128): x1 stage, stage, LDS
+// per workgroup-tile height BM (256, or 128 for short m or short split chunks): x1 stage,
+// stage, LDS
 template <int BM> constexpr int qm_abytes() { return BM * kRA; }          // 16 / 8 KiB
 template <int BM> constexpr int qm_stage() { return qm_abytes<BM>() + kBbytes; }
 template <int BM> constexpr int qm_lds() { return kStages * qm_stage<BM>(); }  // 128 / 96 KiB
