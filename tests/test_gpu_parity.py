@@ -124,6 +124,17 @@ AQ_CASES = [
     ("midm_m57_perchannel_bf16_f8_nosplit", dict(act="bf16", weight="fp8e4m3", x1_shape=(57, 256), n=96,
                                                  mode="channel", with_offset=False,
                                                  scale_dist=("uniform", 2e-4, 1e-3))),
+    # 64 < m <= 128 whose 128-row tiles would split k into chunks of at most 512: two 64-row
+    # tiles (the second ragged), every mode and weight type
+    ("midm_m96_pergroup128_bf16_i4_rows64", dict(act="bf16", weight="int4", x1_shape=(96, 2048), n=512,
+                                                 mode="group", group_size=128)),
+    ("midm_m72_perchannel_bf16_f8_rows64", dict(act="bf16", weight="fp8e4m3", x1_shape=(72, 1024), n=256,
+                                                mode="channel", with_offset=False,
+                                                scale_dist=("uniform", 2e-4, 1e-3))),
+    ("midm_m128_pertensor_fp16_i8_rows64", dict(act="fp16", weight="int8", x1_shape=(2, 64, 4096), n=768,
+                                                mode="tensor")),
+    ("midm_xt_m120_pergroup64_fp16_i8_rows64", dict(act="fp16", weight="int8", x1_shape=(120, 1536), n=320,
+                                                    mode="group", group_size=64, x2_transposed=True)),
     # m > 128 whose 256-row tiles would split k into chunks of at most 512: several 128-row
     # tiles (ragged last row tile), per-tensor / per-channel, every weight type, both x2 layouts
     ("midm_m160_perchannel_bf16_i8_rows128", dict(act="bf16", weight="int8", x1_shape=(160, 2048), n=512,

@@ -282,7 +282,11 @@ def test_workspace_sizes(wqlib):
     # 256 x 16384 x 4096 has 16 such tiles, chunks of 1024, 16 splits (128-row tiles would
     # have taken 8); 512 x 4096 x 4096 would split 32 tiles into chunks of 512, so it takes
     # 64 tiles of 128 rows, chunks of 1024, 4 splits (256-row tiles would have taken 8)
-    for (m, k, n), splits in (((256, 16384, 4096), 16), ((512, 4096, 4096), 4)):
+    # and at 64 < m <= 128 the 64-row tiles likewise: 96 x 4096 x 4096 would split one row of
+    # 16 tiles of 128 rows into chunks of 256, so it takes 2 x 16 tiles of 64 rows, 8 splits;
+    # 128 x 8192 x 8192 keeps 128 rows (chunks of 1024, 8 splits; 64 rows would take 4)
+    for (m, k, n), splits in (((256, 16384, 4096), 16), ((512, 4096, 4096), 4),
+                              ((96, 4096, 4096), 8), ((128, 8192, 8192), 8)):
         x1, x2, sc, out = base(m=m, k=k, n=n)
         assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                             r(out), r(size)) == OK

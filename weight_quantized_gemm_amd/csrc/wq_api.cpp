@@ -17,19 +17,24 @@
 
 namespace wq {
 
-// Workgroup tile rows of the tiled kernel's default configurations (see aq_gemm.h): 64 for
-// m <= 64; 128 for per-group, and for per-tensor / per-channel while m fits one such tile
-// or while 256-row tiles would split k into chunks of at most 512; 256 otherwise.  Such
-// short chunks cost 256-row workgroups more in pipeline fill and drain than 128-row tiles
-// lose by reading each x2 tile from twice as many workgroups (measured 6-30% faster at
-// m = 144..256 with k * n up to 2048 x 8192); with chunks of 1024 and more the 256-row
-// tiles are ahead by up to 7%.
+// Workgroup tile rows of the tiled kernel's default configurations (see aq_gemm.h): the
+// mode's tile (256 rows per-tensor / per-channel, 128 per-group), or the next shorter one
+// while m fits it, or while the longer tiles would split k into chunks of at most 512.
+// Such short chunks cost the taller workgroups more in pipeline fill and drain than the
+// shorter tiles lose by reading each x2 tile from twice as many workgroups: 128 rows
+// instead of 256 measured 6-30% faster at m = 144-1024, 64 instead of 128 6-17% faster at
+// m = 80-128 (both with k * n up to 2048 x 8192); with chunks of 1024 and more the taller
+// tiles are level or ahead by up to 7%.  64 rows are taken only up to m = 128.
 int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped) {
+  const int64_t tiles_n = (n + kAqTileN - 1) / kAqTileN;
+  auto short_chunks = [&](int bm) {
+    const SplitPlan s = gemm_split_plan((m + bm - 1) / bm * tiles_n, k, 64);
+    return s.splits > 1 && s.kchunk <= 512;
+  };
   if (m <= 64) return 64;
-  if (grouped || m <= 128) return 128;
-  const int64_t tiles = (m + 255) / 256 * ((n + kAqTileN - 1) / kAqTileN);
-  const SplitPlan s = gemm_split_plan(tiles, k, 64);
-  return (s.splits > 1 && s.kchunk <= 512) ? 128 : 256;
+  if (m <= 128) return short_chunks(128) ? 64 : 128;
+  if (grouped) return 128;
+  return short_chunks(256) ? 128 : 256;
 }
 
 // Split k when the tiles alone would leave CUs idle: as many splits as bring the workgroups
