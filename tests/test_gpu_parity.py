@@ -446,6 +446,12 @@ W8A8_CASES = [
     ("w8a8_splitk_m64", dict(out="bf16", x1_shape=(64, 4096), n=512)),
     ("w8a8_splitk_m300_tail_xt", dict(out="fp16", x1_shape=(300, 2080), n=320, x2_transposed=True)),
     ("w8a8_splitk_m7_tensor", dict(out="bf16", x1_shape=(7, 3072), n=96, dequant="tensor", with_pertoken=False)),
+    # 64-row tiles: m <= 64, and 64 < m <= 128 where 128-row tiles would split k into chunks
+    # of at most 512 (two row tiles, the second ragged)
+    ("w8a8_rows64_m100", dict(out="bf16", x1_shape=(100, 2048), n=512)),
+    ("w8a8_rows64_m120_xt_3d", dict(out="fp16", x1_shape=(2, 60, 1024), n=768, x2_transposed=True)),
+    ("w8a8_rows64_m64_xt_tensor", dict(out="bf16", x1_shape=(64, 3072), n=320, x2_transposed=True,
+                                       dequant="tensor", with_pertoken=False)),
     # m > 128 with 256-row tiles that would split k into chunks of at most 512: 128-row tiles
     ("w8a8_rows128_m200_3d", dict(out="bf16", x1_shape=(2, 100, 2048), n=768)),
     ("w8a8_rows128_m256_xt", dict(out="fp16", x1_shape=(256, 1536), n=512, x2_transposed=True)),

@@ -291,12 +291,13 @@ def test_workspace_sizes(wqlib):
         assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                             r(out), r(size)) == OK
         assert size.value == splits * m * n * 4 + splits * m * 4, (m, k, n, size.value)
-    # W8A8: int32 partials under the same rules (tiles of 256 x 256, or 128 x 256)
+    # W8A8: int32 partials under the same rules (tiles of 256, 128 or 64 rows)
     i8 = W.WQ_I8
     for (m, k, n), want in (((4096, 4096, 4096), 0), ((32, 8192, 8192), 8 * 32 * 8192 * 4),
                             ((300, 1024, 256), 4 * 300 * 256 * 4),
                             ((256, 16384, 4096), 16 * 256 * 4096 * 4),
-                            ((512, 4096, 4096), 4 * 512 * 4096 * 4)):
+                            ((512, 4096, 4096), 4 * 512 * 4096 * 4),
+                            ((96, 4096, 4096), 8 * 96 * 4096 * 4)):
         assert wqlib.wq_quant_matmul_get_workspace_size(
             r(D([m, k], i8)), r(D([k, n], i8)), None, None, r(D([n], W.WQ_F32)), None,
             r(D([m, n], W.WQ_BF16)), None, r(size)) == OK

@@ -34,11 +34,11 @@ constexpr int kRA = kBK;                        // bytes per x1 row in a stage
 constexpr int kRB = kBN;                        // bytes per x2 row in a stage
 constexpr int kBbytes = kBK * kRB;              // 16 KiB
 static_assert(kBN == kQmTileN, "the planner's tile is the kernel's");
-// per workgroup-tile height BM (256, or 128 for short m or short split chunks): x1 stage,
-// stage, LDS
-template <int BM> constexpr int qm_abytes() { return BM * kRA; }          // 16 / 8 KiB
+// per workgroup-tile height BM (256, or 128 / 64 for short m or short split chunks): x1
+// stage, stage, LDS
+template <int BM> constexpr int qm_abytes() { return BM * kRA; }          // 16 / 8 / 4 KiB
 template <int BM> constexpr int qm_stage() { return qm_abytes<BM>() + kBbytes; }
-template <int BM> constexpr int qm_lds() { return kStages * qm_stage<BM>(); }  // 128 / 96 KiB
+template <int BM> constexpr int qm_lds() { return kStages * qm_stage<BM>(); }  // 128 / 96 / 80 KiB
 
 // Wave grid GM x GN with WM x WN 32x32 blocks per wave (BM x 256 per workgroup); XT: x2
 // stored transposed, (n, k).
@@ -391,22 +391,27 @@ __global__ __launch_bounds__(256) void qm_splitk_finish(const QmArgs a) {
 hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   QmArgs a = a0;
   // default: 2 x 4 waves of 128 x 64 (two per SIMD), a 256 x 256 tile, or with the
-  // planner's 128 tile rows (qm_gemm_tile_m: short m, or short split chunks) 2 x 4 waves of
-  // 64 x 64, a 128 x 256 tile; tuning tile 1: 2 x 2 waves of 128 x 128 (row-major x2 only)
+  // planner's shorter tile rows (qm_gemm_tile_m: short m, or short split chunks) 2 x 4 waves
+  // of 64 x 64, a 128 x 256 tile, or 2 x 2 waves of 32 x 128, a 64 x 256 tile (its x1 stage
+  // is one 16-row block per wave; its 80 KiB of LDS let two workgroups share a CU); tuning
+  // tile 1: 2 x 2 waves of 128 x 128 (row-major x2 only)
   const bool t1 = a.tile == 1 && !a.x2t;
   const int bm = t1 ? 256 : a.bm;
   a.tiles_m = (int)((a.m + bm - 1) / bm);
   a.tiles_n = (a.n + kBN - 1) / kBN;
   void (*kern)(const QmArgs);
-  if (bm == 128)
+  if (bm == 64)
+    kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, true, 64> : qm_gemm_kernel<false, 2, 2, true, 64>)
+                 : (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, false, 64> : qm_gemm_kernel<false, 2, 2, false, 64>);
+  else if (bm == 128)
     kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, true, 128> : qm_gemm_kernel<false, 2, 4, true, 128>)
                  : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false, 128> : qm_gemm_kernel<false, 2, 4, false, 128>);
   else
     kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, true> : qm_gemm_kernel<false, 2, 4, true>)
            : t1  ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, false> : qm_gemm_kernel<false, 2, 2, false>)
                  : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false> : qm_gemm_kernel<false, 2, 4, false>);
-  const int threads = t1 ? 256 : 512;
-  const int kLds = bm == 128 ? qm_lds<128>() : qm_lds<256>();
+  const int threads = (t1 || bm == 64) ? 256 : 512;
+  const int kLds = bm == 64 ? qm_lds<64>() : bm == 128 ? qm_lds<128>() : qm_lds<256>();
   hipError_t e = raise_lds_limit((const void*)kern, kLds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;

@@ -57,14 +57,18 @@ SplitPlan gemm_split_plan(int64_t tiles, int k, int unit) {
   return p;
 }
 
-// Tile rows of the W8A8 kernel's default configuration: 128 while m fits one such tile, or
-// while 256-row tiles would split k into chunks of at most 512 (the rule and its reason are
-// aq_gemm_tile_m's); 256 otherwise.
+// Tile rows of the W8A8 kernel's default configuration, by aq_gemm_tile_m's rule: 256, or
+// the next shorter tile while m fits it or while the taller tiles would split k into chunks
+// of at most 512 (64 rows only up to m = 128).
 int qm_gemm_tile_m(int64_t m, int k, int n) {
-  if (m <= 128) return 128;
-  const int64_t tiles = (m + 255) / 256 * ((n + kQmTileN - 1) / kQmTileN);
-  const SplitPlan s = gemm_split_plan(tiles, k, 64);
-  return (s.splits > 1 && s.kchunk <= 512) ? 128 : 256;
+  const int64_t tiles_n = (n + kQmTileN - 1) / kQmTileN;
+  auto short_chunks = [&](int bm) {
+    const SplitPlan s = gemm_split_plan((m + bm - 1) / bm * tiles_n, k, 64);
+    return s.splits > 1 && s.kchunk <= 512;
+  };
+  if (m <= 64) return 64;
+  if (m <= 128) return short_chunks(128) ? 64 : 128;
+  return short_chunks(256) ? 128 : 256;
 }
 
 namespace {
