@@ -291,6 +291,13 @@ def test_workspace_sizes(wqlib):
         assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 0,
                                                             r(out), r(size)) == OK
         assert size.value == splits * m * n * 4 + splits * m * 4, (m, k, n, size.value)
+    # per-group too: 96 x 8192 x 2048 with g = 128 would split 8 tiles of 128 rows into chunks
+    # of 256 (32 splits), so it takes 16 tiles of 64 rows, chunks of 512, 16 splits; then the
+    # row sums per group, (64, 96) fp32
+    x1, x2, sc, out = base(m=96, k=8192, n=2048, scale=[64, 2048])
+    assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(x2), None, r(sc), None, None, 128,
+                                                        r(out), r(size)) == OK
+    assert size.value == 16 * 96 * 2048 * 4 + 64 * 96 * 4
     # W8A8: int32 partials under the same rules (tiles of 256, 128 or 64 rows)
     i8 = W.WQ_I8
     for (m, k, n), want in (((4096, 4096, 4096), 0), ((32, 8192, 8192), 8 * 32 * 8192 * 4),
