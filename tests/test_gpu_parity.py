@@ -321,8 +321,12 @@ def _antiquant_tensors(case):
                                              mode="channel")),
     ("graph_splitk_pergroup128_fp16_i4", dict(act="fp16", weight="int4", x1_shape=(64, 2048), n=256,
                                               mode="group", group_size=128)),
+    # m > 128 on 128-row tiles (256-row tiles would split k into chunks of 256)
+    ("graph_splitk_rows128_perchannel_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(200, 1024), n=512,
+                                                     mode="channel")),
 ], ids=["graph_smallm_pergroup64_fp16_i8", "graph_largem_pergroup128_bf16_i4", "graph_largem_perchannel_bf16_i8",
-        "graph_splitk_perchannel_bf16_i8", "graph_splitk_pergroup128_fp16_i4"])
+        "graph_splitk_perchannel_bf16_i8", "graph_splitk_pergroup128_fp16_i4",
+        "graph_splitk_rows128_perchannel_fp16_i8"])
 def test_graph_replay_antiquant(name, spec):
     """A prepared call captured in a HIP graph and replayed on new inputs (copied into the
     captured buffers, with eager work and synchronisation between replays): every replay
@@ -356,10 +360,12 @@ def test_graph_replay_antiquant(name, spec):
         assert r["ok"], (case.name, r)
 
 
-@pytest.mark.parametrize("x1_shape,n", [((300, 256), 320), ((64, 2048), 256)], ids=["tiles", "splitk"])
+@pytest.mark.parametrize("x1_shape,n", [((300, 256), 320), ((64, 2048), 256), ((200, 1024), 512)],
+                         ids=["tiles", "splitk", "splitk_rows128"])
 def test_graph_replay_w8a8(x1_shape, n):
     """The W8A8 prepared call captured and replayed on new inputs, checked like the
-    anti-quant graph test (the int32 accumulator bit-exact); the second shape splits k."""
+    anti-quant graph test (the int32 accumulator bit-exact); the second shape splits k on
+    64-row tiles, the third on 128-row tiles beyond m = 128."""
     import torch
     import weight_quantized_gemm_amd as W
     _announce(f"graph_w8a8_{x1_shape}_{n}")
