@@ -17,15 +17,17 @@
 
 namespace wq {
 
-// Workgroup tile rows of the tiled kernel's default configurations (see aq_gemm.h): the
-// mode's tile (256 rows per-tensor / per-channel, 128 per-group), or the next shorter one
-// while m fits it, or while the longer tiles would split k into chunks of at most 512.
-// Such short chunks cost the taller workgroups more in pipeline fill and drain than the
-// shorter tiles lose by reading each x2 tile from twice as many workgroups: 128 rows
-// instead of 256 measured 6-30% faster at m = 144-1024, 64 instead of 128 6-17% faster at
-// m = 80-128 (both with k * n up to 2048 x 8192); with chunks of 1024 and more the taller
-// tiles are level or ahead by up to 7%.  64 rows are taken only up to m = 128.
-int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped) {
+static_assert(kAqTileN == kQmTileN, "both tiled kernels' tiles are equally wide");
+
+// Workgroup tile rows of a tiled kernel's default configuration for an m x k x n product:
+// its tallest tile (`tallest` rows), or the next shorter one while m fits it, or while the
+// taller tiles would split k into chunks of at most 512.  Such short chunks cost the taller
+// workgroups more in pipeline fill and drain than the shorter tiles lose by reading each x2
+// tile from twice as many workgroups: 128 rows instead of 256 measured 6-30% faster at
+// m = 144-1024, 64 instead of 128 6-17% faster at m = 80-128 (both with k * n up to
+// 2048 x 8192); with chunks of 1024 and more the taller tiles are level or ahead by up to
+// 7%.  64 rows are taken only up to m = 128.
+static int tile_rows(int64_t m, int k, int n, int tallest) {
   const int64_t tiles_n = (n + kAqTileN - 1) / kAqTileN;
   auto short_chunks = [&](int bm) {
     const SplitPlan s = gemm_split_plan((m + bm - 1) / bm * tiles_n, k, 64);
@@ -33,8 +35,14 @@ int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped) {
   };
   if (m <= 64) return 64;
   if (m <= 128) return short_chunks(128) ? 64 : 128;
-  if (grouped) return 128;
+  if (tallest == 128) return 128;
   return short_chunks(256) ? 128 : 256;
+}
+
+// The anti-quant kernel (see aq_gemm.h): tallest tiles of 256 rows per-tensor /
+// per-channel, 128 per-group.
+int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped) {
+  return tile_rows(m, k, n, grouped ? 128 : 256);
 }
 
 // Split k when the tiles alone would leave CUs idle: as many splits as bring the workgroups
@@ -57,19 +65,8 @@ SplitPlan gemm_split_plan(int64_t tiles, int k, int unit) {
   return p;
 }
 
-// Tile rows of the W8A8 kernel's default configuration, by aq_gemm_tile_m's rule: 256, or
-// the next shorter tile while m fits it or while the taller tiles would split k into chunks
-// of at most 512 (64 rows only up to m = 128).
-int qm_gemm_tile_m(int64_t m, int k, int n) {
-  const int64_t tiles_n = (n + kQmTileN - 1) / kQmTileN;
-  auto short_chunks = [&](int bm) {
-    const SplitPlan s = gemm_split_plan((m + bm - 1) / bm * tiles_n, k, 64);
-    return s.splits > 1 && s.kchunk <= 512;
-  };
-  if (m <= 64) return 64;
-  if (m <= 128) return short_chunks(128) ? 64 : 128;
-  return short_chunks(256) ? 128 : 256;
-}
+// The W8A8 kernel (qm_gemm.hip): tallest tiles of 256 rows.
+int qm_gemm_tile_m(int64_t m, int k, int n) { return tile_rows(m, k, n, 256); }
 
 namespace {
 

@@ -92,7 +92,7 @@ SplitPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped);
 int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped);
 constexpr int kAqTileN = 256;
 SplitPlan gemm_split_plan(int64_t tiles, int k, int unit);
-// W8A8: the workgroup tile rows of the default configuration (128 or 256)
+// W8A8: the workgroup tile rows of the default configuration (64, 128 or 256)
 int qm_gemm_tile_m(int64_t m, int k, int n);
 constexpr int kQmTileN = 256;
 
