@@ -510,6 +510,44 @@ def test_full_size_sampled(name):
         assert r["ok"], r
 
 
+# ---------------------------------------------------------------- outputs past 2^31 elements
+# m = 262,181 rows of 8192 columns: 2.15e9 output elements (4.3 GB bf16), so element offsets
+# in the output, the int32 accumulator and the row tiles pass the int32 range (32,800 tiles,
+# no split).  Checked on sampled rows that include rows whose first element lies past 2^31;
+# the rows are taken on the device before anything is copied to the host.
+BIG_M, BIG_N = 262181, 8192
+BIG_ROWS = [0, 1, 131072, 262143, 262144, 262145, BIG_M - 1]
+
+
+def test_output_past_int32_elements_antiquant():
+    import torch
+    _announce("big_m_antiquant")
+    case = workloads.make_antiquant(seed=2600, name="big_m", act="bf16", weight="int8",
+                                    x1_shape=(BIG_M, 64), n=BIG_N, mode="channel", with_x3=False)
+    rows = np.array(sorted(set(BIG_ROWS + sampled_rows(case.m).tolist())))
+    y = run_antiquant(case)
+    got = to_f64(y.reshape(-1, case.n)[torch.as_tensor(rows, device=y.device)])
+    del y
+    r = oracle.compare(got, ref_antiquant(case, rows).reshape(got.shape), case.act)
+    assert r["ok"], r
+
+
+def test_output_past_int32_elements_w8a8():
+    import torch
+    _announce("big_m_w8a8")
+    case = workloads.make_w8a8(seed=2601, name="big_m_w8a8", out="bf16", x1_shape=(BIG_M, 64), n=BIG_N,
+                               with_x3=False)
+    rows = np.array(sorted(set(BIG_ROWS + sampled_rows(case.m).tolist())))
+    y, acc = run_w8a8(case)
+    idx = torch.as_tensor(rows, device=y.device)
+    got, got_acc = to_f64(y.reshape(-1, case.n)[idx]), acc[idx].cpu().numpy().astype(np.int64)
+    del y, acc
+    ref, racc = ref_w8a8(case, rows)
+    assert np.array_equal(got_acc, racc)
+    r = oracle.compare(got, ref.reshape(got.shape), case.out)
+    assert r["ok"], r
+
+
 # ---------------------------------------------------------------- seeded sweep
 def _sweep_antiquant(count=48, seed=4242, ms=(1, 2, 7, 31, 32, 33, 65, 100, 257, 300), kmax=24, prefix="sw"):
     """Random combinations of dtype, weight format, mode, layout, optional inputs and ragged
