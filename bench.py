@@ -10,9 +10,10 @@ timed steps read their operands from HBM, not from a warm cache.
 
 Each input set gets a prepared call (descriptors and workspace settled once), so the host
 enqueues steps faster than the device runs them.  The timed region covers exactly the
-timed steps, bracketed by device synchronisation.  As many steps again follow it, each with
-the library's profiling hook recording a pair of HIP events on the launch stream around the
-step's main kernel, which gives that kernel's average launch duration for the roofline.
+timed steps, bracketed by device synchronisation.  In each timed step the library's
+profiling hook passes a pair of HIP events with the launch of the step's main kernel
+(hipExtLaunchKernel), so that they take that kernel's own start and end on its launch
+stream; their average is the kernel duration of the roofline.
 
 Output: one JSON line (the headline workload), with the roofline of the dominant kernel
 and the CPU oracle's rate on the host as a baseline.  ``--all`` prints one line per
@@ -169,6 +170,30 @@ def traffic_for(kernel, name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def make_roofline(bound, dtype, flops, abytes, launch_ms, ms_per_step):
+    """The roofline entry of the dominant kernel from its per-launch durations (ms, one per
+    step).  Each step launches that kernel once, so its average duration cannot exceed the
+    step's: a longer one means the durations do not belong to these steps."""
+    per = sorted(launch_ms)
+    avg_ms = sum(per) / len(per)
+    if avg_ms > ms_per_step * (1 + 1e-9):
+        raise ValueError(f"kernel average {avg_ms * 1e3:.2f} us exceeds the step's {ms_per_step * 1e3:.2f} us")
+    avg_s = avg_ms / 1e3
+    if bound == "mfma":
+        achieved = flops / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[dtype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK[dtype], 4)}
+    else:
+        achieved = abytes / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM, 4)}
+    roof["launch_us_median"] = round(per[len(per) // 2] * 1e3, 2)
+    roof["launch_us_avg"] = round(avg_ms * 1e3, 2)
+    roof["launch_us_min"] = round(per[0] * 1e3, 2)
+    roof["launch_us_max"] = round(per[-1] * 1e3, 2)
+    return roof
+
+
 def bench_one(name, args, torch, dev):
     import weight_quantized_gemm_amd as W
     case = workloads.make_workload(name)
@@ -185,39 +210,32 @@ def bench_one(name, args, torch, dev):
         a.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
+    # The timed steps.  Each arms the library's profiling hook, which hands the two events of
+    # the step to the launch of its main kernel (hipExtLaunchKernel): they take that kernel's
+    # own start and end on the launch stream and add no work of their own to the stream.
+    # With --kernel-events after, the hooked steps run after the timed ones instead.
+    hooked_in_timed = args.kernel_events == "timed"
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if hooked_in_timed:
+            W.profile_next_call(*evs[i])
         calls[(args.warmup + i) % sets](sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Kernel durations: as many steps again, each with the profiling hook's two events around
-    # its main kernel.  They run outside the timed region because the event records are
-    # work of their own on the stream.
-    for i in range(args.steps):
-        W.profile_next_call(*evs[i])
-        calls[(args.warmup + args.steps + i) % sets](sh)
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) for a, b in evs)          # ms, main kernel per step
-    ev_total = sum(per)
+    if not hooked_in_timed:
+        for i in range(args.steps):
+            W.profile_next_call(*evs[i])
+            calls[(args.warmup + args.steps + i) % sets](sh)
+        torch.cuda.synchronize()
+    launch_ms = [a.elapsed_time(b) for a, b in evs]          # ms, main kernel per step
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.0 * case.m * case.k * case.n
     kernel, bound = DOMINANT[name]
     dtype = "int8" if isinstance(case, workloads.W8A8Case) else case.act
-    avg_launch_s = (ev_total / len(per)) / 1e3
-    if bound == "mfma":
-        achieved = flops / avg_launch_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[dtype], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK[dtype], 4)}
-    else:
-        achieved = abytes / avg_launch_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM, 4)}
+    roof = make_roofline(bound, dtype, flops, abytes, launch_ms, ms_per_step)
     roof["traffic"] = traffic_for(kernel, name)
     roof["kernel"] = kernel
-    roof["launch_us_median"] = round(per[len(per) // 2] * 1e3, 2)
-    roof["launch_us_avg"] = round(avg_launch_s * 1e6, 2)
-    roof["launch_us_min"] = round(per[0] * 1e3, 2)
-    roof["launch_us_max"] = round(per[-1] * 1e3, 2)
+    roof["kernel_events"] = "timed steps" if hooked_in_timed else "steps after the timed ones"
     value = flops / (ms_per_step / 1e3) / 1e12
     spec = workloads.WORKLOADS[name]
     line = {
@@ -273,6 +291,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", dest="cpu", action="store_false", help="skip the CPU oracle leg")
+    ap.add_argument("--kernel-events", choices=("timed", "after"), default="timed",
+                    help="where the main kernel's event pairs are taken: on the timed steps (default) "
+                         "or on as many steps after them")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the matmul, time a plain device-to-device copy of this many MiB "
                          "(the reference kernel for scaling HBM byte counters)")

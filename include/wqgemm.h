@@ -151,7 +151,10 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
  *                   Constraints: n may exceed 65535 only when x2 is transposed).
  *   bias            optional; WQ_I32; (n).  Added to the int32 accumulator before scaling.
  *   x3              optional; the output's dtype and shape.
- *   dequant_scale   required; WQ_F32 or WQ_BF16; (1), (n) or (1, n).
+ *   dequant_scale   required; (1), (n) or (1, n).  With a WQ_F16 output: WQ_F32 (the
+ *                   Constraints ask for FLOAT32 when a pertoken scale is given, and for the
+ *                   packed INT64/UINT64 form without one, which FLOAT32 replaces here).
+ *                   With a WQ_BF16 output: WQ_BF16 (the Constraints' type) or WQ_F32.
  *   pertoken_scale  optional; WQ_F32; (m) (m = b*s for 3-D x1).  Absent means 1.
  *   output          required; WQ_F16 or WQ_BF16; (m, n) or (b, s, n) following x1.
  *   acc_out         optional; WQ_I32; (m, n): receives x1 @ x2 + bias as int32 (two's

@@ -24,7 +24,10 @@ def to_f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def run_antiquant(case, device="cuda:0", out=None):
+def run_antiquant(case, device="cuda:0", out=None, stream=None, keep=None):
+    """The one-shot call on `case`.  With `stream`, the call runs there after waiting for the
+    current stream (which made the inputs); `keep` (a list) then receives the input tensors,
+    which the caller holds until it has synchronised `stream`."""
     import weight_quantized_gemm_amd as W
     act = case.act
     x1 = dev_tensor(case.x1, act, device)
@@ -42,8 +45,11 @@ def run_antiquant(case, device="cuda:0", out=None):
     args = dict(antiquant_offset=offset,
                 bias=dev_tensor(case.bias, act, device), x3=dev_tensor(case.x3, act, device),
                 antiquant_group_size=case.group_size, x2_int4=case.weight == "int4", out=out)
-    y = W.antiquant_matmul(x1, x2, scale, **args)
-    return y
+    if stream is not None:
+        stream.wait_stream(torch_mod().cuda.current_stream(device))
+        if keep is not None:
+            keep.extend([x1, x2, scale, args["antiquant_offset"], args["bias"], args["x3"]])
+    return W.antiquant_matmul(x1, x2, scale, **args, stream=stream)
 
 
 def ref_antiquant(case, rows=None):
@@ -67,7 +73,8 @@ def sample_rows(case, rows):
     return dataclasses.replace(case, x1=x1, x3=x3, pertoken_scale=pt)
 
 
-def run_w8a8(case, device="cuda:0", with_acc=True):
+def run_w8a8(case, device="cuda:0", with_acc=True, stream=None, keep=None):
+    """The one-shot W8A8 call; `stream` and `keep` as for run_antiquant."""
     import weight_quantized_gemm_amd as W
     torch = torch_mod()
     x1 = dev_tensor(case.x1, "raw", device)
@@ -80,7 +87,11 @@ def run_w8a8(case, device="cuda:0", with_acc=True):
     x3 = dev_tensor(case.x3, case.out, device)
     acc = torch.empty((case.m, case.n), dtype=torch.int32, device=device) if with_acc else None
     out_dtype = torch.bfloat16 if case.out == "bf16" else torch.float16
-    y = W.quant_matmul(x1, x2, dq, pt, bias, x3, out_dtype=out_dtype, acc_out=acc)
+    if stream is not None:
+        stream.wait_stream(torch.cuda.current_stream(device))
+        if keep is not None:
+            keep.extend([x1, x2, dq, pt, bias, x3, acc])
+    y = W.quant_matmul(x1, x2, dq, pt, bias, x3, out_dtype=out_dtype, acc_out=acc, stream=stream)
     return y, acc
 
 

@@ -339,3 +339,26 @@ def test_w8a8_rules(wqlib):
     assert qm(wqlib, x1, x2, D([2, 128], f32), out) == INVALID
     assert qm(wqlib, D([32, 0], i8, 0), D([0, 128], i8, 0), dq, out) == INVALID  # no empty tensors
     assert qm(wqlib, D([2, 16, 64], i8), x2, dq, D([2, 16, 128], bf), pt=D([32], f32)) == OK
+
+
+@pytest.mark.parametrize("out_dt,dq_dt,with_pt,want", [
+    # FLOAT16 output: FLOAT32 with a pertoken scale; without one the pages' packed
+    # INT64/UINT64 form, which FLOAT32 replaces here; never BFLOAT16
+    ("fp16", "fp32", True, "ok"), ("fp16", "fp32", False, "ok"),
+    ("fp16", "bf16", True, "invalid"), ("fp16", "bf16", False, "invalid"),
+    ("fp16", "fp16", True, "invalid"), ("fp16", "i32", False, "invalid"),
+    # BFLOAT16 output: BFLOAT16 (the pages' type) or FLOAT32 (the W8A8 workload's)
+    ("bf16", "bf16", True, "ok"), ("bf16", "bf16", False, "ok"),
+    ("bf16", "fp32", True, "ok"), ("bf16", "fp32", False, "ok"),
+    ("bf16", "fp16", False, "invalid"), ("bf16", "i32", True, "invalid"),
+])
+def test_w8a8_dequant_dtype_rule(wqlib, out_dt, dq_dt, with_pt, want):
+    """aclnnQuantMatmulAllReduceV2, Constraints: the dequant scale's dtype follows the output
+    dtype and the presence of a pertoken scale."""
+    code = {"fp16": W.WQ_F16, "bf16": W.WQ_BF16, "fp32": W.WQ_F32, "i32": W.WQ_I32}
+    i8 = W.WQ_I8
+    x1, x2 = D([32, 64], i8, FAKE + 0x10000), D([64, 128], i8, FAKE + 0x20000)
+    for dq_shape in ([1], [128], [1, 128]):
+        st = qm(wqlib, x1, x2, D(dq_shape, code[dq_dt], FAKE + 0x30000), D([32, 128], code[out_dt], FAKE + 0x40000),
+                pt=D([32], W.WQ_F32, FAKE + 0x50000) if with_pt else None)
+        assert st == (OK if want == "ok" else INVALID), (out_dt, dq_dt, with_pt, dq_shape, st)

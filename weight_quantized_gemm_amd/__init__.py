@@ -44,7 +44,7 @@ class WqTensor(ctypes.Structure):
                 ("shape", ctypes.c_int64 * 3), ("stride", ctypes.c_int64 * 3)]
 
 
-class WqError(Exception):
+class WqError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{message} (status {status})")
         self.status = status
@@ -152,6 +152,28 @@ def _stream_handle(stream, device) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+class _alloc_on:
+    """Context for a one-shot call: torch's current stream is the call's stream while the
+    call allocates and enqueues, so that its output and workspace belong to that stream (a
+    raw integer handle is wrapped as an external stream).  Yields the torch stream."""
+
+    def __init__(self, stream, device):
+        torch = _torch()
+        if stream is None:
+            stream = torch.cuda.current_stream(device)
+        elif isinstance(stream, int):
+            stream = torch.cuda.ExternalStream(stream, device=device)
+        self.stream = stream
+        self._ctx = torch.cuda.stream(stream)
+
+    def __enter__(self):
+        self._ctx.__enter__()
+        return self.stream
+
+    def __exit__(self, *exc):
+        return self._ctx.__exit__(*exc)
+
+
 def profile_next_call(before, after):
     """Arm the library's profiling hook: the next call on this thread records the torch
     events `before` / `after` (created with enable_timing=True and recorded once before, so
@@ -235,9 +257,13 @@ def antiquant_matmul(x1, x2, antiquant_scale, antiquant_offset=None, bias=None, 
     with a per-channel scale and no offset; scale/offset: (1), (n), (1, n) or (ceil(k/g), n)
     for group size g.  x2 may also be the transpose view ``w.t()`` of a row-major (n, k)
     tensor (int4: of an (n, k/2) tensor packed along k); per-group scale and offset are then
-    transpose views too.  Returns the output tensor."""
-    return AntiquantMatmul(x1, x2, antiquant_scale, antiquant_offset, bias, x3, antiquant_group_size,
-                           x2_int4=x2_int4, out=out, workspace=workspace)(stream)
+    transpose views too.  The output and the workspace (unless given) are allocated on the
+    stream the call runs on (`stream`, default torch's current stream), so that torch's
+    allocator does not hand their memory to other work while the call's kernels may still
+    use it.  Returns the output tensor."""
+    with _alloc_on(stream, x1.device) as s:
+        return AntiquantMatmul(x1, x2, antiquant_scale, antiquant_offset, bias, x3, antiquant_group_size,
+                               x2_int4=x2_int4, out=out, workspace=workspace)(s)
 
 
 def quant_workspace_size(x1, x2, dequant_scale, pertoken_scale=None, bias=None, x3=None, *,
@@ -283,8 +309,10 @@ def quant_matmul(x1, x2, dequant_scale, pertoken_scale=None, bias=None, x3=None,
                  out_dtype=None, out=None, acc_out=None, stream=None):
     """out = dequant_scale * pertoken_scale * (x1 @ x2 + bias) + x3 on x1's device.
 
-    x1, x2 int8; bias int32 (n); dequant_scale fp32/bf16 (1), (n) or (1, n); pertoken_scale
-    fp32 (m); x3 and the output fp16/bf16.  ``acc_out`` (int32, (m, n)) receives
-    x1 @ x2 + bias."""
-    return QuantMatmul(x1, x2, dequant_scale, pertoken_scale, bias, x3, out_dtype=out_dtype, out=out,
-                       acc_out=acc_out)(stream)
+    x1, x2 int8; bias int32 (n); dequant_scale (1), (n) or (1, n), fp32 (fp16 output) or
+    bf16/fp32 (bf16 output); pertoken_scale fp32 (m); x3 and the output fp16/bf16.
+    ``acc_out`` (int32, (m, n)) receives x1 @ x2 + bias.  The output and the workspace are
+    allocated on the stream the call runs on (`stream`, default torch's current stream)."""
+    with _alloc_on(stream, x1.device) as s:
+        return QuantMatmul(x1, x2, dequant_scale, pertoken_scale, bias, x3, out_dtype=out_dtype, out=out,
+                           acc_out=acc_out)(s)

@@ -618,35 +618,28 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   const int splits = a.splits > 1 ? a.splits : 1;
-  if ((e = profile_begin(stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)splits), dim3(T::Threads), lds, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = profile_end(stream)) != hipSuccess) return e;
+  e = launch_main((const void*)kern, dim3((unsigned)blocks, (unsigned)splits), dim3(T::Threads), lds, stream, &a);
+  if (e != hipSuccess) return e;
   return splits > 1 ? launch_aq_splitk_finish(a, stream) : hipSuccess;
 }
 
 // Tile configurations (wave grid GM x GN, blocks per wave WM x WN).  The matrix cores and
 // the VALU hardly overlap on gfx950, and one wave per SIMD leaves LDS latency exposed, so
-// the defaults run two waves per SIMD.  Per-group tiles are wide in n and short in m: the
-// x1 tile (16-bit) costs more load bandwidth per MFMA than the packed weights, and the
-// per-group accumulators (current group + folded total) leave room for 64x64 wave tiles
-// only.  Index 0 is the default of each mode; the others are kept for tuning.
-//   per-tensor / per-channel: 0: 2x4 waves of 128x64 (256x256)   1: 1x8 of 256x32 (int8)
-//                             2: 4x2 of 64x128
-//   per-group:                0: 2x4 waves of 64x64 (128x256)   1: 4x2 of 64x64 (256x128)
-//                             2: 8x1 of 32x64 (int8)
-// Index 0 with the planner's shorter tiles: 2x4 waves of 32x64 (64x256) at 64 rows, and
-// per-tensor / per-channel 2x4 waves of 64x64 (128x256) at 128 rows.
+// every configuration runs two waves per SIMD.  Per-group tiles are wide in n and short in
+// m: the x1 tile (16-bit) costs more load bandwidth per MFMA than the packed weights, and
+// the per-group accumulators (current group + folded total) leave room for 64x64 wave
+// tiles only.
+//   per-tensor / per-channel: 2x4 waves of 128x64 (256x256)
+//   per-group:                2x4 waves of 64x64 (128x256)
+// The planner's shorter tiles (aq_gemm_tile_m: short m, or short split chunks): 2x4 waves
+// of 32x64 (64x256) at 64 rows in every mode, and per-tensor / per-channel 2x4 waves of
+// 64x64 (128x256) at 128 rows.
 template <bool BF16, int WF>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
-  constexpr bool W4 = WF == kWInt4;
-  // Short m computes fewer padding rows on shorter tiles, and short split chunks run on more
-  // workgroups; the planner's tile rows (aq_gemm_tile_m) select them: 64 rows take 2x4 waves
-  // of 32x64 (64x256) in every mode, and 128 rows per-tensor / per-channel the 2x4 waves of
-  // 64x64 (128x256).
   const bool tiny_m = a.bm == 64, short_m = a.bm == 128;
-  if (a.x2t) {  // transposed weights: the default tile of each mode
-    if constexpr (WF != kWFp8) {
+  constexpr bool kGroupedOk = WF != kWFp8;  // FLOAT8_E4M3FN weights come per-channel only
+  if (a.x2t) {  // transposed weights
+    if constexpr (kGroupedOk) {
       if (a.grouped) {
         if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true, true>(a, stream);
         return launch_one<BF16, WF, 2, 4, 2, 2, true, true>(a, stream);
@@ -656,29 +649,15 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
     if (short_m) return launch_one<BF16, WF, 2, 4, 2, 2, false, true>(a, stream);
     return launch_one<BF16, WF, 2, 4, 4, 2, false, true>(a, stream);
   }
-  if constexpr (WF != kWFp8) {  // FLOAT8_E4M3FN weights come per-channel only
+  if constexpr (kGroupedOk) {
     if (a.grouped) {
-      switch (a.tile) {
-        case 1: return launch_one<BF16, WF, 4, 2, 2, 2, true>(a, stream);
-        case 2:
-          if constexpr (!W4) return launch_one<BF16, WF, 8, 1, 1, 2, true>(a, stream);
-          else return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
-        default:
-          if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true>(a, stream);
-          return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
-      }
+      if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true>(a, stream);
+      return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
     }
   }
-  switch (a.tile) {
-    case 1:
-      if constexpr (!W4) return launch_one<BF16, WF, 1, 8, 8, 1, false>(a, stream);
-      else return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
-    case 2: return launch_one<BF16, WF, 4, 2, 2, 4, false>(a, stream);
-    default:
-      if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, false>(a, stream);
-      if (short_m) return launch_one<BF16, WF, 2, 4, 2, 2, false>(a, stream);
-      return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
-  }
+  if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, false>(a, stream);
+  if (short_m) return launch_one<BF16, WF, 2, 4, 2, 2, false>(a, stream);
+  return launch_one<BF16, WF, 2, 4, 4, 2, false>(a, stream);
 }
 
 }  // namespace

@@ -13,10 +13,12 @@ namespace {
 
 // out = bias + x3 (either may be absent); one 16-bit element per thread, grid-stride.
 template <bool BF16>
-__global__ __launch_bounds__(256) void bias_x3_kernel(const uint16_t* __restrict__ bias,
-                                                      const uint16_t* __restrict__ x3,
-                                                      uint16_t* __restrict__ out, int64_t m, int n) {
-  const int64_t total = m * n;
+__global__ __launch_bounds__(256) void bias_x3_kernel(const AqArgs a) {
+  const uint16_t* __restrict__ bias = (const uint16_t*)a.bias;
+  const uint16_t* __restrict__ x3 = (const uint16_t*)a.x3;
+  uint16_t* __restrict__ out = (uint16_t*)a.out;
+  const int n = a.n;
+  const int64_t total = a.m * n;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     float v = 0.f;
@@ -133,16 +135,9 @@ hipError_t launch_transpose16(const void* src0, void* dst0, const void* src1, vo
 hipError_t launch_aq_bias_x3(const AqArgs& a, hipStream_t stream) {
   const int64_t total = a.m * a.n;
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 65536));
-  hipError_t e = profile_begin(stream);
-  if (e != hipSuccess) return e;
-  if (a.bf16)
-    hipLaunchKernelGGL(bias_x3_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)a.bias, (const uint16_t*)a.x3, (uint16_t*)a.out, a.m, a.n);
-  else
-    hipLaunchKernelGGL(bias_x3_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)a.bias, (const uint16_t*)a.x3, (uint16_t*)a.out, a.m, a.n);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  return profile_end(stream);
+  AqArgs args = a;
+  return launch_main(a.bf16 ? (const void*)bias_x3_kernel<true> : (const void*)bias_x3_kernel<false>,
+                     dim3((unsigned)blocks), dim3(256), 0, stream, &args);
 }
 
 }  // namespace wq

@@ -25,10 +25,10 @@
 namespace wq {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = kSmWaves;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSlab = 128;    // logical columns per workgroup
-constexpr int kRows = 64;     // k rows per block, a wave's unit of work
+constexpr int kSlab = kSmSlab;  // logical columns per workgroup
+constexpr int kRows = kSmRows;  // k rows per block, a wave's unit of work
 
 template <bool W4, bool GROUPED>
 struct SmTile {
@@ -445,10 +445,9 @@ hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
   auto kern = a.x2t ? aq_smallm_kernel<BF16, WF, GROUPED, true> : aq_smallm_kernel<BF16, WF, GROUPED, false>;
   hipError_t e = raise_lds_limit((const void*)kern, T::Lds);
   if (e != hipSuccess) return e;
-  if ((e = profile_begin(stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(slabs, a.splits), dim3(kThreads), (size_t)T::Lds, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = profile_end(stream)) != hipSuccess) return e;
+  AqArgs args = a;
+  e = launch_main((const void*)kern, dim3(slabs, a.splits), dim3(kThreads), (size_t)T::Lds, stream, &args);
+  if (e != hipSuccess) return e;
   if (a.splits == 1) return hipSuccess;  // the kernel wrote the output
   return launch_aq_splitk_finish(a, stream);
 }
@@ -462,28 +461,6 @@ hipError_t launch_aq_splitk_finish(const AqArgs& a, hipStream_t stream) {
                      : (a.grouped ? aq_splitk_finish<false, true> : aq_splitk_finish<false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
-}
-
-SplitPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped) {
-  (void)m; (void)group; (void)grouped;
-  SplitPlan p;
-  // A split costs a second launch and a pass over the partials: none for k <= 1024 (a
-  // slab's rows then stream in a few microseconds), and otherwise at least one 64-row block
-  // per wave (512 k) in each split.  At k = n = 1024 this took 10.5 us down to 7.6 us, and
-  // at k = 4096, n = 256 (64 splits of 64 k before) 18.9 us down to 9.3 us.
-  if (k <= 1024) {
-    p.kchunk = std::max(kRows, (k + kRows - 1) / kRows * kRows);
-    p.splits = 1;
-    return p;
-  }
-  const int slabs = (n + kSlab - 1) / kSlab;
-  const int want = std::max(1, 256 / std::max(1, slabs));  // about one workgroup per CU
-  // whole multiples of kWaves blocks per split (every wave gets a block: balance)
-  const int per = (k + want - 1) / want;
-  constexpr int step = kWaves * kRows;
-  p.kchunk = std::max(step, (per + step - 1) / step * step);
-  p.splits = std::max(1, (k + p.kchunk - 1) / p.kchunk);
-  return p;
 }
 
 hipError_t launch_aq_smallm(const AqArgs& a, hipStream_t stream) {

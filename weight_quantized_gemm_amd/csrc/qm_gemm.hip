@@ -390,13 +390,11 @@ __global__ __launch_bounds__(256) void qm_splitk_finish(const QmArgs a) {
 
 hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   QmArgs a = a0;
-  // default: 2 x 4 waves of 128 x 64 (two per SIMD), a 256 x 256 tile, or with the
-  // planner's shorter tile rows (qm_gemm_tile_m: short m, or short split chunks) 2 x 4 waves
-  // of 64 x 64, a 128 x 256 tile, or 2 x 2 waves of 32 x 128, a 64 x 256 tile (its x1 stage
-  // is one 16-row block per wave; its 80 KiB of LDS let two workgroups share a CU); tuning
-  // tile 1: 2 x 2 waves of 128 x 128 (row-major x2 only)
-  const bool t1 = a.tile == 1 && !a.x2t;
-  const int bm = t1 ? 256 : a.bm;
+  // 2 x 4 waves of 128 x 64 (two per SIMD), a 256 x 256 tile, or with the planner's shorter
+  // tile rows (qm_gemm_tile_m: short m, or short split chunks) 2 x 4 waves of 64 x 64, a
+  // 128 x 256 tile, or 2 x 2 waves of 32 x 128, a 64 x 256 tile (its x1 stage is one 16-row
+  // block per wave; its 80 KiB of LDS let two workgroups share a CU)
+  const int bm = a.bm;
   a.tiles_m = (int)((a.m + bm - 1) / bm);
   a.tiles_n = (a.n + kBN - 1) / kBN;
   void (*kern)(const QmArgs);
@@ -408,18 +406,15 @@ hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
                  : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false, 128> : qm_gemm_kernel<false, 2, 4, false, 128>);
   else
     kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, true> : qm_gemm_kernel<false, 2, 4, true>)
-           : t1  ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, false> : qm_gemm_kernel<false, 2, 2, false>)
                  : (a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false> : qm_gemm_kernel<false, 2, 4, false>);
-  const int threads = (t1 || bm == 64) ? 256 : 512;
+  const int threads = bm == 64 ? 256 : 512;
   const int kLds = bm == 64 ? qm_lds<64>() : bm == 128 ? qm_lds<128>() : qm_lds<256>();
   hipError_t e = raise_lds_limit((const void*)kern, kLds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   const int splits = a.splits > 1 ? a.splits : 1;
-  if ((e = profile_begin(stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)splits), dim3(threads), (size_t)kLds, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = profile_end(stream)) != hipSuccess) return e;
+  e = launch_main((const void*)kern, dim3((unsigned)blocks, (unsigned)splits), dim3(threads), (size_t)kLds, stream, &a);
+  if (e != hipSuccess) return e;
   if (splits == 1) return hipSuccess;
   const int64_t quads = a.m * (a.n / 4);
   const int64_t fblocks = std::max<int64_t>(1, std::min<int64_t>((quads + 255) / 256, 8192));

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "wq_plan.h"
+
 namespace wq {
 
 // Anti-quant matmul.  All 16-bit tensors are fp16 or bf16 bit patterns (act dtype).
@@ -24,7 +26,6 @@ struct AqArgs {
   int32_t splits;        // k splits (1: the main kernel writes the output)
   int32_t kchunk;        // k rows per split (a multiple of 64; per-group large m: of the group too)
   int32_t tiles_m, tiles_n;
-  int32_t tile;          // tile configuration index (0 = default)
   int32_t bm;            // tile rows of the default configuration (aq_gemm_tile_m)
   float code_bias;       // C: the fed weight image is code + C
   bool bf16, w4, f8, grouped, per_tensor;  // f8: FLOAT8_E4M3FN weights
@@ -47,7 +48,6 @@ struct QmArgs {
   int32_t splits;        // k splits (1: the main kernel writes the output)
   int32_t kchunk;        // k rows per split (a multiple of 64)
   int32_t tiles_m, tiles_n;
-  int32_t tile;          // tile configuration index (0 = default)
   int32_t bm;            // tile rows of the default configuration (qm_gemm_tile_m)
   bool out_bf16, dq_bf16, dq_per_tensor;
   bool x2t;              // x2 stored transposed, (n, k)
@@ -56,10 +56,11 @@ struct QmArgs {
 // Raise a kernel's dynamic LDS limit; done once per (kernel, device, size) in a process.
 hipError_t raise_lds_limit(const void* kernel, int bytes);
 
-// Profiling hook (wq_profile_next_call): record the armed events on `stream` right before
-// and right after the launch of a call's main kernel; profile_end disarms the hook.
-hipError_t profile_begin(hipStream_t stream);
-hipError_t profile_end(hipStream_t stream);
+// Launch a call's main kernel, whose one argument is the block at `args`.  When
+// wq_profile_next_call has armed two events on this host thread, they are passed with the
+// launch (hipExtLaunchKernel), so that they take the kernel's own start and end, and the
+// hook is disarmed.
+hipError_t launch_main(const void* kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream, void* args);
 
 // large-m kernels, one translation unit per weight format
 hipError_t launch_aq_gemm_int8(const AqArgs& a, hipStream_t stream);
@@ -80,20 +81,5 @@ hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream);
 hipError_t launch_transpose16(const void* src0, void* dst0, const void* src1, void* dst1, int rows,
                               int cols, hipStream_t stream);
 hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);
-
-// Split-k plans, shared by the planners (workspace sizes) and the launches.
-struct SplitPlan {
-  int kchunk = 64;   // k rows per split (a multiple of 64)
-  int splits = 1;
-};
-SplitPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped);
-// Large m: the workgroup tile the default configuration uses, and the k splits that bring
-// the workgroup count up to about one per CU when the tiles alone leave CUs idle.
-int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped);
-constexpr int kAqTileN = 256;
-SplitPlan gemm_split_plan(int64_t tiles, int k, int unit);
-// W8A8: the workgroup tile rows of the default configuration (64, 128 or 256)
-int qm_gemm_tile_m(int64_t m, int k, int n);
-constexpr int kQmTileN = 256;
 
 }  // namespace wq

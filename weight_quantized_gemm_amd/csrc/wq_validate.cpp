@@ -215,6 +215,10 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
   if (output->dtype != WQ_F16 && output->dtype != WQ_BF16) return WQ_ERR_PARAM_INVALID;
   if (x3 && x3->dtype != output->dtype) return WQ_ERR_PARAM_INVALID;
   if (dq->dtype != WQ_F32 && dq->dtype != WQ_BF16) return WQ_ERR_PARAM_INVALID;
+  // an FLOAT16 output takes an FLOAT32 dequant scale: with a pertoken scale the pages ask for
+  // FLOAT32; without one they ask for the packed INT64/UINT64 form, which this library does
+  // not take, and FLOAT32 stands in for it ("aclnnQuantMatmulAllReduceV2", Constraints)
+  if (output->dtype == WQ_F16 && dq->dtype != WQ_F32) return WQ_ERR_PARAM_INVALID;
   if (pt && pt->dtype != WQ_F32) return WQ_ERR_PARAM_INVALID;
   if (acc_out && acc_out->dtype != WQ_I32) return WQ_ERR_PARAM_INVALID;
 
