@@ -166,7 +166,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   const int wm = wave / GN;
   constexpr int wn = WNI;
   int tm, tn;
-  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, a.xcd_rm, tm, tn);
   const int64_t m0 = (int64_t)tm * T::BM;
   const int n0 = tn * BN;
   const int64_t M = a.m;
@@ -612,6 +612,9 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   AqArgs a = a0;
   a.tiles_m = (int)((a.m + T::BM - 1) / T::BM);
   a.tiles_n = (a.n + T::BN - 1) / T::BN;
+  // operand bytes per tile row (x1) and per tile column (weights) over the k range
+  a.xcd_rm = xcd_region_rows(a.tiles_m, a.tiles_n, (double)T::BM * a.kchunk * 2.0,
+                             (double)T::BN * a.kchunk * (WF == kWInt4 ? 0.5 : 1.0));
   const size_t lds = (size_t)T::Total;
   auto kern = aq_gemm_kernel<BF16, WF, GM, GN, WM, WN, GROUPED, XT>;
   hipError_t e = raise_lds_limit((const void*)kern, (int)lds);

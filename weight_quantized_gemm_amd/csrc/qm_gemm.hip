@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kGN, wn = wave % kGN;
   int tm, tn;
-  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, a.xcd_rm, tm, tn);
   const int64_t m0 = (int64_t)tm * kBM;
   const int n0 = tn * kBN;
   const int64_t M = a.m;
@@ -397,6 +397,7 @@ hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   const int bm = a.bm;
   a.tiles_m = (int)((a.m + bm - 1) / bm);
   a.tiles_n = (a.n + kBN - 1) / kBN;
+  a.xcd_rm = xcd_region_rows(a.tiles_m, a.tiles_n, (double)bm * a.kchunk, (double)kBN * a.kchunk);
   void (*kern)(const QmArgs);
   if (bm == 64)
     kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, true, 64> : qm_gemm_kernel<false, 2, 2, true, 64>)

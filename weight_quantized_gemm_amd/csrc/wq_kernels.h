@@ -26,6 +26,7 @@ struct AqArgs {
   int32_t splits;        // k splits (1: the main kernel writes the output)
   int32_t kchunk;        // k rows per split (a multiple of 64; per-group large m: of the group too)
   int32_t tiles_m, tiles_n;
+  int32_t xcd_rm;        // rows of the per-XCD rectangle grid (xcd_region_rows), 0: bands
   int32_t bm;            // tile rows of the default configuration (aq_gemm_tile_m)
   float code_bias;       // C: the fed weight image is code + C
   bool bf16, w4, f8, grouped, per_tensor;  // f8: FLOAT8_E4M3FN weights
@@ -48,6 +49,7 @@ struct QmArgs {
   int32_t splits;        // k splits (1: the main kernel writes the output)
   int32_t kchunk;        // k rows per split (a multiple of 64)
   int32_t tiles_m, tiles_n;
+  int32_t xcd_rm;        // rows of the per-XCD rectangle grid (xcd_region_rows), 0: bands
   int32_t bm;            // tile rows of the default configuration (qm_gemm_tile_m)
   bool out_bf16, dq_bf16, dq_per_tensor;
   bool x2t;              // x2 stored transposed, (n, k)

@@ -6,13 +6,28 @@
 namespace wq {
 
 // Map a linear workgroup id to a tile.  Workgroups are dispatched round-robin over the 8
-// XCDs; consecutive tile ids are handed to one XCD so that its L2 sees a compact band of
-// rows and columns, and inside the band tiles are walked in groups of 4 m-tiles.
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+// XCDs, each with its own L2.  With rm > 0 (xcd_region_rows) the tile grid is cut into an
+// rm x (8 / rm) grid of equal rectangles, one per XCD, so that each L2 sees the x1 rows and
+// weight columns of one rectangle only; otherwise each XCD takes a contiguous band of tile
+// ids.  Inside its share an XCD walks groups of 4 m-tiles, column by column, so that the
+// tiles running at once on its CUs share both their x1 rows and their weight columns.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int rm, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
+  constexpr int kGroupM = 4;
+  if (rm > 0 && (total & 7) == 0) {
+    const int rn = 8 / rm;
+    const int Rm = tiles_m / rm, Rn = tiles_n / rn;   // rectangle size in tiles
+    const int x = bid & 7, t = bid >> 3;              // XCD, index within its rectangle
+    const int per_group = kGroupM * Rn;
+    const int g = t / per_group;
+    const int gm = min(Rm - g * kGroupM, kGroupM);
+    const int r = t - g * per_group;
+    tm = (x / rn) * Rm + g * kGroupM + r % gm;
+    tn = (x % rn) * Rn + r / gm;
+    return;
+  }
   int t = bid;
   if ((total & 7) == 0) t = (bid & 7) * (total >> 3) + (bid >> 3);
-  constexpr int kGroupM = 4;
   const int per_group = kGroupM * tiles_n;
   const int g = t / per_group;
   const int first_m = g * kGroupM;

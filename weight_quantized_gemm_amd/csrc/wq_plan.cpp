@@ -60,6 +60,21 @@ int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 static_assert(kAqTileN == kQmTileN, "both tiled kernels' tiles are equally wide");
 
+int xcd_region_rows(int64_t tiles_m, int64_t tiles_n, double mtile_bytes, double ntile_bytes) {
+  int best = 0;
+  double best_bytes = 0;
+  for (int rm = 8; rm >= 1; rm /= 2) {  // taller rectangles first: they win ties
+    const int rn = 8 / rm;
+    if (tiles_m % rm != 0 || tiles_n % rn != 0) continue;
+    const double bytes = (double)(tiles_m / rm) * mtile_bytes + (double)(tiles_n / rn) * ntile_bytes;
+    if (best == 0 || bytes < best_bytes) {
+      best = rm;
+      best_bytes = bytes;
+    }
+  }
+  return best;
+}
+
 // The anti-quant kernel: tallest tiles of 256 rows per-tensor / per-channel, 128 per-group.
 int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped, int cus) {
   return tile_rows(m, k, n, grouped ? 128 : 256, cus);

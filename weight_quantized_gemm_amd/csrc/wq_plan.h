@@ -34,6 +34,13 @@ SplitPlan gemm_split_plan(int64_t tiles, int k, int unit, int cus);
 int aq_gemm_tile_m(int64_t m, int k, int n, bool grouped, int cus);
 int qm_gemm_tile_m(int64_t m, int k, int n, int cus);
 
+// Per-XCD tile rectangles: the tile grid (tiles_m x tiles_n, 8 XCDs) is cut into an
+// rm x (8 / rm) grid of equal rectangles, rm in {1, 2, 4, 8}, the one whose rectangle needs
+// the fewest operand bytes (rectangle rows x mtile_bytes + columns x ntile_bytes; ties go
+// to the taller rectangle).  0 when no rm divides the grid evenly (the kernels then hand
+// each XCD a band of consecutive tiles).
+int xcd_region_rows(int64_t tiles_m, int64_t tiles_n, double mtile_bytes, double ntile_bytes);
+
 struct AqPlan {
   bool empty_k = false;
   bool small_m = false;
