@@ -83,6 +83,7 @@ typedef struct wq_tensor {
 #define WQ_ERR_PARAM_NULLPTR 161001 /* a required input/output or its data pointer is NULL */
 #define WQ_ERR_PARAM_INVALID 161002 /* dtype, attribute, shape, layout or workspace rule broken */
 #define WQ_ERR_RUNTIME 561001       /* a HIP runtime or kernel-launch failure (library's own code) */
+#define WQ_ERR_SCRATCH_LIMIT 561002 /* the call needs more workspace than WQ_NOALLOC_SCRATCH_BYTES */
 
 /*
  * Workspace size of wq_antiquant_matmul for these arguments, written to *workspace_size.
@@ -140,6 +141,26 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
                         const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,
                         const wq_tensor* x3, int64_t antiquant_group_size, const wq_tensor* output,
                         void* workspace, uint64_t workspace_size, void* stream);
+
+/*
+ * wq_antiquant_matmul for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments and
+ * checks, without a workspace argument.  The workspace is a fixed scratch area inside the
+ * library, WQ_NOALLOC_SCRATCH_BYTES per device, held by each device the library runs on
+ * until the process ends; its device address is looked up on the first call on a device.
+ * The call allocates nothing.
+ * A call whose workspace (wq_antiquant_matmul_get_workspace_size) exceeds the scratch area
+ * returns WQ_ERR_SCRATCH_LIMIT and enqueues nothing.  Every call on a device shares that
+ * device's scratch area: calls that overlap on one device (other streams, other host
+ * threads) race and must be ordered by the caller.  Nothing in the area needs to be zero on
+ * entry; it keeps the last call's contents.  Returns WQ_ERR_RUNTIME if the scratch lookup or
+ * a launch fails.
+ */
+#define WQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+int wq_antiquant_matmul_noalloc(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
+                                const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,
+                                const wq_tensor* x3, int64_t antiquant_group_size, const wq_tensor* output,
+                                void* stream);
 
 /*
  * Workspace size of wq_quant_matmul (the W8A8 sibling).

@@ -23,15 +23,18 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["WQ_F16", "WQ_BF16", "WQ_F32", "WQ_I8", "WQ_I4", "WQ_I32", "WQ_F8E4M3", "WQ_OK",
-           "WQ_ERR_PARAM_NULLPTR", "WQ_ERR_PARAM_INVALID", "WQ_ERR_RUNTIME", "WqTensor",
+           "WQ_ERR_PARAM_NULLPTR", "WQ_ERR_PARAM_INVALID", "WQ_ERR_RUNTIME", "WQ_ERR_SCRATCH_LIMIT",
+           "WQ_NOALLOC_SCRATCH_BYTES", "WqTensor",
            "WqError", "lib", "library_path", "make_desc", "antiquant_matmul",
            "antiquant_workspace_size", "quant_matmul", "quant_workspace_size", "AntiquantMatmul",
            "QuantMatmul", "profile_next_call", "EXPORTS"]
 
 WQ_F16, WQ_BF16, WQ_F32, WQ_I8, WQ_I4, WQ_I32, WQ_F8E4M3 = 1, 2, 3, 4, 5, 6, 7
 WQ_OK, WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID, WQ_ERR_RUNTIME = 0, 161001, 161002, 561001
+WQ_ERR_SCRATCH_LIMIT = 561002
+WQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
-EXPORTS = ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul",
+EXPORTS = ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul", "wq_antiquant_matmul_noalloc",
            "wq_quant_matmul_get_workspace_size", "wq_quant_matmul", "wq_profile_next_call",
            "wq_status_string", "wq_version")
 
@@ -66,10 +69,11 @@ def lib():
         L.wq_antiquant_matmul_get_workspace_size.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, u64p]
         L.wq_antiquant_matmul.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_void_p,
                                           ctypes.c_uint64, ctypes.c_void_p]
+        L.wq_antiquant_matmul_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_void_p]
         L.wq_quant_matmul_get_workspace_size.argtypes = [P, P, P, P, P, P, P, P, u64p]
         L.wq_quant_matmul.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_void_p, ctypes.c_uint64,
                                       ctypes.c_void_p]
-        for f in ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul",
+        for f in ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul", "wq_antiquant_matmul_noalloc",
                   "wq_quant_matmul_get_workspace_size", "wq_quant_matmul"):
             getattr(L, f).restype = ctypes.c_int
         L.wq_profile_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]

@@ -21,7 +21,7 @@ LIB_NAME = "libwqgemm.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["aq_gemm_int8.hip", "aq_gemm_int4.hip", "aq_gemm_fp8.hip", "qm_gemm.hip",
-           "aq_smallm.hip", "aq_prep.hip", "wq_validate.cpp", "wq_plan.cpp", "wq_api.cpp"]
+           "aq_smallm.hip", "aq_prep.hip", "wq_noalloc.hip", "wq_validate.cpp", "wq_plan.cpp", "wq_api.cpp"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -179,6 +179,9 @@ const char* wq_status_string(int status) {
     case WQ_ERR_PARAM_NULLPTR: return "WQ_ERR_PARAM_NULLPTR: a required argument is a null pointer";
     case WQ_ERR_PARAM_INVALID: return "WQ_ERR_PARAM_INVALID: an argument breaks a dtype, attribute, shape, layout or workspace rule";
     case WQ_ERR_RUNTIME: return "WQ_ERR_RUNTIME: a HIP runtime call or kernel launch failed";
+    case WQ_ERR_SCRATCH_LIMIT:
+      return "WQ_ERR_SCRATCH_LIMIT: the call needs more workspace than the no-allocation entry point's "
+             "scratch area (WQ_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
   }
 }
