@@ -79,8 +79,10 @@ def to_dev(a, kind, torch, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def make_runner(case, torch, dev, sets):
-    """Device-resident input sets and one prepared call per set."""
+def make_runner(case, torch, dev, sets, packed=False):
+    """Device-resident input sets and one prepared call per set.  With `packed`, each set's
+    weight is converted once to the packed layout (wq_prepack_weight) before any timing, as
+    an offline weight conversion would be."""
     import weight_quantized_gemm_amd as W
     calls, bufs = [], []
     if isinstance(case, workloads.AntiquantCase):
@@ -92,6 +94,8 @@ def make_runner(case, torch, dev, sets):
             x2 = to_dev(case.x2, "raw", torch, dev)
             if case.weight == "fp8e4m3":
                 x2 = x2.view(torch.float8_e4m3fn)
+            if packed:
+                x2 = W.prepack_weight(x2, x2_int4=int4)
             b = dict(x1=to_dev(case.x1, act, torch, dev), x2=x2,
                      scale=to_dev(case.scale, act, torch, dev), offset=to_dev(case.offset, act, torch, dev),
                      bias=to_dev(case.bias, act, torch, dev), x3=to_dev(case.x3, act, torch, dev))
@@ -199,7 +203,8 @@ def bench_one(name, args, torch, dev):
     case = workloads.make_workload(name)
     abytes = algorithmic_bytes(case)
     sets = max(1, min(8, -(-2 * CACHE_BYTES // max(abytes, 1))))
-    calls, bufs = make_runner(case, torch, dev, sets)
+    packed = bool(getattr(args, "packed", False)) and isinstance(case, workloads.AntiquantCase)
+    calls, bufs = make_runner(case, torch, dev, sets, packed=packed)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     for i in range(args.warmup):
@@ -253,6 +258,7 @@ def bench_one(name, args, torch, dev):
         "data": "synthetic (seeded generators; inputs resident in HBM, rotated over "
                 f"{sets} sets to defeat the Infinity Cache)",
         "config": {"workload": name, "m": case.m, "k": case.k, "n": case.n,
+                   "weight_layout": "packed (wq_prepack_weight, outside the timed steps)" if packed else "ND",
                    "x1_shape": list(case.x1.shape), "seed": spec["seed"],
                    "algorithmic_bytes": abytes, "flops": flops,
                    "hbm_gbps": round(abytes / (ms_per_step / 1e3) / 1e9, 1),
@@ -291,6 +297,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", dest="cpu", action="store_false", help="skip the CPU oracle leg")
+    ap.add_argument("--packed", action="store_true",
+                    help="anti-quant workloads with their weights prepacked once before timing")
     ap.add_argument("--kernel-events", choices=("timed", "after"), default="timed",
                     help="where the main kernel's event pairs are taken: on the timed steps (default) "
                          "or on as many steps after them")

@@ -52,6 +52,12 @@ typedef enum wq_dtype {
   WQ_F8E4M3 = 7
 } wq_dtype;
 
+/* Layout flag, or-ed into the dtype of an anti-quant weight (WQ_I8, WQ_I4 or WQ_F8E4M3):
+ * the tensor holds the packed layout wq_prepack_weight writes (the role of the pages'
+ * FRACTAL_NZ weight format), not an ND array.  Its descriptor keeps the logical shape
+ * (k, n); its strides are not read. */
+#define WQ_PACKED 0x100
+
 /*
  * Tensor descriptor (the role of the pages' aclTensor).
  *   data    device address of the first element, 16-byte aligned (for an empty tensor it
@@ -91,7 +97,8 @@ typedef struct wq_tensor {
  * Arguments (guide, "aclnnWeightQuantMatmulAllReduceGetWorkspaceSize 参数详解" and
  * "约束说明 / 形状与范围约束" (shape constraints)):
  *   x1               required; WQ_F16 or WQ_BF16; (m, k) or (b, s, k); m = b*s in [1, 2^31-1].
- *   x2               required; WQ_I8, WQ_I4 or WQ_F8E4M3; (k, n); k in [0, 65535],
+ *   x2               required; WQ_I8, WQ_I4 or WQ_F8E4M3, alone or with WQ_PACKED (the
+ *                    output of wq_prepack_weight); (k, n); k in [0, 65535],
  *                    n in [1, 65535].  Alignment (guide, 950 format/alignment rules): int8
  *                    needs k and n multiples of 32, int4 multiples of 64 (k = 0 is allowed);
  *                    FLOAT8_E4M3FN, one byte per element like int8, multiples of 32.
@@ -161,6 +168,36 @@ int wq_antiquant_matmul_noalloc(const wq_tensor* x1, const wq_tensor* x2, const 
                                 const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,
                                 const wq_tensor* x3, int64_t antiquant_group_size, const wq_tensor* output,
                                 void* stream);
+
+/*
+ * Offline weight prepack, after the pages' two-call weight conversion
+ * ("aclnnQuantMatmulAllReduceV2", Parameters table, x2 in FRACTAL_NZ format, produced by
+ * aclnnCalculateMatmulWeightSizeV2 then aclnnTransMatmulWeight; guide,
+ * 产品相关的格式与对齐约束).  The packed layout is this library's, made for the gfx950
+ * matrix cores rather than the pages' NZ tiles:
+ *   the (k, n) weight is cut into blocks of 64 k x 32 columns, stored block row by block row
+ *   (k blocks outer, n blocks inner); a block holds, for each of its four 16-k steps s, the
+ *   64 lanes of an MFMA B fragment in lane order: lane l is column l % 32 and k
+ *   16 s + 8 (l / 32) + 0 .. 7, i.e. 8 codes, k ascending -- 8 bytes (int8, FLOAT8_E4M3FN)
+ *   or 4 bytes (int4: two nibbles a byte, the even k in bits 0-3).  Blocks are 2048 bytes
+ *   (1024 for int4); codes of k >= k (a final half block) are zero.
+ * Every B fragment the kernels need is then one contiguous run of bytes.
+ *
+ * wq_prepack_weight_get_size: the packed size in bytes of x2 (WQ_I8, WQ_I4 or WQ_F8E4M3,
+ * (k, n) with k in [1, 65535] and n in [1, 65535], the alignment rules of
+ * wq_antiquant_matmul; row-major or transposed as there), written to *packed_bytes.
+ * Touches no device.
+ *
+ * wq_prepack_weight: enqueue the relayout of x2 into `packed` on `stream`.  `packed` is a
+ * descriptor with dtype x2->dtype | WQ_PACKED, shape (k, n), data a caller-owned device
+ * buffer of at least the packed size, 16-byte aligned, not x2's.  The packed tensor can then
+ * be passed as x2 to wq_antiquant_matmul_get_workspace_size, wq_antiquant_matmul and
+ * wq_antiquant_matmul_noalloc; per-group scale and offset go with it row-major,
+ * (ceil(k / g), n).  Returns WQ_OK, WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID or
+ * WQ_ERR_RUNTIME.
+ */
+int wq_prepack_weight_get_size(const wq_tensor* x2, uint64_t* packed_bytes);
+int wq_prepack_weight(const wq_tensor* x2, const wq_tensor* packed, void* stream);
 
 /*
  * Workspace size of wq_quant_matmul (the W8A8 sibling).

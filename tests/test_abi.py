@@ -14,7 +14,7 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     assert names == sorted(["wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul",
-                            "wq_antiquant_matmul_noalloc",
+                            "wq_antiquant_matmul_noalloc", "wq_prepack_weight_get_size", "wq_prepack_weight",
                             "wq_quant_matmul_get_workspace_size", "wq_quant_matmul",
                             "wq_profile_next_call", "wq_status_string", "wq_version"])
 

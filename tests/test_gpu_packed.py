@@ -1,0 +1,153 @@
+"""GPU: the offline weight prepack (wq_prepack_weight) and the anti-quant calls on packed
+weights.
+
+The packed bytes must equal the NumPy restatement of the layout (tests/packing.py) bit for
+bit (byte work), from row-major and transposed weights of every code type, with a k tail.
+Matmuls on the packed weight must match the fp64 oracle evaluated on the original logical
+weight, to the usual tolerances (fp16 outputs 2e-3, bf16 1e-2, relative to max(1, |ref|)):
+the small-m kernel on packed weights (with and without k splits) and the tiled kernels'
+packed path (64-, 128- and 256-row tiles, split k), every mode and code type, and the
+full-size small-m workload.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import weight_quantized_gemm_amd as W
+from gpu_util import dev_tensor, ref_antiquant, to_f64
+from packing import logical_codes, pack_reference
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(name):
+    print(f"[gpu-case] {name}", flush=True)
+
+
+def _x2_dev(case):
+    x2 = dev_tensor(case.x2, "raw")
+    if case.weight == "fp8e4m3":
+        x2 = x2.view(torch.float8_e4m3fn)
+    return x2.t() if case.x2_transposed else x2
+
+
+@pytest.mark.parametrize("weight,k,n,xt", [
+    ("int8", 96, 64, False), ("int8", 256, 320, True), ("fp8e4m3", 160, 96, False),
+    ("fp8e4m3", 64, 32, True), ("int4", 192, 128, False), ("int4", 128, 192, True),
+], ids=lambda v: str(v))
+def test_prepack_bytes(weight, k, n, xt):
+    _announce(f"prepack_bytes_{weight}_{k}x{n}_{xt}")
+    case = workloads.make_antiquant(seed=k * 31 + n, act="bf16", weight=weight, x1_shape=(1, k), n=n,
+                                    mode="channel", with_offset=weight != "fp8e4m3", x2_transposed=xt)
+    pw = W.prepack_weight(_x2_dev(case), x2_int4=weight == "int4")
+    torch.cuda.synchronize()
+    got = pw.data.cpu().numpy()
+    want = pack_reference(logical_codes(case.x2, weight, xt), weight == "int4")
+    assert got.size == want.size == W.packed_weight_bytes(_x2_dev(case), x2_int4=weight == "int4")
+    assert np.array_equal(got, want)
+
+
+def check_packed(case):
+    _announce(f"packed:{case.name}")
+    act = case.act
+    pw = W.prepack_weight(_x2_dev(case), x2_int4=case.weight == "int4")
+    scale, offset = case.scale, case.offset
+    if case.x2_transposed and case.group_size:
+        # packed weights take row-major per-group parameters
+        scale = np.ascontiguousarray(scale.T)
+        offset = None if offset is None else np.ascontiguousarray(offset.T)
+    y = W.antiquant_matmul(dev_tensor(case.x1, act), pw, dev_tensor(scale, act), dev_tensor(offset, act),
+                           dev_tensor(case.bias, act), dev_tensor(case.x3, act), case.group_size)
+    got = to_f64(y).reshape(case.out_shape)
+    r = oracle.compare(got, ref_antiquant(case), act)
+    assert r["ok"], (case.name, r)
+
+
+PACKED_CASES = [
+    # small m (m <= 32): the column-block kernel; n < 4096 splits k
+    ("pk_sm_m1_perchannel_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(1, 2048), n=256, mode="channel")),
+    ("pk_sm_m7_pertensor_fp16_i8_ktail", dict(act="fp16", weight="int8", x1_shape=(7, 1056), n=96, mode="tensor")),
+    ("pk_sm_m32_pergroup64_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(32, 4096), n=512, mode="group",
+                                          group_size=64, offset_dist=("uniform", -4, 4), with_x3=False)),
+    ("pk_sm_m17_pergroup96_bf16_i8_partial", dict(act="bf16", weight="int8", x1_shape=(17, 1120), n=192,
+                                                  mode="group", group_size=96)),
+    ("pk_sm_m3_pergroup128_bf16_i4_3d", dict(act="bf16", weight="int4", x1_shape=(3, 1, 2048), n=256, mode="group",
+                                             group_size=128)),
+    ("pk_sm_m24_perchannel_fp16_i4_xt", dict(act="fp16", weight="int4", x1_shape=(24, 1024), n=384, mode="channel",
+                                             x2_transposed=True)),
+    ("pk_sm_m16_perchannel_bf16_f8", dict(act="bf16", weight="fp8e4m3", x1_shape=(16, 2048), n=320, mode="channel",
+                                          with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
+    ("pk_sm_m32_pergroup64_fp16_i8_xt_wide", dict(act="fp16", weight="int8", x1_shape=(32, 2048), n=8192,
+                                                  mode="group", group_size=64, x2_transposed=True)),
+    ("pk_sm_m5_pergroup32_bf16_i8_k96", dict(act="bf16", weight="int8", x1_shape=(5, 96), n=64, mode="group",
+                                             group_size=32)),
+    # large m: the tiled kernels' packed path (64-, 128-, 256-row tiles; split k; n edge; k tail)
+    ("pk_tl_m40_perchannel_bf16_i8_split", dict(act="bf16", weight="int8", x1_shape=(40, 2048), n=320,
+                                                mode="channel")),
+    ("pk_tl_m100_pergroup96_fp16_i8_split", dict(act="fp16", weight="int8", x1_shape=(100, 2304), n=384,
+                                                 mode="group", group_size=96, offset_dist=("uniform", -4, 4))),
+    ("pk_tl_m300_pertensor_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(300, 1024), n=320, mode="tensor")),
+    ("pk_tl_m600_perchannel_bf16_i8_ktail", dict(act="bf16", weight="int8", x1_shape=(600, 288), n=544,
+                                                 mode="channel")),
+    ("pk_tl_m1100_pergroup128_bf16_i4_3d", dict(act="bf16", weight="int4", x1_shape=(2, 550, 512), n=320,
+                                                mode="group", group_size=128, with_bias=False)),
+    ("pk_tl_m257_perchannel_fp16_f8_xt", dict(act="fp16", weight="fp8e4m3", x1_shape=(257, 320), n=288,
+                                              mode="channel", with_offset=False, scale_dist=("uniform", 2e-4, 1e-3),
+                                              x2_transposed=True)),
+    ("pk_tl_m200_pergroup64_bf16_i8_xt", dict(act="bf16", weight="int8", x1_shape=(200, 2048), n=256, mode="group",
+                                              group_size=64, x2_transposed=True)),
+    ("pk_tl_m1024_perchannel_fp16_i4", dict(act="fp16", weight="int4", x1_shape=(1024, 1024), n=1024,
+                                            mode="channel")),
+]
+
+
+@pytest.mark.parametrize("name,spec", PACKED_CASES, ids=[c[0] for c in PACKED_CASES])
+def test_packed_parity(name, spec):
+    case = workloads.make_antiquant(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec)
+    check_packed(case)
+
+
+@pytest.mark.parametrize("name", ["smallm_pergroup64_fp16_int8_32x8192x8192", "perchannel_bf16_int8_4096x4096x4096",
+                                  "pergroup128_bf16_int4_4x2048x8192x2048",
+                                  "smallm_perchannel_bf16_fp8e4m3_32x8192x8192"])
+def test_full_size_packed(name):
+    """Measured workloads with their weights prepacked: every output element."""
+    check_packed(workloads.make_workload(name))
+
+
+def test_packed_noalloc_and_graph():
+    """The packed small-m call through the no-allocation entry point equals the ordinary call
+    bit for bit, and replays from a HIP graph."""
+    import ctypes
+    _announce("packed_noalloc_graph")
+    case = workloads.make_antiquant(seed=77, name="pk_graph", act="fp16", weight="int8", x1_shape=(16, 2048),
+                                    n=256, mode="group", group_size=64)
+    act = case.act
+    pw = W.prepack_weight(_x2_dev(case))
+    t = [dev_tensor(case.x1, act), pw, dev_tensor(case.scale, act), dev_tensor(case.offset, act),
+         dev_tensor(case.bias, act), dev_tensor(case.x3, act)]
+    call = W.AntiquantMatmul(*t, case.group_size)
+    ref = call().clone()
+    out = torch.empty_like(ref)
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    descs = [W._desc(t[0]), pw.desc(), W._desc(t[4]), W._desc(t[2]), W._desc(t[3]), W._desc(t[5])]
+    st = W.lib().wq_antiquant_matmul_noalloc(*map(r, descs), case.group_size, r(W._desc(out)),
+                                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == W.WQ_OK
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        call.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out.view(torch.int16), ref.view(torch.int16))
+    res = oracle.compare(to_f64(ref).reshape(case.out_shape), ref_antiquant(case), act)
+    assert res["ok"], res

@@ -24,7 +24,8 @@ from typing import Optional, Sequence
 
 __all__ = ["WQ_F16", "WQ_BF16", "WQ_F32", "WQ_I8", "WQ_I4", "WQ_I32", "WQ_F8E4M3", "WQ_OK",
            "WQ_ERR_PARAM_NULLPTR", "WQ_ERR_PARAM_INVALID", "WQ_ERR_RUNTIME", "WQ_ERR_SCRATCH_LIMIT",
-           "WQ_NOALLOC_SCRATCH_BYTES", "WqTensor",
+           "WQ_NOALLOC_SCRATCH_BYTES", "WQ_PACKED", "WqTensor", "PackedWeight", "prepack_weight",
+           "packed_weight_bytes",
            "WqError", "lib", "library_path", "make_desc", "antiquant_matmul",
            "antiquant_workspace_size", "quant_matmul", "quant_workspace_size", "AntiquantMatmul",
            "QuantMatmul", "profile_next_call", "EXPORTS"]
@@ -32,9 +33,11 @@ __all__ = ["WQ_F16", "WQ_BF16", "WQ_F32", "WQ_I8", "WQ_I4", "WQ_I32", "WQ_F8E4M3
 WQ_F16, WQ_BF16, WQ_F32, WQ_I8, WQ_I4, WQ_I32, WQ_F8E4M3 = 1, 2, 3, 4, 5, 6, 7
 WQ_OK, WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID, WQ_ERR_RUNTIME = 0, 161001, 161002, 561001
 WQ_ERR_SCRATCH_LIMIT = 561002
+WQ_PACKED = 0x100
 WQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul", "wq_antiquant_matmul_noalloc",
+           "wq_prepack_weight_get_size", "wq_prepack_weight",
            "wq_quant_matmul_get_workspace_size", "wq_quant_matmul", "wq_profile_next_call",
            "wq_status_string", "wq_version")
 
@@ -76,6 +79,10 @@ def lib():
         for f in ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul", "wq_antiquant_matmul_noalloc",
                   "wq_quant_matmul_get_workspace_size", "wq_quant_matmul"):
             getattr(L, f).restype = ctypes.c_int
+        L.wq_prepack_weight_get_size.argtypes = [P, u64p]
+        L.wq_prepack_weight.argtypes = [P, P, ctypes.c_void_p]
+        L.wq_prepack_weight_get_size.restype = ctypes.c_int
+        L.wq_prepack_weight.restype = ctypes.c_int
         L.wq_profile_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.wq_profile_next_call.restype = ctypes.c_int
         L.wq_status_string.argtypes = [ctypes.c_int]
@@ -125,9 +132,53 @@ def _dtype_code(t) -> int:
     return m[t.dtype]
 
 
+class PackedWeight:
+    """A weight in the packed layout written by :func:`prepack_weight` (64 k x 32 column
+    blocks in MFMA B-fragment order, see include/wqgemm.h).  ``data`` is the uint8 device
+    tensor; ``k``, ``n`` the logical shape; ``dtype`` the WQ_* code of the codes (WQ_I8, WQ_I4
+    or WQ_F8E4M3).  Pass it as x2 to the anti-quant calls."""
+
+    def __init__(self, data, k: int, n: int, dtype: int):
+        self.data, self.k, self.n, self.dtype = data, int(k), int(n), int(dtype)
+
+    @property
+    def shape(self):
+        return (self.k, self.n)
+
+    def desc(self):
+        return make_desc([self.k, self.n], self.dtype | WQ_PACKED, self.data.data_ptr(), [0, 0])
+
+
+def packed_weight_bytes(x2, *, x2_int4: bool = False) -> int:
+    """Bytes of the packed layout of x2 (wq_prepack_weight_get_size)."""
+    size = ctypes.c_uint64(0)
+    _check(lib().wq_prepack_weight_get_size(ctypes.byref(_desc(x2, x2_int4)), ctypes.byref(size)))
+    return size.value
+
+
+def prepack_weight(x2, *, x2_int4: bool = False, out=None, stream=None) -> PackedWeight:
+    """Relayout a weight (int8 (k, n), packed int4 (k, n/2) bytes, or float8_e4m3fn (k, n);
+    row-major or the transpose view of a row-major (n, k) tensor) into the packed layout, on
+    `stream` (default torch's current stream).  Returns a :class:`PackedWeight`; `out`, if
+    given, is a uint8 device tensor of at least packed_weight_bytes(x2) bytes."""
+    torch = _torch()
+    d = _desc(x2, x2_int4)
+    size = packed_weight_bytes(x2, x2_int4=x2_int4)
+    with _alloc_on(stream, x2.device) as s:
+        if out is None:
+            out = torch.empty(max(size, 1), dtype=torch.uint8, device=x2.device)
+        elif out.numel() < size or out.dtype != torch.uint8:
+            raise ValueError(f"the packed weight needs a uint8 tensor of at least {size} bytes")
+        pw = PackedWeight(out, d.shape[0], d.shape[1], d.dtype)
+        _check(lib().wq_prepack_weight(ctypes.byref(d), ctypes.byref(pw.desc()), _stream_handle(s, x2.device)))
+    return pw
+
+
 def _desc(t, int4: bool = False):
     if t is None:
         return None
+    if isinstance(t, PackedWeight):
+        return t.desc()
     if int4:
         torch = _torch()
         if t.dtype not in (torch.uint8, torch.int8) or t.dim() != 2:
@@ -207,6 +258,8 @@ def _is_t_view(t) -> bool:
 
 def _weight_n(x2, x2_int4: bool) -> int:
     """Output columns n of a weight tensor (row-major int4 storage packs two columns a byte)."""
+    if isinstance(x2, PackedWeight):
+        return x2.n
     return x2.shape[1] * (2 if x2_int4 and not _is_t_view(x2) else 1)
 
 
@@ -261,7 +314,8 @@ def antiquant_matmul(x1, x2, antiquant_scale, antiquant_offset=None, bias=None, 
     with a per-channel scale and no offset; scale/offset: (1), (n), (1, n) or (ceil(k/g), n)
     for group size g.  x2 may also be the transpose view ``w.t()`` of a row-major (n, k)
     tensor (int4: of an (n, k/2) tensor packed along k); per-group scale and offset are then
-    transpose views too.  The output and the workspace (unless given) are allocated on the
+    transpose views too.  x2 may also be a :class:`PackedWeight` (prepack_weight), with
+    row-major per-group parameters.  The output and the workspace (unless given) are allocated on the
     stream the call runs on (`stream`, default torch's current stream), so that torch's
     allocator does not hand their memory to other work while the call's kernels may still
     use it.  Returns the output tensor."""

@@ -50,7 +50,9 @@ constexpr int kBK = 64;
 constexpr int kArow = 128;                 // bytes per x1 row in a stage (64 x 16-bit)
 
 // XT: the weights are stored transposed, (n, k) (int4: (n, k/2) bytes packed along k).
-template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false>
+// PK: the weights are in the packed layout (wq_prepack_weight): 64 k x 32 column blocks in
+// MFMA B-fragment order.
+template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false, bool PK = false>
 struct Tile {
   static constexpr int Waves = GM * GN;              // wave grid GM x GN
   static constexpr int Threads = 64 * Waves;
@@ -79,9 +81,13 @@ struct Tile {
   static constexpr int Pwave = Waves - 1;            // issues the group-parameter loads
   static constexpr int WCols = 32 * WN;              // logical columns per wave
   static constexpr bool XTile = XT;
+  static constexpr bool PKed = PK;
+  // packed weights: bytes of a 64 k x 32 column block, and of one lane's codes of a 16-k step
+  static constexpr int PkBlock = W4 ? 1024 : 2048;
+  static constexpr int PkLane = W4 ? 4 : 8;
   // B fragment reads per wave per 16-k step: tr8 reads (an int4 one feeds two blocks), or
   // one 8-byte (int4: 4-byte) read per block from transposed weights
-  static constexpr int Reads = (W4 && !XT) ? WN / 2 : WN;
+  static constexpr int Reads = (W4 && !XT && !PK) ? WN / 2 : WN;
   // LDS layout: stages (x1 | weights | group parameters | group row sums) | per-channel S
   // rows (BM fp32).  As many stages as fit (3 to 6): a deeper pipeline hides more load
   // latency where a stage is small.
@@ -95,7 +101,8 @@ struct Tile {
   static_assert(Ablocks % Waves == 0, "x1 DMA blocks split evenly over the waves");
   static_assert(Bblocks % Waves == 0 || Bblocks < Waves, "weight DMA blocks split");
   static_assert(Win >= 1 && Win <= 4, "weight row bytes 64..256");
-  static_assert(!W4 || XT || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
+  static_assert(!W4 || XT || PK || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
+  static_assert(!(XT && PK), "one weight layout");
 };
 
 // Stage barrier allowing `ahead` later stages (OWN loads each) to stay in flight, for a
@@ -130,6 +137,17 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
     const int c = 2 * kk + (lane >> 5);
     f.a[i] = *(const u32x4_t*)(As + r * kArow + 16 * row_slot<kArow>(r, c));
   }
+  if constexpr (T::PKed) {
+    // the stage holds the tile's 32-column blocks of one 64-k block side by side; the codes
+    // of 16-k step kk of block b are lane-ordered at b * PkBlock + kk * 64 * PkLane
+#pragma unroll
+    for (int j = 0; j < T::Reads; ++j) {
+      const uint8_t* p = Bs + (wn * T::Reads + j) * T::PkBlock + kk * 64 * T::PkLane + T::PkLane * lane;
+      if constexpr (T::PkLane == 8) f.raw[j] = *(const u32x2_t*)p;
+      else f.raw[j] = u32x2_t{*(const uint32_t*)p, 0u};
+    }
+    return;
+  }
   if constexpr (T::XTile) {
     // column row r holds the stage's k for one column, 16-byte chunks swizzled like x1
     // rows; lane half h = lane / 32 takes k 16 kk + 8 h .. + 7
@@ -157,10 +175,10 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
 
 // The kernel body, specialised on the wave's column index WNI in the GM x GN wave grid:
 // column offsets and the per-channel row-sum block become compile-time constants.
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT, int WNI>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT, bool PK, int WNI>
 __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int wave) {
   constexpr bool W4 = WF == kWInt4;
-  using T = Tile<W4, GM, GN, WM, WN, GROUPED, XT>;
+  using T = Tile<W4, GM, GN, WM, WN, GROUPED, XT, PK>;
   constexpr int BN = T::BN, RB = T::RB, WC = T::WCols;
   const int lane = threadIdx.x & 63;
   const int wm = wave / GN;
@@ -207,7 +225,10 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
 #pragma unroll
   for (int j = 0; j < T::Bper; ++j) {
     const int b = wave + T::Waves * j;
-    if constexpr (XT) {
+    if constexpr (PK) {                // the stage's blocks are one contiguous run
+      b_k[j] = 0;
+      b_off[j] = 1024u * (uint32_t)b + 16u * (uint32_t)lane;
+    } else if constexpr (XT) {
       constexpr int L = T::RowT / 16;  // 16-byte chunks per column row
       const int r = T::ColsPerKB * b + lane / L;
       const int c = row_slot<T::RowT>(r, lane % L);
@@ -250,7 +271,14 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     r.k0 = kbeg + ks * kBK;
     r.st = smem + (ks % T::Stages) * T::Stage;
     r.ra = make_rsrc32(x1b + (int64_t)r.k0 * 2, x1_bytes - (uint32_t)r.k0 * 2);
-    if constexpr (XT) {
+    if constexpr (PK) {
+      // the tile's column blocks of 64-k block k0 / 64; blocks past n read zero (the
+      // packed layout pads k past the end with zero codes)
+      const int nbl = N / 32, nbt = n0 / 32;
+      const int valid = nbl - nbt < BN / 32 ? nbl - nbt : BN / 32;
+      r.rb = make_rsrc((const uint8_t*)a.x2 + ((int64_t)(r.k0 / kBK) * nbl + nbt) * T::PkBlock,
+                       (int64_t)valid * T::PkBlock);
+    } else if constexpr (XT) {
       const uint32_t kb = W4 ? (uint32_t)r.k0 / 2 : (uint32_t)r.k0;
       r.rb = make_rsrc32(x2b + kb, x2t_bytes - kb);
     } else {
@@ -348,7 +376,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
 
   // logical column of lane's block j (int4: block 2p + e covers byte pair p, parity e)
   auto block_col = [&](int j) -> int {
-    if constexpr (W4 && !XT) return n0 + wn * WC + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
+    if constexpr (W4 && !XT && !PK) return n0 + wn * WC + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
     else return n0 + wn * WC + 32 * j + (lane & 31);
   };
 
@@ -453,7 +481,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       u32x4_t bfr[WN];
 #pragma unroll
       for (int j = 0; j < T::Reads; ++j) {
-        if constexpr (W4 && XT) bfr[j] = i4x8_k_to_act<BF16>(cur.raw[j][0]);
+        if constexpr (W4 && (XT || PK)) bfr[j] = i4x8_k_to_act<BF16>(cur.raw[j][0]);
         else if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
         else bfr[j] = w8x8_to_act<BF16, WF>(cur.raw[j]);
       }
@@ -588,7 +616,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   }
 }
 
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT, bool PK>
 __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
@@ -596,7 +624,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #define WQ_WAVE_COLUMN(c)                                                      \
   if constexpr (GN > c) {                                                     \
     if (wn == c) {                                                            \
-      aq_gemm_body<BF16, WF, GM, GN, WM, WN, GROUPED, XT, c>(a, smem, wave);   \
+      aq_gemm_body<BF16, WF, GM, GN, WM, WN, GROUPED, XT, PK, c>(a, smem, wave); \
       return;                                                                 \
     }                                                                         \
   }
@@ -605,10 +633,10 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #undef WQ_WAVE_COLUMN
 }
 
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false, bool PK = false>
 hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   static_assert(GN <= 8, "wave grids have at most 8 columns");
-  using T = Tile<WF == kWInt4, GM, GN, WM, WN, GROUPED, XT>;
+  using T = Tile<WF == kWInt4, GM, GN, WM, WN, GROUPED, XT, PK>;
   AqArgs a = a0;
   a.tiles_m = (int)((a.m + T::BM - 1) / T::BM);
   a.tiles_n = (a.n + T::BN - 1) / T::BN;
@@ -616,7 +644,7 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   a.xcd_rm = xcd_region_rows(a.tiles_m, a.tiles_n, (double)T::BM * a.kchunk * 2.0,
                              (double)T::BN * a.kchunk * (WF == kWInt4 ? 0.5 : 1.0));
   const size_t lds = (size_t)T::Total;
-  auto kern = aq_gemm_kernel<BF16, WF, GM, GN, WM, WN, GROUPED, XT>;
+  auto kern = aq_gemm_kernel<BF16, WF, GM, GN, WM, WN, GROUPED, XT, PK>;
   hipError_t e = raise_lds_limit((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
@@ -641,6 +669,17 @@ template <bool BF16, int WF>
 hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   const bool tiny_m = a.bm == 64, short_m = a.bm == 128;
   constexpr bool kGroupedOk = WF != kWFp8;  // FLOAT8_E4M3FN weights come per-channel only
+  if (a.x2p) {  // packed weights
+    if constexpr (kGroupedOk) {
+      if (a.grouped) {
+        if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true, false, true>(a, stream);
+        return launch_one<BF16, WF, 2, 4, 2, 2, true, false, true>(a, stream);
+      }
+    }
+    if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, false, false, true>(a, stream);
+    if (short_m) return launch_one<BF16, WF, 2, 4, 2, 2, false, false, true>(a, stream);
+    return launch_one<BF16, WF, 2, 4, 4, 2, false, false, true>(a, stream);
+  }
   if (a.x2t) {  // transposed weights
     if constexpr (kGroupedOk) {
       if (a.grouped) {

@@ -52,7 +52,10 @@ struct SmTile {
 };
 
 // XT: the weights are stored transposed, (n, k) (int4: (n, k/2) bytes packed along k).
-template <bool BF16, int WF, bool GROUPED, bool XT>
+// PK: the weights are in the packed layout (wq_prepack_weight): a block's four 32-column
+// pieces are adjacent 2 KiB (int4: 1 KiB) runs of B fragments in lane order, so the whole
+// block is one contiguous DMA and each fragment one contiguous LDS read.
+template <bool BF16, int WF, bool GROUPED, bool XT, bool PK = false>
 __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) {
   constexpr bool W4 = WF == kWInt4;
   using T = SmTile<W4, GROUPED>;
@@ -77,9 +80,14 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   // per-lane DMA offsets inside a block
   uint32_t w_off[T::WDma];
   int w_k[T::WDma];  // transposed weights: first k (within the block) of this lane's chunk
+  constexpr int kPkBlock = W4 ? 1024 : 2048;     // packed: bytes of a 64 k x 32 column block
+  constexpr int kPkLane = W4 ? 4 : 8;            // packed: bytes of a lane's codes of a 16-k step
 #pragma unroll
   for (int j = 0; j < T::WDma; ++j) {
-    if constexpr (XT) {
+    if constexpr (PK) {
+      w_k[j] = 0;
+      w_off[j] = 1024u * (uint32_t)j + 16u * (uint32_t)lane;
+    } else if constexpr (XT) {
       constexpr int L = T::RowT / 16;
       const int r = T::ColsPerKB * j + lane / L;
       const int c = row_slot<T::RowT>(r, lane % L);
@@ -110,7 +118,16 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   }
   auto issue = [&](int t) {
     const int k0 = block_k0(t);
-    if constexpr (XT) {
+    if constexpr (PK) {
+      // the slab's four column blocks of 64-k block k0 / 64, side by side; blocks past n
+      // read zero, and so do codes past k (the packed layout pads them with zeros)
+      const int nbl = N / 32, nbt = n0 / 32;
+      const int valid = nbl - nbt < kSlab / 32 ? nbl - nbt : kSlab / 32;
+      const u32x4_t rw = make_rsrc((const uint8_t*)a.x2 + ((int64_t)(k0 / kRows) * nbl + nbt) * kPkBlock,
+                                   (int64_t)valid * kPkBlock);
+#pragma unroll
+      for (int j = 0; j < T::WDma; ++j) dma16(rw, st + 1024 * j, w_off[j]);
+    } else if constexpr (XT) {
       // the slab's column rows from k0 on; k >= kend (the split's end) is masked per chunk
       const int64_t kb = W4 ? k0 / 2 : k0;
       const int cols = N - n0 < kSlab ? N - n0 : kSlab;
@@ -146,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   float ssum = 0.f;  // row sum of x1 (row lane % 32, k half lane / 32)
   // logical column of this lane in block j (int4: byte pair p = j >> 1, parity j & 1)
   auto block_col = [&](int j) -> int {
-    if constexpr (W4 && !XT) return n0 + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
+    if constexpr (W4 && !XT && !PK) return n0 + 64 * (j >> 1) + 2 * (lane & 31) + (j & 1);
     else return n0 + 32 * j + (lane & 31);
   };
   const float cbias = a.code_bias;
@@ -189,14 +206,21 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
     const uint8_t* X = st + T::Wbytes;
     // B fragment reads per 16-k step: tr8 reads (an int4 one feeds two column blocks), or
     // one 8-byte (int4: 4-byte) read per block from transposed weights
-    constexpr int kP = (W4 && !XT) ? 2 : 4;
+    constexpr int kP = (W4 && !XT && !PK) ? 2 : 4;
     u32x4_t af[kRows / 16];
     u32x2_t braw[kRows / 16][kP];
 #pragma unroll
     for (int kk = 0; kk < kRows / 16; ++kk) {
       const int r = lane & 31;
       af[kk] = *(const u32x4_t*)(X + r * 128 + 16 * row_slot<128>(r, 2 * kk + (lane >> 5)));
-      if constexpr (XT) {
+      if constexpr (PK) {
+#pragma unroll
+        for (int p = 0; p < kP; ++p) {
+          const uint8_t* q = W + p * kPkBlock + kk * 64 * kPkLane + kPkLane * lane;
+          if constexpr (W4) braw[kk][p] = u32x2_t{*(const uint32_t*)q, 0u};
+          else braw[kk][p] = *(const u32x2_t*)q;
+        }
+      } else if constexpr (XT) {
         constexpr int RowT = T::RowT;
         const int c = 2 * kk + (lane >> 5);  // 8-k piece within the column row
 #pragma unroll
@@ -239,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
       auto step = [&](bool zero) {
 #pragma unroll
         for (int p = 0; p < kP; ++p) {
-          if constexpr (W4 && XT) {
+          if constexpr (W4 && (XT || PK)) {
             acc[p] = mfma32x32x16<BF16>(af[kk], i4x8_k_to_act<BF16>(braw[kk][p][0]), zero ? f32x16_t{} : acc[p]);
           } else if constexpr (W4) {
             u32x4_t ev, od;
@@ -442,7 +466,8 @@ template <bool BF16, int WF, bool GROUPED>
 hipError_t launch_sm(const AqArgs& a, hipStream_t stream) {
   using T = SmTile<WF == kWInt4, GROUPED>;
   const int slabs = (a.n + kSlab - 1) / kSlab;
-  auto kern = a.x2t ? aq_smallm_kernel<BF16, WF, GROUPED, true> : aq_smallm_kernel<BF16, WF, GROUPED, false>;
+  auto kern = a.x2p ? aq_smallm_kernel<BF16, WF, GROUPED, false, true>
+            : a.x2t ? aq_smallm_kernel<BF16, WF, GROUPED, true> : aq_smallm_kernel<BF16, WF, GROUPED, false>;
   hipError_t e = raise_lds_limit((const void*)kern, T::Lds);
   if (e != hipSuccess) return e;
   AqArgs args = a;

@@ -102,7 +102,7 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.x3 = p.x3; a.out = p.out;
   a.m = p.m; a.k = (int32_t)p.k; a.n = (int32_t)p.n;
   a.group = (int32_t)p.group; a.groups = (int32_t)p.groups;
-  a.bf16 = p.act == WQ_BF16; a.w4 = p.w4; a.f8 = p.f8; a.x2t = p.x2t;
+  a.bf16 = p.act == WQ_BF16; a.w4 = p.w4; a.f8 = p.f8; a.x2t = p.x2t; a.x2p = p.x2p;
   a.grouped = p.mode == wq::QuantMode::kGroup;
   a.per_tensor = p.mode == wq::QuantMode::kTensor;
   a.code_bias = wq::code_bias(p);
@@ -168,6 +168,14 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
   a.bm = pl.bm;
   hipError_t e = wq::launch_qm_gemm(a, (hipStream_t)stream);
   return e == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
+}
+
+int wq_prepack_weight(const wq_tensor* x2, const wq_tensor* packed, void* stream) {
+  if (!packed) return WQ_ERR_PARAM_NULLPTR;
+  wq::PrepackProblem p;
+  const int st = wq::validate_prepack(x2, packed, &p);
+  if (st != WQ_OK) return st;
+  return wq::launch_prepack(p, (hipStream_t)stream) == hipSuccess ? WQ_OK : WQ_ERR_RUNTIME;
 }
 
 int wq_profile_next_call(void* before, void* after) {

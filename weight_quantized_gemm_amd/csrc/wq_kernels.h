@@ -31,6 +31,7 @@ struct AqArgs {
   float code_bias;       // C: the fed weight image is code + C
   bool bf16, w4, f8, grouped, per_tensor;  // f8: FLOAT8_E4M3FN weights
   bool x2t;              // x2 stored transposed: (n, k) (int4: (n, k/2) bytes along k)
+  bool x2p;              // x2 in the packed layout (wq_prepack_weight)
 };
 
 // W8A8 matmul.
@@ -83,5 +84,7 @@ hipError_t launch_group_rowsums(const AqArgs& a, hipStream_t stream);
 hipError_t launch_transpose16(const void* src0, void* dst0, const void* src1, void* dst1, int rows,
                               int cols, hipStream_t stream);
 hipError_t launch_qm_gemm(const QmArgs& a, hipStream_t stream);
+// the offline weight prepack (wq_prepack_weight)
+hipError_t launch_prepack(const PrepackProblem& p, hipStream_t stream);
 
 }  // namespace wq

@@ -173,6 +173,15 @@ int wq_quant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor* x2,
   return WQ_OK;
 }
 
+int wq_prepack_weight_get_size(const wq_tensor* x2, uint64_t* packed_bytes) {
+  wq::PrepackProblem p;
+  const int st = wq::validate_prepack(x2, nullptr, &p);
+  if (st != WQ_OK) return st;
+  if (!packed_bytes) return WQ_ERR_PARAM_NULLPTR;
+  *packed_bytes = (uint64_t)p.bytes;
+  return WQ_OK;
+}
+
 const char* wq_status_string(int status) {
   switch (status) {
     case WQ_OK: return "WQ_OK";

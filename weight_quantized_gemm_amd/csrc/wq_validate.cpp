@@ -102,13 +102,15 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
   for (const wq_tensor* t : {x1, x2, scale, output, offset, bias, x3})
     if (t && !data_ok(t)) return WQ_ERR_PARAM_NULLPTR;
 
-  // 2. dtypes
+  // 2. dtypes (x2 may carry the packed-layout flag, wq_prepack_weight's output)
   const int32_t act = x1->dtype;
   if (act != WQ_F16 && act != WQ_BF16) return WQ_ERR_PARAM_INVALID;
-  if (x2->dtype != WQ_I8 && x2->dtype != WQ_I4 && x2->dtype != WQ_F8E4M3) return WQ_ERR_PARAM_INVALID;
+  const bool x2p = (x2->dtype & WQ_PACKED) != 0;
+  const int32_t wdt = x2->dtype & ~WQ_PACKED;
+  if (wdt != WQ_I8 && wdt != WQ_I4 && wdt != WQ_F8E4M3) return WQ_ERR_PARAM_INVALID;
   for (const wq_tensor* t : {scale, output, offset, bias, x3})
     if (t && t->dtype != act) return WQ_ERR_PARAM_INVALID;
-  const bool f8 = x2->dtype == WQ_F8E4M3;
+  const bool f8 = wdt == WQ_F8E4M3;
   if (f8 && offset) return WQ_ERR_PARAM_INVALID;  // fp8 weights take no offset
 
   // 3. attributes (the group size rule needs k, the last dimension of x1)
@@ -135,7 +137,7 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
     if (m > kMaxM) return WQ_ERR_PARAM_INVALID;
   }
   if (k < 0 || k > kMaxKN || n < 1 || n > kMaxKN) return WQ_ERR_PARAM_INVALID;
-  const bool w4 = x2->dtype == WQ_I4;
+  const bool w4 = wdt == WQ_I4;
   const int64_t align = w4 ? 64 : 32;
   if (k % align != 0 || n % align != 0) return WQ_ERR_PARAM_INVALID;
 
@@ -172,8 +174,9 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
   // layout: row-major contiguous, except that x2 may be the transpose of a row-major (n, k)
   // tensor; per-group parameters then must be transposed with it (and only then).  No
   // output aliasing.
-  const bool x2t = k > 0 && transposed2(x2);
-  if (!x2t && !contiguous(x2)) return WQ_ERR_PARAM_INVALID;
+  // A packed x2 is an opaque buffer (its strides are not read); it is never transposed.
+  const bool x2t = !x2p && k > 0 && transposed2(x2);
+  if (!x2p && !x2t && !contiguous(x2)) return WQ_ERR_PARAM_INVALID;
   const bool pt = mode == QuantMode::kGroup && groups > 0 && x2t;
   for (const wq_tensor* t : {scale, offset}) {
     if (!t) continue;
@@ -192,7 +195,7 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
 
   if (p) {
     p->m = m; p->k = k; p->n = n; p->act = act; p->w4 = w4; p->f8 = f8; p->mode = mode;
-    p->x2t = x2t; p->params_t = pt;
+    p->x2t = x2t; p->x2p = x2p; p->params_t = pt;
     p->group = group; p->groups = groups;
     p->x1 = x1->data; p->x2 = x2->data; p->scale = scale->data;
     p->offset = offset ? offset->data : nullptr;
@@ -272,6 +275,33 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
     p->x1 = x1->data; p->x2 = x2->data; p->bias = bias ? bias->data : nullptr;
     p->x3 = x3 ? x3->data : nullptr; p->dq = dq->data; p->pt = pt ? pt->data : nullptr;
     p->out = output->data; p->acc_out = acc_out ? acc_out->data : nullptr;
+  }
+  return WQ_OK;
+}
+
+int validate_prepack(const wq_tensor* x2, const wq_tensor* packed, PrepackProblem* p) {
+  if (!x2) return WQ_ERR_PARAM_NULLPTR;
+  if (!data_ok(x2)) return WQ_ERR_PARAM_NULLPTR;
+  if (x2->dtype != WQ_I8 && x2->dtype != WQ_I4 && x2->dtype != WQ_F8E4M3) return WQ_ERR_PARAM_INVALID;
+  if (!dims_ok(x2) || x2->ndim != 2) return WQ_ERR_PARAM_INVALID;
+  const int64_t k = x2->shape[0], n = x2->shape[1];
+  if (k < 1 || k > kMaxKN || n < 1 || n > kMaxKN) return WQ_ERR_PARAM_INVALID;
+  const int64_t align = x2->dtype == WQ_I4 ? 64 : 32;
+  if (k % align != 0 || n % align != 0) return WQ_ERR_PARAM_INVALID;
+  const bool x2t = transposed2(x2);
+  if (!x2t && !contiguous(x2)) return WQ_ERR_PARAM_INVALID;
+  if (!aligned16(x2)) return WQ_ERR_PARAM_INVALID;
+  if (packed) {
+    if (!data_ok(packed)) return WQ_ERR_PARAM_NULLPTR;
+    if (packed->dtype != (x2->dtype | WQ_PACKED)) return WQ_ERR_PARAM_INVALID;
+    if (!dims_ok(packed) || !shape_is(packed, 2, k, n)) return WQ_ERR_PARAM_INVALID;
+    if (!aligned16(packed) || aliases(packed->data, x2)) return WQ_ERR_PARAM_INVALID;
+  }
+  if (p) {
+    p->k = k; p->n = n; p->w4 = x2->dtype == WQ_I4; p->x2t = x2t;
+    p->x2 = x2->data;
+    p->packed = packed ? packed->data : nullptr;
+    p->bytes = packed_weight_bytes(k, n, p->w4);
   }
   return WQ_OK;
 }
