@@ -56,6 +56,34 @@ class WqError(RuntimeError):
         self.status = status
 
 
+def declare(L):
+    """Set the argument and result types of the C-ABI functions a loaded library exports
+    (all of them for the full library; a host-only build of the validation and planning
+    code exports the size queries, the status strings and the version)."""
+    P = ctypes.POINTER(WqTensor)
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    sigs = {
+        "wq_antiquant_matmul_get_workspace_size": ([P, P, P, P, P, P, ctypes.c_int64, P, u64p], ctypes.c_int),
+        "wq_antiquant_matmul": ([P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_void_p, ctypes.c_uint64,
+                                 ctypes.c_void_p], ctypes.c_int),
+        "wq_antiquant_matmul_noalloc": ([P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_void_p], ctypes.c_int),
+        "wq_quant_matmul_get_workspace_size": ([P, P, P, P, P, P, P, P, u64p], ctypes.c_int),
+        "wq_quant_matmul": ([P, P, P, P, P, P, P, P, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p],
+                            ctypes.c_int),
+        "wq_prepack_weight_get_size": ([P, u64p], ctypes.c_int),
+        "wq_prepack_weight": ([P, P, ctypes.c_void_p], ctypes.c_int),
+        "wq_profile_next_call": ([ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+        "wq_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "wq_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sigs.items():
+        if hasattr(L, name):
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+    return L
+
+
 _lib = None
 
 
@@ -66,29 +94,7 @@ def lib():
         if not os.path.exists(library_path):
             raise ImportError(f"{library_path} is missing: build it with "
                               "`python -m weight_quantized_gemm_amd.build`")
-        L = ctypes.CDLL(library_path)
-        P = ctypes.POINTER(WqTensor)
-        u64p = ctypes.POINTER(ctypes.c_uint64)
-        L.wq_antiquant_matmul_get_workspace_size.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, u64p]
-        L.wq_antiquant_matmul.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_void_p,
-                                          ctypes.c_uint64, ctypes.c_void_p]
-        L.wq_antiquant_matmul_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_void_p]
-        L.wq_quant_matmul_get_workspace_size.argtypes = [P, P, P, P, P, P, P, P, u64p]
-        L.wq_quant_matmul.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_void_p, ctypes.c_uint64,
-                                      ctypes.c_void_p]
-        for f in ("wq_antiquant_matmul_get_workspace_size", "wq_antiquant_matmul", "wq_antiquant_matmul_noalloc",
-                  "wq_quant_matmul_get_workspace_size", "wq_quant_matmul"):
-            getattr(L, f).restype = ctypes.c_int
-        L.wq_prepack_weight_get_size.argtypes = [P, u64p]
-        L.wq_prepack_weight.argtypes = [P, P, ctypes.c_void_p]
-        L.wq_prepack_weight_get_size.restype = ctypes.c_int
-        L.wq_prepack_weight.restype = ctypes.c_int
-        L.wq_profile_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-        L.wq_profile_next_call.restype = ctypes.c_int
-        L.wq_status_string.argtypes = [ctypes.c_int]
-        L.wq_status_string.restype = ctypes.c_char_p
-        L.wq_version.restype = ctypes.c_int
-        _lib = L
+        _lib = declare(ctypes.CDLL(library_path))
     return _lib
 
 

@@ -24,6 +24,7 @@
 #include <climits>
 #include <cstddef>
 #include <cstdint>
+#include <initializer_list>
 
 #include "wq_problem.h"
 
