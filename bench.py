@@ -238,7 +238,7 @@ def bench_one(name, args, torch, dev):
     kernel, bound = DOMINANT[name]
     dtype = "int8" if isinstance(case, workloads.W8A8Case) else case.act
     roof = make_roofline(bound, dtype, flops, abytes, launch_ms, ms_per_step)
-    roof["traffic"] = traffic_for(kernel, name)
+    roof["traffic"] = traffic_for(kernel, name + (".packed" if packed else ""))
     roof["kernel"] = kernel
     roof["kernel_events"] = "timed steps" if hooked_in_timed else "steps after the timed ones"
     value = flops / (ms_per_step / 1e3) / 1e12
