@@ -10,10 +10,12 @@ timed steps read their operands from HBM, not from a warm cache.
 
 Each input set gets a prepared call (descriptors and workspace settled once), so the host
 enqueues steps faster than the device runs them.  The timed region covers exactly the
-timed steps, bracketed by device synchronisation.  In each timed step the library's
-profiling hook passes a pair of HIP events with the launch of the step's main kernel
-(hipExtLaunchKernel), so that they take that kernel's own start and end on its launch
-stream; their average is the kernel duration of the roofline.
+timed steps, bracketed by device synchronisation.  In every fifth timed step the
+library's profiling hook passes a pair of HIP events with the launch of the step's main
+kernel (hipExtLaunchKernel), so that they take that kernel's own start and end on its
+launch stream; their average is the kernel duration of the roofline.  The events are
+created without a system-scope fence; a hooked launch still costs the stream a few
+microseconds, which is why only a sample of the steps carries them.
 
 Output: one JSON line (the headline workload), with the roofline of the dominant kernel
 and the CPU oracle's rate on the host as a baseline.  ``--all`` prints one line per
@@ -22,6 +24,7 @@ workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -176,12 +179,15 @@ def traffic_for(kernel, name):
 
 def make_roofline(bound, dtype, flops, abytes, launch_ms, ms_per_step):
     """The roofline entry of the dominant kernel from its per-launch durations (ms, one per
-    step).  Each step launches that kernel once, so its average duration cannot exceed the
-    step's: a longer one means the durations do not belong to these steps."""
+    hooked step).  Each step launches that kernel once, so the kernel cannot take longer
+    than the mean step of a back-to-back stream; an event average above it (the events'
+    own overhead, e.g. under a tracing profiler) is replaced by the mean step, an upper
+    bound on the kernel's duration, and the entry says so.  The events' own figures are
+    kept under events_us_*."""
     per = sorted(launch_ms)
-    avg_ms = sum(per) / len(per)
-    if avg_ms > ms_per_step * (1 + 1e-9):
-        raise ValueError(f"kernel average {avg_ms * 1e3:.2f} us exceeds the step's {ms_per_step * 1e3:.2f} us")
+    ev_ms = sum(per) / len(per)
+    bounded = ev_ms > ms_per_step
+    avg_ms = ms_per_step if bounded else ev_ms
     avg_s = avg_ms / 1e3
     if bound == "mfma":
         achieved = flops / avg_s / 1e12
@@ -191,11 +197,62 @@ def make_roofline(bound, dtype, flops, abytes, launch_ms, ms_per_step):
         achieved = abytes / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM, 4)}
-    roof["launch_us_median"] = round(per[len(per) // 2] * 1e3, 2)
     roof["launch_us_avg"] = round(avg_ms * 1e3, 2)
-    roof["launch_us_min"] = round(per[0] * 1e3, 2)
-    roof["launch_us_max"] = round(per[-1] * 1e3, 2)
+    roof["kernel_time"] = "mean step (events above it)" if bounded else "kernel events"
+    roof["events_us_avg"] = round(ev_ms * 1e3, 2)
+    roof["events_us_median"] = round(per[len(per) // 2] * 1e3, 2)
+    roof["events_us_min"] = round(per[0] * 1e3, 2)
+    roof["events_us_max"] = round(per[-1] * 1e3, 2)
     return roof
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (torch's, which the library shares)."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64" in os.path.basename(path):
+                return ctypes.CDLL(path)
+    return ctypes.CDLL("libamdhip64.so")
+
+
+class KernelEvents:
+    """Pairs of HIP timing events for the profiling hook, created without the system-scope
+    fence that a default event's record performs (hipEventDisableSystemFence): the hook
+    records a pair at every timed step, and fenced records would add several microseconds of
+    stream time to each step, more than a small call takes."""
+
+    NO_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        rt = _hip_runtime()
+        rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        for f in (rt.hipEventCreateWithFlags, rt.hipEventElapsedTime, rt.hipEventDestroy):
+            f.restype = ctypes.c_int
+        self.rt = rt
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            for e in (a, b):
+                st = rt.hipEventCreateWithFlags(ctypes.byref(e), self.NO_SYSTEM_FENCE)
+                if st != 0:
+                    raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+            self.pairs.append((a.value, b.value))
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float(0.0)
+        st = self.rt.hipEventElapsedTime(ctypes.byref(ms), *self.pairs[i])
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def close(self):
+        for a, b in self.pairs:
+            self.rt.hipEventDestroy(a)
+            self.rt.hipEventDestroy(b)
+        self.pairs = []
 
 
 def bench_one(name, args, torch, dev):
@@ -209,30 +266,36 @@ def bench_one(name, args, torch, dev):
     sh = stream.cuda_stream
     for i in range(args.warmup):
         calls[i % sets](sh)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:  # create the underlying HIP events before the hook refers to them
-        a.record(stream)
-        b.record(stream)
+    # The timed steps.  A hooked step arms the library's profiling hook, which hands a pair
+    # of events to the launch of the step's main kernel (hipExtLaunchKernel): they take that
+    # kernel's own start and end on its launch stream.  A hooked launch costs the stream a
+    # few microseconds, and the idle gap lets the clock recover, so that the hooked kernel
+    # itself runs faster than in a back-to-back stream (C2: 141-155 us against 160 us, by
+    # rocprofv3 kernel traces).  By default every fifth timed step is hooked
+    # (--kernel-events sampled), which keeps the stream close to back-to-back; `timed`
+    # hooks every timed step, `after` as many steps after the timed ones.
+    mode = args.kernel_events
+    every = max(1, args.kernel_sample_every) if mode == "sampled" else 1
+    hooked = [i for i in range(args.steps) if (mode == "timed" or (mode == "sampled" and i % every == every - 1))]
+    if mode == "sampled" and not hooked:
+        hooked = [args.steps - 1]
+    evs = KernelEvents(len(hooked) if mode != "after" else args.steps)
+    slot = {i: n for n, i in enumerate(hooked)}
     torch.cuda.synchronize()
-    # The timed steps.  Each arms the library's profiling hook, which hands the two events of
-    # the step to the launch of its main kernel (hipExtLaunchKernel): they take that kernel's
-    # own start and end on the launch stream and add no work of their own to the stream.
-    # With --kernel-events after, the hooked steps run after the timed ones instead.
-    hooked_in_timed = args.kernel_events == "timed"
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if hooked_in_timed:
-            W.profile_next_call(*evs[i])
+        if i in slot:
+            W.profile_next_call(*evs.pairs[slot[i]])
         calls[(args.warmup + i) % sets](sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if not hooked_in_timed:
+    if mode == "after":
         for i in range(args.steps):
-            W.profile_next_call(*evs[i])
+            W.profile_next_call(*evs.pairs[i])
             calls[(args.warmup + args.steps + i) % sets](sh)
         torch.cuda.synchronize()
-    launch_ms = [a.elapsed_time(b) for a, b in evs]          # ms, main kernel per step
+    launch_ms = [evs.elapsed_ms(i) for i in range(len(evs.pairs))]  # ms, main kernel per hooked step
+    evs.close()
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.0 * case.m * case.k * case.n
     kernel, bound = DOMINANT[name]
@@ -240,7 +303,9 @@ def bench_one(name, args, torch, dev):
     roof = make_roofline(bound, dtype, flops, abytes, launch_ms, ms_per_step)
     roof["traffic"] = traffic_for(kernel, name + (".packed" if packed else ""))
     roof["kernel"] = kernel
-    roof["kernel_events"] = "timed steps" if hooked_in_timed else "steps after the timed ones"
+    roof["kernel_events"] = {"sampled": f"every {every}th timed step ({len(launch_ms)} launches)",
+                             "timed": "every timed step",
+                             "after": "steps after the timed ones"}[mode]
     value = flops / (ms_per_step / 1e3) / 1e12
     spec = workloads.WORKLOADS[name]
     line = {
@@ -299,9 +364,12 @@ def main():
     ap.add_argument("--no-cpu", dest="cpu", action="store_false", help="skip the CPU oracle leg")
     ap.add_argument("--packed", action="store_true",
                     help="anti-quant workloads with their weights prepacked once before timing")
-    ap.add_argument("--kernel-events", choices=("timed", "after"), default="timed",
-                    help="where the main kernel's event pairs are taken: on the timed steps (default) "
-                         "or on as many steps after them")
+    ap.add_argument("--kernel-events", choices=("sampled", "timed", "after"), default="sampled",
+                    help="which steps carry the main kernel's event pairs: every Nth timed step "
+                         "(default; N = --kernel-sample-every), every timed step, or as many steps "
+                         "after the timed ones")
+    ap.add_argument("--kernel-sample-every", type=int, default=5,
+                    help="with --kernel-events sampled: hook every Nth timed step")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the matmul, time a plain device-to-device copy of this many MiB "
                          "(the reference kernel for scaling HBM byte counters)")

@@ -236,11 +236,15 @@ class _alloc_on:
 
 
 def profile_next_call(before, after):
-    """Arm the library's profiling hook: the next call on this thread records the torch
-    events `before` / `after` (created with enable_timing=True and recorded once before, so
-    that their HIP events exist) around the launch of its main kernel."""
-    b = before.cuda_event if before is not None else 0
-    a = after.cuda_event if after is not None else 0
+    """Arm the library's profiling hook: the next call on this thread records the events
+    `before` / `after` around the launch of its main kernel.  Each is a raw hipEvent_t handle
+    (an int) or a torch event (created with enable_timing=True and recorded once before, so
+    that its HIP event exists)."""
+    def handle(e):
+        if e is None:
+            return 0
+        return e if isinstance(e, int) else e.cuda_event
+    b, a = handle(before), handle(after)
     if (before is not None and not b) or (after is not None and not a):
         raise ValueError("record the events once before arming the hook")
     _check(lib().wq_profile_next_call(ctypes.c_void_p(b or None), ctypes.c_void_p(a or None)))
