@@ -83,6 +83,13 @@ PACKED_CASES = [
                                           with_offset=False, scale_dist=("uniform", 2e-4, 1e-3))),
     ("pk_sm_m32_pergroup64_fp16_i8_xt_wide", dict(act="fp16", weight="int8", x1_shape=(32, 2048), n=8192,
                                                   mode="group", group_size=64, x2_transposed=True)),
+    # n >= 8192 with k > 1024: split k, a k tail, n not a multiple of the slab
+    ("pk_wide_m32_pergroup128_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(32, 2048), n=8192, mode="group",
+                                           group_size=128, offset_dist=("uniform", -1, 1))),
+    ("pk_wide_m9_perchannel_fp16_i8_ktail", dict(act="fp16", weight="int8", x1_shape=(9, 1056), n=8192,
+                                               mode="channel")),
+    ("pk_wide_m2_pertensor_bf16_i4_nooff", dict(act="bf16", weight="int4", x1_shape=(2, 1152), n=8256, mode="tensor",
+                                              with_offset=False)),
     ("pk_sm_m5_pergroup32_bf16_i8_k96", dict(act="bf16", weight="int8", x1_shape=(5, 96), n=64, mode="group",
                                              group_size=32)),
     # large m: the tiled kernels' packed path (64-, 128-, 256-row tiles; split k; n edge; k tail)

@@ -69,6 +69,20 @@ AQ_CASES = [
     ("smallm_m3_pergroup128_bf16_i4", dict(act="bf16", weight="int4", x1_shape=(3, 1024), n=256, mode="group",
                                            group_size=128)),
     ("smallm_m17_pertensor_fp16_i4", dict(act="fp16", weight="int4", x1_shape=(17, 320), n=128, mode="tensor")),
+    # small m at n >= 8192 with k > 1024 (split k over 128-column slabs): ragged k, a 32-row
+    # k tail, every mode, fp8, 3-D x1, n not a multiple of the slab
+    ("wide_m32_pergroup64_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(32, 1088), n=8192, mode="group",
+                                           group_size=64, offset_dist=("uniform", -4, 4))),
+    ("wide_m5_perchannel_bf16_i8_k1056", dict(act="bf16", weight="int8", x1_shape=(5, 1056), n=8192,
+                                                mode="channel")),
+    ("wide_m1_pertensor_fp16_i8_nooff", dict(act="fp16", weight="int8", x1_shape=(1, 2048), n=8192,
+                                               mode="tensor", with_offset=False, with_x3=False)),
+    ("wide_m17_perchannel_bf16_f8_n8224", dict(act="bf16", weight="fp8e4m3", x1_shape=(17, 1536), n=8224,
+                                                 mode="channel", with_offset=False, with_bias=False)),
+    ("wide_3d_pergroup32_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(2, 4, 1152), n=8192, mode="group",
+                                          group_size=32)),
+    ("wide_m32_pergroup96_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(32, 1056), n=8192, mode="group",
+                                           group_size=96, with_bias=False)),
     ("smallm_m5_pergroup96_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(5, 544), n=160, mode="group",
                                           group_size=96)),
     ("smallm_m8_pergroup64_bf16_i8_k96", dict(act="bf16", weight="int8", x1_shape=(8, 96), n=64, mode="group",

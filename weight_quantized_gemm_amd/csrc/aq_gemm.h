@@ -12,14 +12,17 @@
 // C is the constant bias of the fed weight images (136 for bf16/int4, 0 otherwise).  The
 // matrix cores see only exact 16-bit images of the weight codes (int8, int4 or
 // FLOAT8_E4M3FN, all exact in fp16 and bf16) and x1; scale and offset
-// are applied in fp32 on the accumulators, per group at each group end, or once in the
-// epilogue for per-tensor / per-channel parameters.  Per-channel S is summed in-kernel from
-// the x1 fragments (v_dot2 against ones), each row by one wave.  Per-group S_g come from a
-// pass before the product (group_rowsums_kernel, aq_prep.hip): summed in the k-loop they
-// cost every wave of a row band the same work, about a sixth of the kernel's time.
-// Per-group scale and offset rows and the S_g rows of the tile travel with the weight tile
-// of the k-step in which their group ends, so a fold reads them from LDS and never waits on
-// a global load (which would also wait for every stage in flight).
+// are applied in fp32 on the accumulators, or once in the epilogue for per-tensor /
+// per-channel parameters.  Per-channel S is summed in-kernel from the x1 fragments (v_dot2
+// against ones), each row by one wave.  Per group, the scale part is folded at each group
+// end (tot += s * acc), with the group's scale row travelling with the weight tile of the
+// k-step in which the group ends, so a fold reads it from LDS and never waits on a global
+// load (which would also wait for every stage in flight).  The offset part,
+// sum_g s[g,n] * (off[g,n] - C) * S_g[m], is a product of depth G between the per-group row
+// sums of x1 and the parameter rows: it runs once per tile after the k loop, on the matrix
+// cores in fp32.  The S_g come from a pass before the product (group_rowsums_kernel,
+// aq_prep.hip): summed in the k-loop they cost every wave of a row band the same work,
+// about a sixth of the kernel's time.
 //
 // Pipeline: GM x GN waves, wave tile (32*WM) x (32*WN), workgroup tile (32*WM*GM) x (32*WN*GN),
 // BK = 64.  Operands travel global -> LDS by direct-to-LDS buffer loads
@@ -61,11 +64,9 @@ struct Tile {
   static constexpr int BN = 32 * WN * GN;            // logical columns
   static constexpr int RB = W4 ? BN / 2 : BN;        // weight bytes per k row
   static constexpr int Bbytes = kBK * RB;
-  // per-group scale and offset rows of the two groups a k-step can close, then their S_g
-  // rows (BM fp32 each)
+  // per-group scale and offset rows of the two groups a k-step can close
   static constexpr int Pbytes = GROUPED ? (BN > 128 ? 2048 : 1024) : 0;
-  static constexpr int Sbytes = GROUPED ? 2 * BM * 4 : 0;
-  static constexpr int Stage = Abytes + Bbytes + Pbytes + Sbytes;
+  static constexpr int Stage = Abytes + Bbytes + Pbytes;
   static constexpr int Win = 256 / RB;               // k rows per 256-byte bank window
   static constexpr int PairMask = 8 / Win - 1;       // swizzle span of 32-byte pairs
   static constexpr int RowsPerKB = 1024 / RB;        // k rows per 1 KiB DMA block
@@ -249,10 +250,10 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     rsc = make_rsrc((const uint8_t*)a.scale + 2 * (int64_t)n0, pbytes);
     rof = has_offset ? make_rsrc((const uint8_t*)a.offset + 2 * (int64_t)n0, pbytes) : rsc;
   }
-  // per-group: the tile's rows of the precomputed S_g, (groups, m) fp32, from row m0 on
+  // per-group: the precomputed S_g, (groups, m) fp32, read after the k loop
   const float* gsum = a.gsum;
-  // loads this wave issues per stage (the parameter wave: 2 parameter and 2 row-sum loads)
-  constexpr int kOwnA = T::Aper, kOwnB = T::Bper, kOwnP = GROUPED ? 4 : 0;
+  // loads this wave issues per stage (the parameter wave: 2 parameter-row loads)
+  constexpr int kOwnA = T::Aper, kOwnB = T::Bper, kOwnP = GROUPED ? 2 : 0;
   const bool has_b = wave < T::Bwaves, has_p = GROUPED && wave == T::Pwave;
 
   // The loads of one stage, as items that can be issued separately: x1 blocks j (kind 0),
@@ -307,23 +308,6 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       const int gb = min((r.k0 + 63) / a.group, a.groups - 1);
       uint8_t* pd = r.st + T::Abytes + T::Bbytes;
       dma_group_params<BN>(pd, rsc, rof, has_offset, ga, gb, N, lane);
-      // S_g rows of ga then gb: BM fp32 each, rows past m read zero
-      const uint32_t rows_bytes = (uint32_t)((M - m0 < T::BM ? M - m0 : T::BM) * 4);
-      const u32x4_t rsa = make_rsrc32(gsum + (int64_t)ga * M + m0, rows_bytes);
-      const u32x4_t rsb = make_rsrc32(gsum + (int64_t)gb * M + m0, rows_bytes);
-      uint8_t* sd = pd + T::Pbytes;
-      if constexpr (T::BM == 64) {  // 256 bytes a row: a quarter-wave load each
-        if (lane < 16) dma16(rsa, sd, 16u * (uint32_t)lane);
-        else if (lane < 32) dma16(rsb, sd, 16u * (uint32_t)(lane - 16));  // lands at sd + 256
-      } else if constexpr (T::BM == 128) {  // 512 bytes a row: one half-wave load each
-        const uint32_t off = 16u * (uint32_t)(lane & 31);
-        if (lane < 32) dma16(rsa, sd, off);
-        else dma16(rsb, sd, off);  // lands at sd + 512 + 16 (lane - 32)
-      } else {                       // 1 KiB a row: one full-wave load each
-        static_assert(T::BM == 256, "x1 tiles of 64, 128 or 256 rows");
-        dma16(rsa, sd, 16u * (uint32_t)lane);
-        dma16(rsb, sd + 1024, 16u * (uint32_t)lane);
-      }
     }
   };
   // the items of 16-k step kk: x1 blocks j with j % 4 == kk, weight blocks j with
@@ -381,33 +365,62 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   };
 
   // fold the group that ends at row 32 (e = 0) or 64 (e = 1) of the k-step whose
-  // parameter rows are at Ps (and S_g rows after them): tot += s * acc + s * (off - C) * S_g
+  // parameter rows are at Ps: tot += s * acc.  The group's offset term s * (off - C) * S_g is
+  // added after the k loop, for all groups at once (offset_product).
   auto rescale = [&](const uint16_t* Ps, int e) {
-    const float* Sg = (const float*)((const uint8_t*)Ps + T::Pbytes) + e * T::BM + wm * (32 * WM);
-    float s[WN], q[WN];
+    float s[WN];
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int lc = block_col(j) - n0;
-      const float sv = act_to_f32<BF16>(Ps[e * BN + lc]);
-      const float ov = act_to_f32<BF16>(Ps[T::Pbytes / 4 + e * BN + lc]);
-      s[j] = sv;
-      q[j] = sv * (ov - cbias);
-    }
+    for (int j = 0; j < WN; ++j) s[j] = act_to_f32<BF16>(Ps[e * BN + block_col(j) - n0]);
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const f32x4_t sr = *(const f32x4_t*)(Sg + 32 * i + 8 * rq + 4 * (lane >> 5));
+      for (int j = 0; j < WN; ++j)
 #pragma unroll
-        for (int j = 0; j < WN; ++j)
+        for (int r = 0; r < 16; ++r) tot[i][j][r] = fmaf(s[j], acc[i][j][r], tot[i][j][r]);
+    // acc is not cleared: the next group's first MFMA starts from zero
+  };
+
+  // The offset terms of this split's groups g0 .. g1 - 1, sum_g S_g[row] * q_g[col] with
+  // q_g = s_g * (off_g - C): a product of depth g1 - g0 between the precomputed row sums
+  // (groups, m) and the parameter rows, on the matrix cores in fp32 (32x32x2 MFMAs, two
+  // groups each: lane l holds group g + l / 32 of row or column l % 32), added to tot.
+  auto offset_product = [&]() {
+    if constexpr (GROUPED) {
+      if (!has_offset && cbias == 0.f) return;
+      const int g0 = kbeg / a.group;
+      const int g1 = min(a.groups, (kend + a.group - 1) / a.group);
+      const uint16_t* sp = (const uint16_t*)a.scale;
+      const uint16_t* op = (const uint16_t*)a.offset;
+      int64_t rows[WM];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rq + e;
-            tot[i][j][r] = fmaf(s[j], acc[i][j][r], fmaf(q[j], sr[e], tot[i][j][r]));
+      for (int i = 0; i < WM; ++i) rows[i] = m0 + wm * (32 * WM) + 32 * i + (lane & 31);
+      int cols[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) cols[j] = block_col(j);
+#pragma unroll 4
+      for (int g = g0; g < g1; g += 2) {
+        const int gl = g + (lane >> 5);
+        const bool gv = gl < g1;
+        float av[WM], bv[WN];
+#pragma unroll
+        for (int i = 0; i < WM; ++i) av[i] = (gv && rows[i] < M) ? gsum[(int64_t)gl * M + rows[i]] : 0.f;
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          float q = 0.f;
+          if (gv && cols[j] < N) {
+            const int64_t pi = (int64_t)gl * N + cols[j];
+            const float sv = act_to_f32<BF16>(sp[pi]);
+            q = sv * ((has_offset ? act_to_f32<BF16>(op[pi]) : 0.f) - cbias);
           }
+          bv[j] = q;
+        }
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            tot[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], tot[i][j], 0, 0, 0);
       }
     }
-    // acc is not cleared: the next group's first MFMA starts from zero
   };
 
   // ---------------------------------------------------------------- epilogue geometry
@@ -515,6 +528,8 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
       }
     }
   }
+
+  offset_product();
 
   // ---------------------------------------------------------------- epilogue
   __syncthreads();  // every wave is done with the stage buffers
