@@ -111,7 +111,10 @@ def make_runner(case, torch, dev, sets, packed=False):
         return calls, bufs
     odt = torch.bfloat16 if case.out == "bf16" else torch.float16
     for s in range(sets):
-        b = dict(x1=to_dev(case.x1, "raw", torch, dev), x2=to_dev(case.x2, "raw", torch, dev),
+        x2 = to_dev(case.x2, "raw", torch, dev)
+        if packed:
+            x2 = W.prepack_weight(x2)
+        b = dict(x1=to_dev(case.x1, "raw", torch, dev), x2=x2,
                  dq=to_dev(case.dequant_scale, case.dequant_dtype, torch, dev),
                  pt=to_dev(case.pertoken_scale, "fp32", torch, dev), bias=to_dev(case.bias, "raw", torch, dev),
                  x3=to_dev(case.x3, case.out, torch, dev))
@@ -260,7 +263,7 @@ def bench_one(name, args, torch, dev):
     case = workloads.make_workload(name)
     abytes = algorithmic_bytes(case)
     sets = max(1, min(8, -(-2 * CACHE_BYTES // max(abytes, 1))))
-    packed = bool(getattr(args, "packed", False)) and isinstance(case, workloads.AntiquantCase)
+    packed = bool(getattr(args, "packed", False))
     calls, bufs = make_runner(case, torch, dev, sets, packed=packed)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -363,7 +366,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", dest="cpu", action="store_false", help="skip the CPU oracle leg")
     ap.add_argument("--packed", action="store_true",
-                    help="anti-quant workloads with their weights prepacked once before timing")
+                    help="weights prepacked once before timing (wq_prepack_weight)")
     ap.add_argument("--kernel-events", choices=("sampled", "timed", "after"), default="sampled",
                     help="which steps carry the main kernel's event pairs: every Nth timed step "
                          "(default; N = --kernel-sample-every), every timed step, or as many steps "

@@ -52,7 +52,8 @@ typedef enum wq_dtype {
   WQ_F8E4M3 = 7
 } wq_dtype;
 
-/* Layout flag, or-ed into the dtype of an anti-quant weight (WQ_I8, WQ_I4 or WQ_F8E4M3):
+/* Layout flag, or-ed into the dtype of a weight (anti-quant: WQ_I8, WQ_I4 or WQ_F8E4M3;
+ * W8A8: WQ_I8):
  * the tensor holds the packed layout wq_prepack_weight writes (the role of the pages'
  * FRACTAL_NZ weight format), not an ND array.  Its descriptor keeps the logical shape
  * (k, n); its strides are not read. */
@@ -192,8 +193,9 @@ int wq_antiquant_matmul_noalloc(const wq_tensor* x1, const wq_tensor* x2, const 
  * descriptor with dtype x2->dtype | WQ_PACKED, shape (k, n), data a caller-owned device
  * buffer of at least the packed size, 16-byte aligned, not x2's.  The packed tensor can then
  * be passed as x2 to wq_antiquant_matmul_get_workspace_size, wq_antiquant_matmul and
- * wq_antiquant_matmul_noalloc; per-group scale and offset go with it row-major,
- * (ceil(k / g), n).  Returns WQ_OK, WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID or
+ * wq_antiquant_matmul_noalloc (per-group scale and offset go with it row-major,
+ * (ceil(k / g), n)), and, packed int8, to wq_quant_matmul_get_workspace_size and
+ * wq_quant_matmul.  Returns WQ_OK, WQ_ERR_PARAM_NULLPTR, WQ_ERR_PARAM_INVALID or
  * WQ_ERR_RUNTIME.
  */
 int wq_prepack_weight_get_size(const wq_tensor* x2, uint64_t* packed_bytes);
@@ -206,7 +208,8 @@ int wq_prepack_weight(const wq_tensor* x2, const wq_tensor* packed, void* stream
  *   x2              required; WQ_I8; (k, n); k and n multiples of 32.  Row-major with n in
  *                   [1, 65535], or transposed (strides (1, k): storage (n, k)) with n in
  *                   [1, 2^23] (Parameters table: only the last two axes may be swapped;
- *                   Constraints: n may exceed 65535 only when x2 is transposed).
+ *                   Constraints: n may exceed 65535 only when x2 is transposed), or
+ *                   WQ_I8 | WQ_PACKED, the output of wq_prepack_weight, with n in [1, 65535].
  *   bias            optional; WQ_I32; (n).  Added to the int32 accumulator before scaling.
  *   x3              optional; the output's dtype and shape.
  *   dequant_scale   required; (1), (n) or (1, n).  With a WQ_F16 output: WQ_F32 (the

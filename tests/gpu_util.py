@@ -73,14 +73,17 @@ def sample_rows(case, rows):
     return dataclasses.replace(case, x1=x1, x3=x3, pertoken_scale=pt)
 
 
-def run_w8a8(case, device="cuda:0", with_acc=True, stream=None, keep=None):
-    """The one-shot W8A8 call; `stream` and `keep` as for run_antiquant."""
+def run_w8a8(case, device="cuda:0", with_acc=True, stream=None, keep=None, packed=False):
+    """The one-shot W8A8 call; `stream` and `keep` as for run_antiquant; with `packed` the
+    weight goes through wq_prepack_weight first."""
     import weight_quantized_gemm_amd as W
     torch = torch_mod()
     x1 = dev_tensor(case.x1, "raw", device)
     x2 = dev_tensor(case.x2, "raw", device)
     if case.x2_transposed:
         x2 = x2.t()
+    if packed:
+        x2 = W.prepack_weight(x2)
     dq = dev_tensor(case.dequant_scale, case.dequant_dtype, device)
     pt = dev_tensor(case.pertoken_scale, "fp32", device)
     bias = dev_tensor(case.bias, "raw", device)

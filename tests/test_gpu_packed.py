@@ -7,7 +7,8 @@ Matmuls on the packed weight must match the fp64 oracle evaluated on the origina
 weight, to the usual tolerances (fp16 outputs 2e-3, bf16 1e-2, relative to max(1, |ref|)):
 the small-m kernel on packed weights (with and without k splits) and the tiled kernels'
 packed path (64-, 128- and 256-row tiles, split k), every mode and code type, and the
-full-size small-m workload.
+full-size small-m workload.  The W8A8 call on a packed int8 weight must give the oracle's
+int32 accumulator bit for bit and its output to the same tolerances.
 """
 import zlib
 
@@ -18,7 +19,7 @@ import torch
 import oracle
 import workloads
 import weight_quantized_gemm_amd as W
-from gpu_util import dev_tensor, ref_antiquant, to_f64
+from gpu_util import dev_tensor, ref_antiquant, ref_w8a8, run_w8a8, to_f64
 from packing import logical_codes, pack_reference
 
 pytestmark = pytest.mark.gpu
@@ -158,3 +159,39 @@ def test_packed_noalloc_and_graph():
         assert torch.equal(call.out.view(torch.int16), ref.view(torch.int16))
     res = oracle.compare(to_f64(ref).reshape(case.out_shape), ref_antiquant(case), act)
     assert res["ok"], res
+
+
+# W8A8 on packed int8 weights: 256-, 128- and 64-row tiles, split k with a k tail, n not a
+# multiple of the tile, 3-D x1, packed from a transposed weight, and the full-size workload
+W8A8_PACKED_CASES = [
+    ("pk_w8a8_ragged_bf16", dict(out="bf16", x1_shape=(600, 288), n=544)),
+    ("pk_w8a8_fp16_tensor_nopt_3d", dict(out="fp16", x1_shape=(2, 130, 256), n=96, dequant="tensor",
+                                         with_pertoken=False, with_bias=False)),
+    ("pk_w8a8_m1", dict(out="bf16", x1_shape=(1, 128), n=64)),
+    ("pk_w8a8_splitk_m300_tail_xt", dict(out="fp16", x1_shape=(300, 2080), n=320, x2_transposed=True)),
+    ("pk_w8a8_rows64_m100_bf16dq", dict(out="bf16", x1_shape=(100, 2048), n=512, dequant_dtype="bf16")),
+    ("pk_w8a8_rows128_m200", dict(out="bf16", x1_shape=(200, 4096), n=1024)),
+]
+
+
+@pytest.mark.parametrize("name,spec", W8A8_PACKED_CASES, ids=[c[0] for c in W8A8_PACKED_CASES])
+def test_w8a8_packed_parity(name, spec):
+    _announce(f"packed:{name}")
+    case = workloads.make_w8a8(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec)
+    y, acc = run_w8a8(case, packed=True)
+    ref, racc = ref_w8a8(case)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), racc)
+    r = oracle.compare(to_f64(y).reshape(ref.shape), ref, case.out)
+    assert r["ok"], (name, r)
+
+
+def test_w8a8_full_size_packed():
+    """The measured W8A8 workload with its weight prepacked: every output element, and the
+    int32 accumulator bit for bit."""
+    case = workloads.make_workload("w8a8_bf16_8192x4096x8192")
+    _announce("packed:w8a8 full size")
+    y, acc = run_w8a8(case, packed=True)
+    ref, racc = ref_w8a8(case)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), racc)
+    r = oracle.compare(to_f64(y).reshape(ref.shape), ref, case.out)
+    assert r["ok"], r

@@ -105,8 +105,8 @@ def test_prepack_size_and_rules(wqlib):
 
 def test_packed_weight_in_the_size_query(wqlib):
     """A packed x2 is accepted by the anti-quant size query (the same workspace as the ND
-    weight: the same kernels' splits), refused by the W8A8 one, and takes row-major
-    per-group parameters only."""
+    weight: the same kernels' splits) and, int8 only, by the W8A8 one; the anti-quant call
+    takes row-major per-group parameters only with it."""
     D, r = W.make_desc, ctypes.byref
     f16, i8 = W.WQ_F16, W.WQ_I8
     size = ctypes.c_uint64(0)
@@ -125,7 +125,12 @@ def test_packed_weight_in_the_size_query(wqlib):
     oft = D([128, 8192], f16, 0x400000, [1, 128])
     assert wqlib.wq_antiquant_matmul_get_workspace_size(r(x1), r(pk), None, r(sct), r(oft), None, 64, r(out),
                                                         r(size)) == W.WQ_ERR_PARAM_INVALID
-    q1, q2 = D([32, 64], i8, 0x100000), D([64, 128], i8 | W.WQ_PACKED, 0x200000)
+    # W8A8 takes a packed int8 weight, and no other packed code type
+    q1, q2 = D([32, 64], i8, 0x100000), D([64, 128], i8 | W.WQ_PACKED, 0x200000, [0, 0])
     dq, qo = D([128], W.WQ_F32, 0x300000), D([32, 128], W.WQ_BF16, 0x400000)
     assert wqlib.wq_quant_matmul_get_workspace_size(r(q1), r(q2), None, None, r(dq), None, r(qo), None,
-                                                    r(size)) == W.WQ_ERR_PARAM_INVALID
+                                                    r(size)) == W.WQ_OK
+    for bad in (W.WQ_I4 | W.WQ_PACKED, W.WQ_F8E4M3 | W.WQ_PACKED):
+        q2b = D([64, 128], bad, 0x200000, [0, 0])
+        assert wqlib.wq_quant_matmul_get_workspace_size(r(q1), r(q2b), None, None, r(dq), None, r(qo), None,
+                                                        r(size)) == W.WQ_ERR_PARAM_INVALID

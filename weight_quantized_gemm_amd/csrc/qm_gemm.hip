@@ -41,9 +41,14 @@ template <int BM> constexpr int qm_stage() { return qm_abytes<BM>() + kBbytes; }
 template <int BM> constexpr int qm_lds() { return kStages * qm_stage<BM>(); }  // 128 / 96 / 80 KiB
 
 // Wave grid GM x GN with WM x WN 32x32 blocks per wave (BM x 256 per workgroup); XT: x2
-// stored transposed, (n, k).
-template <bool OUT_BF16, int kGM, int kGN, bool XT, int BM = 256>
+// stored transposed, (n, k); PK: x2 in the packed layout (wq_prepack_weight: 64 k x 32
+// column blocks holding, per 16-k step, each lane's 8 codes).  An int8 MFMA takes 32 k: a
+// packed B fragment is the block's two 16-k pieces of the lane (k 32t + 8h + 0..7 and
+// 32t + 16 + 8h + 0..7, h = lane / 32), and the A fragment is read in the same k order,
+// so the product is unchanged.
+template <bool OUT_BF16, int kGM, int kGN, bool XT, int BM = 256, bool PK = false>
 __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs a) {
+  static_assert(!(XT && PK), "one weight layout");
   constexpr int kWaves = kGM * kGN;
   constexpr int kBM = BM;
   constexpr int kAbytes = qm_abytes<BM>(), kStage = qm_stage<BM>();
@@ -90,7 +95,10 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
 #pragma unroll
   for (int j = 0; j < kBper; ++j) {
     const int b = wave + kWaves * j;
-    if constexpr (XT) {                              // 16 columns of 64 bytes of k
+    if constexpr (PK) {                              // the stage's blocks are one contiguous run
+      b_chunk[j] = 0;
+      b_off[j] = 1024u * (uint32_t)b + 16u * (uint32_t)lane;
+    } else if constexpr (XT) {                       // 16 columns of 64 bytes of k
       const int r = 16 * b + (lane >> 2);
       b_chunk[j] = row_slot<kRA>(r, lane & 3);
       b_off[j] = (uint32_t)(r * K + 16 * b_chunk[j]);
@@ -115,7 +123,13 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
     r.k0 = kbeg + ks * kBK;
     r.st = smem + (ks % kStages) * kStage;
     r.ra = make_rsrc(x1b + r.k0, x1_bytes - r.k0);
-    if constexpr (XT) {
+    if constexpr (PK) {
+      // the tile's column blocks of 64-k block k0 / 64; blocks past n read zero, and so do
+      // codes past k (the packed layout pads them with zeros)
+      const int nbl = N / 32, nbt = n0 / 32;
+      const int valid = nbl - nbt < kBN / 32 ? nbl - nbt : kBN / 32;
+      r.rb = make_rsrc((const uint8_t*)a.x2 + ((int64_t)(r.k0 / kBK) * nbl + nbt) * 2048, (int64_t)valid * 2048);
+    } else if constexpr (XT) {
       r.rb = make_rsrc32(x2b + r.k0, x2t_bytes - (uint32_t)r.k0);
     } else {
       const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
@@ -190,6 +204,24 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   u32x4_t af[2][kWM], bfr[2][kWN];
   auto load = [&](const uint8_t* As, int kk, int buf) {
     const uint8_t* Bs = As + kAbytes;
+    if constexpr (PK) {
+      const int h = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < kWM; ++i) {
+        const int r = wm * (32 * kWM) + 32 * i + (lane & 31);
+        const u32x2_t lo = *(const u32x2_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk) + 8 * h);
+        const u32x2_t hi = *(const u32x2_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + 1) + 8 * h);
+        af[buf][i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int j = 0; j < kWN; ++j) {
+        const uint8_t* q = Bs + (wn * kWN + j) * 2048 + 2 * kk * 512 + 8 * lane;
+        const u32x2_t lo = *(const u32x2_t*)q;
+        const u32x2_t hi = *(const u32x2_t*)(q + 512);
+        bfr[buf][j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kWM; ++i) {
       const int r = wm * (32 * kWM) + 32 * i + (lane & 31);
@@ -399,7 +431,14 @@ hipError_t launch_qm_gemm(const QmArgs& a0, hipStream_t stream) {
   a.tiles_n = (a.n + kBN - 1) / kBN;
   a.xcd_rm = xcd_region_rows(a.tiles_m, a.tiles_n, (double)bm * a.kchunk, (double)kBN * a.kchunk);
   void (*kern)(const QmArgs);
-  if (bm == 64)
+  if (a.x2p) {  // packed weights
+    if (bm == 64)
+      kern = a.out_bf16 ? qm_gemm_kernel<true, 2, 2, false, 64, true> : qm_gemm_kernel<false, 2, 2, false, 64, true>;
+    else if (bm == 128)
+      kern = a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false, 128, true> : qm_gemm_kernel<false, 2, 4, false, 128, true>;
+    else
+      kern = a.out_bf16 ? qm_gemm_kernel<true, 2, 4, false, 256, true> : qm_gemm_kernel<false, 2, 4, false, 256, true>;
+  } else if (bm == 64)
     kern = a.x2t ? (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, true, 64> : qm_gemm_kernel<false, 2, 2, true, 64>)
                  : (a.out_bf16 ? qm_gemm_kernel<true, 2, 2, false, 64> : qm_gemm_kernel<false, 2, 2, false, 64>);
   else if (bm == 128)

@@ -162,6 +162,7 @@ int wq_quant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* b
   a.out_bf16 = p.out_dtype == WQ_BF16; a.dq_bf16 = p.dq_dtype == WQ_BF16;
   a.dq_per_tensor = p.dq_per_tensor;
   a.x2t = p.x2t;
+  a.x2p = p.x2p;
   a.splits = pl.split.splits;
   a.kchunk = pl.split.kchunk;
   a.partial = pl.workspace ? (int32_t*)workspace : nullptr;

@@ -54,6 +54,7 @@ struct QmArgs {
   int32_t bm;            // tile rows of the default configuration (qm_gemm_tile_m)
   bool out_bf16, dq_bf16, dq_per_tensor;
   bool x2t;              // x2 stored transposed, (n, k)
+  bool x2p;              // x2 in the packed layout (wq_prepack_weight)
 };
 
 // Raise a kernel's dynamic LDS limit; done once per (kernel, device, size) in a process.

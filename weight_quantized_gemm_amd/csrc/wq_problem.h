@@ -35,6 +35,7 @@ struct QuantProblem {
   int32_t dq_dtype = WQ_F32;     // WQ_F32 | WQ_BF16
   bool dq_per_tensor = false;
   bool x2t = false;              // x2 stored transposed: row-major (n, k)
+  bool x2p = false;              // x2 in the packed layout (wq_prepack_weight)
   const void* x1 = nullptr;
   const void* x2 = nullptr;
   const void* bias = nullptr;      // int32, may be null

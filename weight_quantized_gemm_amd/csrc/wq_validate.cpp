@@ -214,7 +214,10 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
   for (const wq_tensor* t : {x1, x2, dq, output, bias, x3, pt, acc_out})
     if (t && !data_ok(t)) return WQ_ERR_PARAM_NULLPTR;
 
-  if (x1->dtype != WQ_I8 || x2->dtype != WQ_I8) return WQ_ERR_PARAM_INVALID;
+  // x2: int8, row-major, transposed, or in the packed layout (an opaque buffer whose strides
+  // are not read; never transposed)
+  const bool x2p = x2->dtype == (WQ_I8 | WQ_PACKED);
+  if (x1->dtype != WQ_I8 || (x2->dtype != WQ_I8 && !x2p)) return WQ_ERR_PARAM_INVALID;
   if (bias && bias->dtype != WQ_I32) return WQ_ERR_PARAM_INVALID;
   if (output->dtype != WQ_F16 && output->dtype != WQ_BF16) return WQ_ERR_PARAM_INVALID;
   if (x3 && x3->dtype != output->dtype) return WQ_ERR_PARAM_INVALID;
@@ -241,7 +244,7 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
   }
   // the W8A8 op supports no empty tensor (Constraints, "Empty tensor support"); n may exceed
   // 65535 only with a transposed x2 (Constraints)
-  const bool x2t = transposed2(x2);
+  const bool x2t = !x2p && transposed2(x2);
   if (k < 1 || k > kMaxKN || n < 1 || n > (x2t ? kMaxNT : kMaxKN)) return WQ_ERR_PARAM_INVALID;
   if (k % 32 != 0 || n % 32 != 0) return WQ_ERR_PARAM_INVALID;
 
@@ -258,7 +261,7 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
   if (pt && !shape_is(pt, 1, m)) return WQ_ERR_PARAM_INVALID;
   if (acc_out && !shape_is(acc_out, 2, m, n)) return WQ_ERR_PARAM_INVALID;
 
-  if (!x2t && !contiguous(x2)) return WQ_ERR_PARAM_INVALID;
+  if (!x2p && !x2t && !contiguous(x2)) return WQ_ERR_PARAM_INVALID;
   for (const wq_tensor* t : {x1, dq, output, bias, x3, pt, acc_out})
     if (t && !contiguous(t)) return WQ_ERR_PARAM_INVALID;
   for (const wq_tensor* t : {x1, x2, dq, bias, x3, pt, acc_out})
@@ -273,6 +276,7 @@ int validate_quant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bi
     p->m = m; p->k = k; p->n = n; p->out_dtype = output->dtype; p->dq_dtype = dq->dtype;
     p->dq_per_tensor = dq_tensor;
     p->x2t = x2t;
+    p->x2p = x2p;
     p->x1 = x1->data; p->x2 = x2->data; p->bias = bias ? bias->data : nullptr;
     p->x3 = x3 ? x3->data : nullptr; p->dq = dq->data; p->pt = pt ? pt->data : nullptr;
     p->out = output->data; p->acc_out = acc_out ? acc_out->data : nullptr;
