@@ -43,9 +43,8 @@ template <int BM> constexpr int qm_lds() { return kStages * qm_stage<BM>(); }  /
 // Wave grid GM x GN with WM x WN 32x32 blocks per wave (BM x 256 per workgroup); XT: x2
 // stored transposed, (n, k); PK: x2 in the packed layout (wq_prepack_weight: 64 k x 32
 // column blocks holding, per 16-k step, each lane's 8 codes).  An int8 MFMA takes 32 k: a
-// packed B fragment is the block's two 16-k pieces of the lane (k 32t + 8h + 0..7 and
-// 32t + 16 + 8h + 0..7, h = lane / 32), and the A fragment is read in the same k order,
-// so the product is unchanged.
+// lane's 16 codes of a packed B fragment are the two 8-code pieces that the anti-quant
+// layout gives to lanes c and c + 32 of one 16-k step.
 template <bool OUT_BF16, int kGM, int kGN, bool XT, int BM = 256, bool PK = false>
 __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs a) {
   static_assert(!(XT && PK), "one weight layout");
@@ -204,28 +203,23 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
   u32x4_t af[2][kWM], bfr[2][kWN];
   auto load = [&](const uint8_t* As, int kk, int buf) {
     const uint8_t* Bs = As + kAbytes;
-    if constexpr (PK) {
-      const int h = lane >> 5;
-#pragma unroll
-      for (int i = 0; i < kWM; ++i) {
-        const int r = wm * (32 * kWM) + 32 * i + (lane & 31);
-        const u32x2_t lo = *(const u32x2_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk) + 8 * h);
-        const u32x2_t hi = *(const u32x2_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + 1) + 8 * h);
-        af[buf][i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      }
-#pragma unroll
-      for (int j = 0; j < kWN; ++j) {
-        const uint8_t* q = Bs + (wn * kWN + j) * 2048 + 2 * kk * 512 + 8 * lane;
-        const u32x2_t lo = *(const u32x2_t*)q;
-        const u32x2_t hi = *(const u32x2_t*)(q + 512);
-        bfr[buf][j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      }
-      return;
-    }
 #pragma unroll
     for (int i = 0; i < kWM; ++i) {
       const int r = wm * (32 * kWM) + 32 * i + (lane & 31);
       af[buf][i] = *(const u32x4_t*)(As + r * kRA + 16 * row_slot<kRA>(r, 2 * kk + (lane >> 5)));
+    }
+    if constexpr (PK) {
+      // lane (h, c) takes k 32 kk + 16 h + 0..15 of column c: the 16-k step 2 kk + h of the
+      // packed block, where lane c holds its k 0..7 and lane c + 32 its k 8..15
+      const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+      for (int j = 0; j < kWN; ++j) {
+        const uint8_t* q = Bs + (wn * kWN + j) * 2048 + (2 * kk + h) * 512 + 8 * c;
+        const u32x2_t lo = *(const u32x2_t*)q;
+        const u32x2_t hi = *(const u32x2_t*)(q + 256);
+        bfr[buf][j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+      return;
     }
     if constexpr (XT) {
 #pragma unroll
