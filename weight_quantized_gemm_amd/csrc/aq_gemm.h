@@ -89,8 +89,8 @@ struct Tile {
   // B fragment reads per wave per 16-k step: tr8 reads (an int4 one feeds two blocks), or
   // one 8-byte (int4: 4-byte) read per block from transposed weights
   static constexpr int Reads = (W4 && !XT && !PK) ? WN / 2 : WN;
-  // LDS layout: stages (x1 | weights | group parameters | group row sums) | per-channel S
-  // rows (BM fp32).  As many stages as fit (3 to 6): a deeper pipeline hides more load
+  // LDS layout: stages (x1 | weights | group scale / offset rows) | per-channel S rows
+  // (BM fp32).  As many stages as fit (3 to 6): a deeper pipeline hides more load
   // latency where a stage is small.
   static constexpr int Extra = BM * 4;
   static constexpr int FitStages = (160 * 1024 - Extra) / Stage;

@@ -4,7 +4,7 @@
 //  * per-group scale and offset stored transposed with a transposed x2 (section 参数说明):
 //    copied to the row-major (groups, n) layout the GEMM kernels read, in the workspace;
 //  * per-group row sums of x1, S_g[r] = sum of x1[r, k] over the k of group g, which the
-//    factored product needs at each group end (see aq_gemm.h);
+//    factored product's offset term needs (read after the k loop, see aq_gemm.h);
 //  * the offline weight prepack (wq_prepack_weight): x2 into the packed layout of 64 k x 32
 //    column blocks in MFMA B-fragment order (the layout is described in wqgemm.h).
 #include "wq_device.h"

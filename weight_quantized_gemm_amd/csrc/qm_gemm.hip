@@ -16,7 +16,9 @@
 // read as MFMA A fragments by 16-byte loads; x2 rows (256 bytes, n-contiguous) give B
 // fragments by two tr8 transpose reads (16 consecutive k of one column).  A transposed x2
 // (stored (n, k), which the Parameters table allows) travels exactly like x1: 64-byte rows
-// of k per column, 16-byte fragment loads, no transpose.  The epilogue
+// of k per column, 16-byte fragment loads, no transpose.  A packed x2 (wq_prepack_weight)
+// travels as one contiguous 16 KiB run per stage and gives each B fragment in two 8-byte
+// reads.  The epilogue
 // stages the accumulators through LDS so that x3, the output and the int32 accumulator
 // move in 16-byte row-contiguous accesses.  With few output tiles k is split (grid y):
 // the splits write int32 partial tiles and qm_splitk_finish adds them, in split order.
