@@ -8,7 +8,9 @@ weight, to the usual tolerances (fp16 outputs 2e-3, bf16 1e-2, relative to max(1
 the small-m kernel on packed weights (with and without k splits) and the tiled kernels'
 packed path (64-, 128- and 256-row tiles, split k), every mode and code type, and the
 full-size small-m workload.  The W8A8 call on a packed int8 weight must give the oracle's
-int32 accumulator bit for bit and its output to the same tolerances.
+int32 accumulator bit for bit and its output to the same tolerances.  Seeded random sweeps
+cover both calls on packed weights across dtypes, code types, modes, optional inputs,
+ragged shapes and transposed sources.
 """
 import zlib
 
@@ -195,3 +197,74 @@ def test_w8a8_full_size_packed():
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), racc)
     r = oracle.compare(to_f64(y).reshape(ref.shape), ref, case.out)
     assert r["ok"], r
+
+
+# ---------------------------------------------------------------- seeded sweeps, packed
+def _sweep_packed(count, seed, ms, kmax, prefix):
+    """Random combinations of dtype, code type, mode, optional inputs, ragged shapes and a
+    transposed source weight, all prepacked (small-m and tiled paths), from fixed seeds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        act = str(rng.choice(["fp16", "bf16"]))
+        weight = str(rng.choice(["int8", "int4", "fp8e4m3"], p=[0.45, 0.35, 0.2]))
+        align = 64 if weight == "int4" else 32
+        k = int(align * rng.integers(1, kmax + 1))
+        n = int(align * rng.integers(1, 13))
+        m = int(rng.choice(list(ms)))
+        mode = "channel" if weight == "fp8e4m3" else str(rng.choice(["tensor", "channel", "group"]))
+        g = 0
+        if mode == "group":
+            gs = list(range(32, k, 32))
+            if gs:
+                g = int(rng.choice(gs))
+            else:
+                mode = "channel"
+        spec = dict(act=act, weight=weight, x1_shape=(m, k), n=n, mode=mode, group_size=g,
+                    with_offset=weight != "fp8e4m3" and bool(rng.random() < 0.7),
+                    with_bias=bool(rng.random() < 0.6), with_x3=bool(rng.random() < 0.6),
+                    x2_transposed=bool(rng.random() < 0.3))
+        if weight == "fp8e4m3":
+            spec["scale_dist"] = ("uniform", 2e-4, 1e-3)
+        out.append((f"{prefix}{i}_{act}_{weight}_{mode}{g or ''}_m{m}k{k}n{n}"
+                    f"{'_xt' if spec['x2_transposed'] else ''}", spec))
+    return out
+
+
+PACKED_SWEEP = (_sweep_packed(24, 5151, (1, 3, 16, 31, 32), 40, "pksw")
+                + _sweep_packed(24, 5252, (33, 64, 100, 129, 257, 600), 64, "pkswt"))
+
+
+@pytest.mark.parametrize("name,spec", PACKED_SWEEP, ids=[c[0] for c in PACKED_SWEEP])
+def test_packed_sweep(name, spec):
+    check_packed(workloads.make_antiquant(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec))
+
+
+def _sweep_w8a8_packed(count=12, seed=5353):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        k = int(32 * rng.integers(1, 65))
+        n = int(32 * rng.integers(1, 17))
+        m = int(rng.choice([1, 5, 32, 77, 256, 300, 640]))
+        out_dt = str(rng.choice(["fp16", "bf16"]))
+        spec = dict(out=out_dt, x1_shape=(m, k), n=n, dequant=str(rng.choice(["tensor", "channel"])),
+                    dequant_dtype=str(rng.choice(["fp32", "bf16"])) if out_dt == "bf16" else "fp32",
+                    with_bias=bool(rng.random() < 0.7), with_pertoken=bool(rng.random() < 0.7),
+                    with_x3=bool(rng.random() < 0.6), x2_transposed=bool(rng.random() < 0.4))
+        out.append((f"pksw8_{i}_m{m}k{k}n{n}{'_xt' if spec['x2_transposed'] else ''}", spec))
+    return out
+
+
+W8A8_PACKED_SWEEP = _sweep_w8a8_packed()
+
+
+@pytest.mark.parametrize("name,spec", W8A8_PACKED_SWEEP, ids=[c[0] for c in W8A8_PACKED_SWEEP])
+def test_w8a8_packed_sweep(name, spec):
+    _announce(f"packed:{name}")
+    case = workloads.make_w8a8(seed=zlib.crc32(name.encode()) % 10000, name=name, **spec)
+    y, acc = run_w8a8(case, packed=True)
+    ref, racc = ref_w8a8(case)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), racc)
+    r = oracle.compare(to_f64(y).reshape(ref.shape), ref, case.out)
+    assert r["ok"], (name, r)
