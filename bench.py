@@ -209,6 +209,18 @@ def make_roofline(bound, dtype, flops, abytes, launch_ms, ms_per_step):
     return roof
 
 
+def hooked_steps(mode, steps, every):
+    """The timed steps that carry the profiling hook's events: every `every`-th one
+    (`sampled`, at least the last), all (`timed`), or none (`after`: the events go to as many
+    steps after the timed ones)."""
+    if mode == "timed":
+        return list(range(steps))
+    if mode == "after" or steps < 1:
+        return []
+    every = max(1, every)
+    return [i for i in range(steps) if i % every == every - 1] or [steps - 1]
+
+
 def _hip_runtime():
     """The HIP runtime this process already uses (torch's, which the library shares)."""
     with open("/proc/self/maps") as f:
@@ -279,9 +291,7 @@ def bench_one(name, args, torch, dev):
     # hooks every timed step, `after` as many steps after the timed ones.
     mode = args.kernel_events
     every = max(1, args.kernel_sample_every) if mode == "sampled" else 1
-    hooked = [i for i in range(args.steps) if (mode == "timed" or (mode == "sampled" and i % every == every - 1))]
-    if mode == "sampled" and not hooked:
-        hooked = [args.steps - 1]
+    hooked = hooked_steps(mode, args.steps, every)
     evs = KernelEvents(len(hooked) if mode != "after" else args.steps)
     slot = {i: n for n, i in enumerate(hooked)}
     torch.cuda.synchronize()

@@ -68,3 +68,12 @@ def test_roofline_from_kernel_durations():
     assert b["launch_us_avg"] == pytest.approx(162.0) and b["events_us_avg"] == pytest.approx(167.5)
     assert b["kernel_time"].startswith("mean step")
     assert b["launch_us_avg"] <= 162.0
+
+
+def test_hooked_steps():
+    """Which timed steps carry the kernel events: every fifth by default, at least one."""
+    assert bench.hooked_steps("sampled", 50, 5) == [4, 9, 14, 19, 24, 29, 34, 39, 44, 49]
+    assert bench.hooked_steps("sampled", 3, 5) == [2]
+    assert bench.hooked_steps("sampled", 7, 1) == list(range(7))
+    assert bench.hooked_steps("timed", 4, 5) == [0, 1, 2, 3]
+    assert bench.hooked_steps("after", 4, 5) == []
