@@ -26,8 +26,9 @@
 //
 // Pipeline: GM x GN waves, wave tile (32*WM) x (32*WN), workgroup tile (32*WM*GM) x (32*WN*GN),
 // BK = 64.  Operands travel global -> LDS by direct-to-LDS buffer loads
-// (no registers, out-of-range lanes read zero) through 3 LDS stages, one barrier per
-// k-step.  x1 tiles are row-major with a 16-byte-chunk XOR swizzle and are read as MFMA A
+// (no registers, out-of-range lanes read zero) through 3 to 6 LDS stages (as many as fit),
+// one barrier per k-step; every k-step issues a full stage of loads, those past the k range
+// from empty resources, so that the loop needs no branches around them.  x1 tiles are row-major with a 16-byte-chunk XOR swizzle and are read as MFMA A
 // fragments by ds_read_b128.  Weight tiles stay raw (one-byte codes or packed int4, n-contiguous,
 // 32-byte-pair XOR swizzle); B fragments come from ds_read_b64_tr_b8 (8 consecutive k of
 // one column per lane) and are turned into exact 16-bit images in registers.  The
@@ -105,21 +106,6 @@ struct Tile {
   static_assert(!W4 || XT || PK || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
   static_assert(!(XT && PK), "one weight layout");
 };
-
-// Stage barrier allowing `ahead` later stages (OWN loads each) to stay in flight, for a
-// run-time ahead in [0, MAXA].
-template <int OWN, int MAXA>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  if constexpr (MAXA > 0) {
-    if (ahead >= MAXA) {
-      stage_barrier<OWN * MAXA>();
-      return;
-    }
-    wait_stage<OWN, MAXA - 1>(ahead);
-  } else {
-    stage_barrier<0>();
-  }
-}
 
 // One 16-k step of MFMA operands for a wave: WM x1 fragments (16-byte reads) and the raw
 // weight bytes of its tr8 reads.
@@ -271,36 +257,36 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     StageRsrc r;
     r.k0 = kbeg + ks * kBK;
     r.st = smem + (ks % T::Stages) * T::Stage;
-    r.ra = make_rsrc32(x1b + (int64_t)r.k0 * 2, x1_bytes - (uint32_t)r.k0 * 2);
+    // Every k-step issues the loads of the stage S - 1 ahead, also past the split's range:
+    // those get empty resources, so they read nothing and write zeros into a stage no wave
+    // reads any more.  The loop then has one wait count and no branches around its loads.
+    const bool live = ks < nk;
+    r.ra = make_rsrc32(x1b + (int64_t)r.k0 * 2, live ? x1_bytes - (uint32_t)r.k0 * 2 : 0u);
     if constexpr (PK) {
       // the tile's column blocks of 64-k block k0 / 64; blocks past n read zero (the
       // packed layout pads k past the end with zero codes)
       const int nbl = N / 32, nbt = n0 / 32;
       const int valid = nbl - nbt < BN / 32 ? nbl - nbt : BN / 32;
       r.rb = make_rsrc((const uint8_t*)a.x2 + ((int64_t)(r.k0 / kBK) * nbl + nbt) * T::PkBlock,
-                       (int64_t)valid * T::PkBlock);
+                       live ? (int64_t)valid * T::PkBlock : 0);
     } else if constexpr (XT) {
       const uint32_t kb = W4 ? (uint32_t)r.k0 / 2 : (uint32_t)r.k0;
-      r.rb = make_rsrc32(x2b + kb, x2t_bytes - kb);
+      r.rb = make_rsrc32(x2b + kb, live ? x2t_bytes - kb : 0u);
     } else {
       const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
-      r.rb = make_rsrc32(x2b + (int64_t)r.k0 * x2_pitch, (uint32_t)(rows * x2_pitch - nb0));
+      r.rb = make_rsrc32(x2b + (int64_t)r.k0 * x2_pitch, live ? (uint32_t)(rows * x2_pitch - nb0) : 0u);
     }
     r.tail = r.k0 + kBK > K;  // only the last k-step can reach past k
     return r;
   };
   auto issue_a = [&](const StageRsrc& r, int j) {
     uint8_t* dst = r.st + 1024 * (wave + T::Waves * j);
-    if (!r.tail) {
-      dma16(r.ra, dst, a_off[j]);
-    } else {
-      dma16(r.ra, dst, r.k0 + a_k[j] >= K ? kOOB : a_off[j]);
-    }
+    dma16(r.ra, dst, (r.tail && r.k0 + a_k[j] >= K) ? kOOB : a_off[j]);
   };
   auto issue_b = [&](const StageRsrc& r, int j) {
     uint8_t* dst = r.st + T::Abytes + 1024 * (wave + T::Waves * j);
-    if (!XT || !r.tail) dma16(r.rb, dst, b_off[j]);
-    else dma16(r.rb, dst, r.k0 + b_k[j] >= K ? kOOB : b_off[j]);  // k past the end reads 0
+    if constexpr (!XT) dma16(r.rb, dst, b_off[j]);
+    else dma16(r.rb, dst, (r.tail && r.k0 + b_k[j] >= K) ? kOOB : b_off[j]);  // k past the end reads 0
   };
   auto issue_p = [&](const StageRsrc& r) {
     if constexpr (GROUPED) {
@@ -452,17 +438,15 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
 
   // ---------------------------------------------------------------- main loop
   constexpr int S = T::Stages;
-  for (int ks = 0; ks < S - 1 && ks < nk; ++ks) issue(ks);
+  for (int ks = 0; ks < S - 1; ++ks) issue(ks);
   for (int ks = 0; ks < nk; ++ks) {
-    // stage ks is complete once only the stages issued after it may still be in flight
-    const int ahead = min(S - 2, nk - 1 - ks);
-    if (has_b && has_p) wait_stage<kOwnA + kOwnB + kOwnP, S - 2>(ahead);
-    else if (has_b) wait_stage<kOwnA + kOwnB, S - 2>(ahead);
-    else if (has_p) wait_stage<kOwnA + kOwnP, S - 2>(ahead);
-    else wait_stage<kOwnA, S - 2>(ahead);
-    const bool more = ks + S - 1 < nk;
-    const StageRsrc nr = stage_rsrc(ks + S - 1);  // scalar work; unused on the last steps
-    if (ks == nk - 1) {  // no DMA left: start the epilogue's x3 reads under the last MFMAs
+    // stage ks is complete once only the S - 2 stages issued after it may still be in flight
+    if (has_b && has_p) stage_barrier<(kOwnA + kOwnB + kOwnP) * (S - 2)>();
+    else if (has_b) stage_barrier<(kOwnA + kOwnB) * (S - 2)>();
+    else if (has_p) stage_barrier<(kOwnA + kOwnP) * (S - 2)>();
+    else stage_barrier<kOwnA * (S - 2)>();
+    const StageRsrc nr = stage_rsrc(ks + S - 1);
+    if (ks == nk - 1) {  // only loads past the range left: start the epilogue's x3 reads
       prefetch_x3(0, 0);
       if (XP > 1 && WM > 1) prefetch_x3(1, 1 % XP);
     }
@@ -517,7 +501,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
 #pragma unroll
           for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], acc[i][j]);
       }
-      if (more) issue_step(nr, kk);  // behind this step's matrix-core work
+      issue_step(nr, kk);  // behind this step's matrix-core work
 
       if constexpr (GROUPED) {
         if (kk & 1) {  // groups end on multiples of 32
@@ -532,6 +516,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   offset_product();
 
   // ---------------------------------------------------------------- epilogue
+  wave_wait<0>();   // the loads past the range (zeros) have landed
   __syncthreads();  // every wave is done with the stage buffers
   float* srow = (float*)(smem + T::SOff);
   if constexpr (!GROUPED) {

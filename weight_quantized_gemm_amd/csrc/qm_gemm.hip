@@ -123,18 +123,23 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
     StageRsrc r;
     r.k0 = kbeg + ks * kBK;
     r.st = smem + (ks % kStages) * kStage;
-    r.ra = make_rsrc(x1b + r.k0, x1_bytes - r.k0);
+    // Every k-step issues the loads of the stage kStages - 1 ahead, also past the split's
+    // range: those get empty resources, so they read nothing and write zeros into a stage no
+    // wave reads any more.  The loop then has one wait count and no branches around its loads.
+    const bool live = ks < nk;
+    r.ra = make_rsrc(x1b + r.k0, live ? x1_bytes - r.k0 : 0);
     if constexpr (PK) {
       // the tile's column blocks of 64-k block k0 / 64; blocks past n read zero, and so do
       // codes past k (the packed layout pads them with zeros)
       const int nbl = N / 32, nbt = n0 / 32;
       const int valid = nbl - nbt < kBN / 32 ? nbl - nbt : kBN / 32;
-      r.rb = make_rsrc((const uint8_t*)a.x2 + ((int64_t)(r.k0 / kBK) * nbl + nbt) * 2048, (int64_t)valid * 2048);
+      r.rb = make_rsrc((const uint8_t*)a.x2 + ((int64_t)(r.k0 / kBK) * nbl + nbt) * 2048,
+                       live ? (int64_t)valid * 2048 : 0);
     } else if constexpr (XT) {
-      r.rb = make_rsrc32(x2b + r.k0, x2t_bytes - (uint32_t)r.k0);
+      r.rb = make_rsrc32(x2b + r.k0, live ? x2t_bytes - (uint32_t)r.k0 : 0u);
     } else {
       const int rows = K - r.k0 < kBK ? K - r.k0 : kBK;
-      r.rb = make_rsrc32(x2b + (int64_t)r.k0 * N, (uint32_t)(rows * N - n0));
+      r.rb = make_rsrc32(x2b + (int64_t)r.k0 * N, live ? (uint32_t)(rows * N - n0) : 0u);
     }
     r.tail = r.k0 + kBK > K;
     return r;
@@ -145,15 +150,14 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
     for (int j = 0; j < kAper; ++j) {
       if (j % 2 != h) continue;
       uint8_t* dst = r.st + 1024 * (wave + kWaves * j);
-      if (!r.tail) dma16(r.ra, dst, a_off[j]);
-      else dma16(r.ra, dst, r.k0 + 16 * a_chunk[j] >= K ? kOOB : a_off[j]);
+      dma16(r.ra, dst, (r.tail && r.k0 + 16 * a_chunk[j] >= K) ? kOOB : a_off[j]);
     }
 #pragma unroll
     for (int j = 0; j < kBper; ++j) {
       if (j % 2 != h) continue;
       uint8_t* dst = r.st + kAbytes + 1024 * (wave + kWaves * j);
-      if (!XT || !r.tail) dma16(r.rb, dst, b_off[j]);
-      else dma16(r.rb, dst, r.k0 + 16 * b_chunk[j] >= K ? kOOB : b_off[j]);
+      if constexpr (!XT) dma16(r.rb, dst, b_off[j]);
+      else dma16(r.rb, dst, (r.tail && r.k0 + 16 * b_chunk[j] >= K) ? kOOB : b_off[j]);
     }
   };
   auto issue = [&](int ks) {
@@ -241,19 +245,15 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
       }
     }
   };
+  static_assert(kStages == 4, "three stages ahead");
   issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 2) issue(2);
-  // stage 0 complete; the other prologue stages may stay in flight
-  if (nk > 2) stage_barrier<2 * kDma>();
-  else if (nk > 1) stage_barrier<kDma>();
-  else stage_barrier<0>();
+  issue(1);
+  issue(2);
+  stage_barrier<2 * kDma>();  // stage 0 complete; stages 1 and 2 may stay in flight
   load(smem, 0, 0);
   for (int ks = 0; ks < nk; ++ks) {
-    const bool more = ks + kStages - 1 < nk;
-    StageRsrc nr{};
-    if (more) nr = stage_rsrc(ks + kStages - 1);
-    if (ks == nk - 1) {  // no DMA left: start the epilogue's x3 reads under the last MFMAs
+    const StageRsrc nr = stage_rsrc(ks + kStages - 1);
+    if (ks == nk - 1) {  // only loads past the range left: start the epilogue's x3 reads
       prefetch_x3(0, 0);
       if (kWM > 1) prefetch_x3(1, 1);
     }
@@ -266,14 +266,7 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
       } else if (ks + 1 < nk) {
         // stage ks + 1 complete: in flight may stay stage ks + 2 and the first-half loads
         // of stage ks + 3
-        const bool full = ks + 2 < nk;
-        if (more) {
-          if (full) stage_barrier<kDma + kEarly>();
-          else stage_barrier<kEarly>();
-        } else {
-          if (full) stage_barrier<kDma>();
-          else stage_barrier<0>();
-        }
+        stage_barrier<kDma + kEarly>();
         load(smem + ((ks + 1) % kStages) * kStage, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -281,11 +274,12 @@ __global__ __launch_bounds__(64 * kGM * kGN, 1) void qm_gemm_kernel(const QmArgs
       for (int i = 0; i < kWM; ++i)
 #pragma unroll
         for (int j = 0; j < kWN; ++j) acc[i][j] = mfma32x32x32_i8(af[kk][i], bfr[kk][j], acc[i][j]);
-      if (more) issue_half(nr, kk);  // behind this step's matrix-core work
+      issue_half(nr, kk);  // behind this step's matrix-core work
     }
   }
 
   // ------------------------------------------------------------------ epilogue
+  wave_wait<0>();   // the loads past the range (zeros) have landed
   __syncthreads();
   int32_t* E = (int32_t*)smem + wave * (32 * EP);
   int32_t cb[8];
