@@ -62,6 +62,9 @@ AQ_CASES = [
     ("perchannel_bf16_i8_longk", dict(act="bf16", weight="int8", x1_shape=(256, 4096), n=256, mode="channel")),
     ("pergroup512_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(64, 2048), n=128, mode="group",
                                  group_size=512)),
+    # groups longer than the row-sum pass's 2048-k chunk: one group per chunk, the last partial
+    ("pergroup3008_fp16_i8_long", dict(act="fp16", weight="int8", x1_shape=(300, 8192), n=256, mode="group",
+                                       group_size=3008)),
     # small-m (split-k) path
     ("smallm_pergroup64_fp16_i8", dict(act="fp16", weight="int8", x1_shape=(32, 1024), n=384, mode="group",
                                        group_size=64, offset_dist=("uniform", -4, 4), with_x3=False)),
