@@ -36,11 +36,6 @@ int device_cu_count() {
 
 namespace {
 
-float code_bias(const AntiquantProblem& p) {
-  // bf16 images of int4 codes are code + 136 (see wq_device.h); all other images are exact
-  return (p.act == WQ_BF16 && p.w4) ? 136.f : 0.f;
-}
-
 // the events armed by wq_profile_next_call on this host thread
 struct ProfileHook {
   hipEvent_t before = nullptr;
@@ -133,7 +128,7 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   if (pl.small_m) {
     e = wq::launch_aq_smallm(a, s);
   } else {
-    if (pl.gsum_bytes) {  // per-group row sums first (the tiled kernel reads them per stage)
+    if (pl.gsum_bytes) {  // per-group row sums first (read by the tiled kernel's offset product)
       a.gsum = (float*)((char*)workspace + pl.partial_bytes + pl.rowsum_bytes + 2 * pl.param_bytes);
       if ((e = wq::launch_group_rowsums(a, s)) != hipSuccess) return WQ_ERR_RUNTIME;
     }

@@ -105,6 +105,8 @@ SplitPlan aq_smallm_plan(int64_t m, int k, int n, int group, bool grouped, int c
   return p;
 }
 
+float code_bias(const AntiquantProblem& p) { return (p.act == WQ_BF16 && p.w4) ? 136.f : 0.f; }
+
 AqPlan plan_antiquant(const AntiquantProblem& p, int cus) {
   AqPlan pl;
   if (p.k == 0) {
@@ -127,7 +129,10 @@ AqPlan plan_antiquant(const AntiquantProblem& p, int cus) {
     pl.rowsum_bytes = grouped ? 0 : align_up((int64_t)pl.split.splits * p.m * (int64_t)sizeof(float));
   }
   if (p.params_t) pl.param_bytes = align_up(p.groups * p.n * 2);
-  if (!pl.small_m && p.mode == QuantMode::kGroup) pl.gsum_bytes = align_up(p.groups * p.m * 4);
+  // per-group row sums S_g feed only the offset term s * (off - C) * S_g: none without an
+  // offset and with exact images
+  if (!pl.small_m && p.mode == QuantMode::kGroup && (p.has_offset || code_bias(p) != 0.f))
+    pl.gsum_bytes = align_up(p.groups * p.m * 4);
   pl.workspace = pl.partial_bytes + pl.rowsum_bytes + 2 * pl.param_bytes + pl.gsum_bytes;
   return pl;
 }

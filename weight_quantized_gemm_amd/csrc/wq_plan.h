@@ -53,6 +53,9 @@ struct AqPlan {
   int64_t workspace = 0;
 };
 AqPlan plan_antiquant(const AntiquantProblem& p, int cus);
+// C, the constant the fed weight images add to the codes: bf16 images of int4 codes are
+// code + 136 (the magic-exponent image, wq_device.h); all other images are exact.
+float code_bias(const AntiquantProblem& p);
 
 struct QmPlan {
   SplitPlan split;

@@ -27,6 +27,7 @@ struct AntiquantProblem {
   const void* bias = nullptr;    // may be null
   const void* x3 = nullptr;      // may be null
   void* out = nullptr;
+  bool has_offset = false;       // an offset tensor is given
 };
 
 struct QuantProblem {

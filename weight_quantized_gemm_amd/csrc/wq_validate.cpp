@@ -200,6 +200,7 @@ int validate_antiquant(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor
     p->group = group; p->groups = groups;
     p->x1 = x1->data; p->x2 = x2->data; p->scale = scale->data;
     p->offset = offset ? offset->data : nullptr;
+    p->has_offset = offset != nullptr;
     p->bias = bias ? bias->data : nullptr;
     p->x3 = x3 ? x3->data : nullptr;
     p->out = output->data;
