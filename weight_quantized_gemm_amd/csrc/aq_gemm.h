@@ -44,6 +44,8 @@
 // This header holds the kernel templates; aq_gemm_int8.hip, aq_gemm_int4.hip and
 // aq_gemm_fp8.hip instantiate them, one weight format per translation unit.
 #pragma once
+#include <type_traits>
+
 #include "wq_kernels.h"
 #include "wq_pipeline.h"
 
@@ -439,78 +441,89 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   // ---------------------------------------------------------------- main loop
   constexpr int S = T::Stages;
   for (int ks = 0; ks < S - 1; ++ks) issue(ks);
-  for (int ks = 0; ks < nk; ++ks) {
-    // stage ks is complete once only the S - 2 stages issued after it may still be in flight
-    if (has_b && has_p) stage_barrier<(kOwnA + kOwnB + kOwnP) * (S - 2)>();
-    else if (has_b) stage_barrier<(kOwnA + kOwnB) * (S - 2)>();
-    else if (has_p) stage_barrier<(kOwnA + kOwnP) * (S - 2)>();
-    else stage_barrier<kOwnA * (S - 2)>();
-    const StageRsrc nr = stage_rsrc(ks + S - 1);
-    if (ks == nk - 1) {  // only loads past the range left: start the epilogue's x3 reads
-      prefetch_x3(0, 0);
-      if (XP > 1 && WM > 1) prefetch_x3(1, 1 % XP);
-    }
+  // The k loop, in two versions: with the per-channel row sums (RS) where the offset term
+  // needs them, without where that term is zero (no offset and exact images, C = 0).
+  auto k_loop = [&](auto rs_c) {
+    constexpr bool RS = decltype(rs_c)::value;
+    for (int ks = 0; ks < nk; ++ks) {
+      // stage ks is complete once only the S - 2 stages issued after it may still be in flight
+      if (has_b && has_p) stage_barrier<(kOwnA + kOwnB + kOwnP) * (S - 2)>();
+      else if (has_b) stage_barrier<(kOwnA + kOwnB) * (S - 2)>();
+      else if (has_p) stage_barrier<(kOwnA + kOwnP) * (S - 2)>();
+      else stage_barrier<kOwnA * (S - 2)>();
+      const StageRsrc nr = stage_rsrc(ks + S - 1);
+      if (ks == nk - 1) {  // only loads past the range left: start the epilogue's x3 reads
+        prefetch_x3(0, 0);
+        if (XP > 1 && WM > 1) prefetch_x3(1, 1 % XP);
+      }
 
-    const uint8_t* As = smem + (ks % T::Stages) * T::Stage;
-    const uint8_t* Bs = As + T::Abytes;
-    // Fragments are double-buffered across the four 16-k steps: the reads of step kk + 1
-    // are issued before the MFMAs of step kk, so LDS latency hides behind them.
-    Frag<WM, T::Reads> f0, f1;
-    load_frag<T, WM>(As, Bs, 0, wm, wn, lane, f0);
+      const uint8_t* As = smem + (ks % T::Stages) * T::Stage;
+      const uint8_t* Bs = As + T::Abytes;
+      // Fragments are double-buffered across the four 16-k steps: the reads of step kk + 1
+      // are issued before the MFMAs of step kk, so LDS latency hides behind them.
+      Frag<WM, T::Reads> f0, f1;
+      load_frag<T, WM>(As, Bs, 0, wm, wn, lane, f0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      Frag<WM, T::Reads>& cur = (kk & 1) ? f1 : f0;
-      Frag<WM, T::Reads>& nxt = (kk & 1) ? f0 : f1;
-      if (kk < 3) load_frag<T, WM>(As, Bs, kk + 1, wm, wn, lane, nxt);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!GROUPED) {
+      for (int kk = 0; kk < 4; ++kk) {
+        Frag<WM, T::Reads>& cur = (kk & 1) ? f1 : f0;
+        Frag<WM, T::Reads>& nxt = (kk & 1) ? f0 : f1;
+        if (kk < 3) load_frag<T, WM>(As, Bs, kk + 1, wm, wn, lane, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!GROUPED && RS) {
 #pragma unroll
-        for (int t = 0; t < SB; ++t) {
-          // sb0 is a constant and t an unrolled index: the block is chosen at compile time
-          constexpr int kLast = WM - 1;
-          const int blk = sb0 + t < WM ? sb0 + t : kLast;
-          if (sb0 + t < WM) {
+          for (int t = 0; t < SB; ++t) {
+            // sb0 is a constant and t an unrolled index: the block is chosen at compile time
+            constexpr int kLast = WM - 1;
+            const int blk = sb0 + t < WM ? sb0 + t : kLast;
+            if (sb0 + t < WM) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ssum[t] = dot2_ones<BF16>(cur.a[blk][q], ssum[t]);
+              for (int q = 0; q < 4; ++q) ssum[t] = dot2_ones<BF16>(cur.a[blk][q], ssum[t]);
+            }
+          }
+        }
+        u32x4_t bfr[WN];
+#pragma unroll
+        for (int j = 0; j < T::Reads; ++j) {
+          if constexpr (W4 && (XT || PK)) bfr[j] = i4x8_k_to_act<BF16>(cur.raw[j][0]);
+          else if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
+          else bfr[j] = w8x8_to_act<BF16, WF>(cur.raw[j]);
+        }
+        // Per-group: a group's first 16-k step (group starts fall on multiples of 32, so on
+        // steps 0 and 2; k is counted from the split's start, a group boundary) starts its
+        // accumulators from zero through the MFMA's own operand instead of clearing them
+        // after the previous group's fold.
+        bool fresh = false;
+        if constexpr (GROUPED) {
+          if (kk % 2 == 0) fresh = (ks * kBK + kk * 16) % a.group == 0;
+        }
+        if (fresh) {
+#pragma unroll
+          for (int i = 0; i < WM; ++i)
+#pragma unroll
+            for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], f32x16_t{});
+        } else {
+#pragma unroll
+          for (int i = 0; i < WM; ++i)
+#pragma unroll
+            for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], acc[i][j]);
+        }
+        issue_step(nr, kk);  // behind this step's matrix-core work
+
+        if constexpr (GROUPED) {
+          if (kk & 1) {  // groups end on multiples of 32
+            const int kdone = ks * kBK + kk * 16 + 16;
+            if (kdone <= klen && (kdone % a.group == 0 || kdone == klen))
+              rescale((const uint16_t*)(Bs + T::Bbytes), kk >> 1);
           }
         }
       }
-      u32x4_t bfr[WN];
-#pragma unroll
-      for (int j = 0; j < T::Reads; ++j) {
-        if constexpr (W4 && (XT || PK)) bfr[j] = i4x8_k_to_act<BF16>(cur.raw[j][0]);
-        else if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
-        else bfr[j] = w8x8_to_act<BF16, WF>(cur.raw[j]);
-      }
-      // Per-group: a group's first 16-k step (group starts fall on multiples of 32, so on
-      // steps 0 and 2; k is counted from the split's start, a group boundary) starts its
-      // accumulators from zero through the MFMA's own operand instead of clearing them
-      // after the previous group's fold.
-      bool fresh = false;
-      if constexpr (GROUPED) {
-        if (kk % 2 == 0) fresh = (ks * kBK + kk * 16) % a.group == 0;
-      }
-      if (fresh) {
-#pragma unroll
-        for (int i = 0; i < WM; ++i)
-#pragma unroll
-          for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], f32x16_t{});
-      } else {
-#pragma unroll
-        for (int i = 0; i < WM; ++i)
-#pragma unroll
-          for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16<BF16>(cur.a[i], bfr[j], acc[i][j]);
-      }
-      issue_step(nr, kk);  // behind this step's matrix-core work
-
-      if constexpr (GROUPED) {
-        if (kk & 1) {  // groups end on multiples of 32
-          const int kdone = ks * kBK + kk * 16 + 16;
-          if (kdone <= klen && (kdone % a.group == 0 || kdone == klen))
-            rescale((const uint16_t*)(Bs + T::Bbytes), kk >> 1);
-        }
-      }
     }
+  };
+  if constexpr (GROUPED) {
+    k_loop(std::false_type{});
+  } else {
+    if (a.offset != nullptr || cbias != 0.f) k_loop(std::true_type{});
+    else k_loop(std::false_type{});  // the row sums stay zero: the term they feed is zero
   }
 
   offset_product();
