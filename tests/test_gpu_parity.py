@@ -62,6 +62,17 @@ AQ_CASES = [
     ("perchannel_bf16_i8_longk", dict(act="bf16", weight="int8", x1_shape=(256, 4096), n=256, mode="channel")),
     ("pergroup512_bf16_i8", dict(act="bf16", weight="int8", x1_shape=(64, 2048), n=128, mode="group",
                                  group_size=512)),
+    # no offset: the row sums' term is s * (0 - C) * S, non-zero for bf16 images of int4
+    # codes (C = 136), so those keep the sums (per-channel in the k loop, per-group in the
+    # pass before the product); exact images (C = 0) skip them
+    ("nooff_perchannel_bf16_i4_c136", dict(act="bf16", weight="int4", x1_shape=(300, 512), n=256,
+                                           mode="channel", with_offset=False)),
+    ("nooff_pergroup128_bf16_i4_c136", dict(act="bf16", weight="int4", x1_shape=(300, 1024), n=256,
+                                            mode="group", group_size=128, with_offset=False)),
+    ("nooff_pergroup64_bf16_i8_exact", dict(act="bf16", weight="int8", x1_shape=(300, 1024), n=256,
+                                            mode="group", group_size=64, with_offset=False)),
+    ("nooff_pergroup96_fp16_i4_exact_splitk", dict(act="fp16", weight="int4", x1_shape=(100, 2304), n=384,
+                                                   mode="group", group_size=96, with_offset=False)),
     # groups longer than the row-sum pass's 2048-k chunk: one group per chunk, the last partial
     ("pergroup3008_fp16_i8_long", dict(act="fp16", weight="int8", x1_shape=(300, 8192), n=256, mode="group",
                                        group_size=3008)),
