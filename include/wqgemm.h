@@ -143,9 +143,8 @@ int wq_antiquant_matmul_get_workspace_size(const wq_tensor* x1, const wq_tensor*
  * kernel of the same call has added them in split order -- at m <= 32 when k > 1024, and at
  * larger m when the output tiles alone would leave compute units idle; per-group scale and
  * offset given transposed, copied row-major; and, per-group with m > 32 when an offset is
- * given or the weight images carry a bias (bf16 activations with int4 weights) and one k
- * split holds more than 64 groups, the fp32 row sums of x1 over each group, (groups, m),
- * written before the product (with 64 groups or fewer the product kernel sums them itself).
+ * given or the weight images carry a bias (bf16 activations with int4 weights), the fp32
+ * row sums of x1 over each group, (groups, m), written before the product.
  */
 int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tensor* bias,
                         const wq_tensor* antiquant_scale, const wq_tensor* antiquant_offset,

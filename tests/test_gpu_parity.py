@@ -76,9 +76,8 @@ AQ_CASES = [
     # groups of 3008 k: three splits of one group each, the last partial
     ("pergroup3008_fp16_i8_long", dict(act="fp16", weight="int8", x1_shape=(300, 8192), n=256, mode="group",
                                        group_size=3008)),
-    # the tiled kernel sums the per-group row sums itself up to 64 groups per k split, and a
-    # pass before it sums them beyond: 5 x 32 tiles fill the CUs without a split, so k = 2048
-    # (64 groups of 32) takes the kernel's sums and k = 2304 (72 groups) the pass
+    # many short groups on wide tiles without a k split (5 x 32 tiles fill the CUs): 64 groups
+    # of 32 with bf16 images of int4 codes (C = 136, no offset), 72 groups with an offset
     ("pergroup32_bf16_i4_sg64", dict(act="bf16", weight="int4", x1_shape=(520, 2048), n=8192, mode="group",
                                      group_size=32, with_offset=False, scale_dist=("uniform", 0.01, 0.05))),
     ("pergroup32_fp16_i8_pass72", dict(act="fp16", weight="int8", x1_shape=(520, 2304), n=8192, mode="group",

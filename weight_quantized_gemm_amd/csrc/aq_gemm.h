@@ -20,10 +20,9 @@
 // load (which would also wait for every stage in flight).  The offset part,
 // sum_g s[g,n] * (off[g,n] - C) * S_g[m], is a product of depth G between the per-group row
 // sums of x1 and the parameter rows: it runs once per tile after the k loop, on the matrix
-// cores in fp32.  The S_g are summed in the k loop from the x1 fragments (SG), one wave per
-// SIMD summing one 32-row block, into an LDS region of kSgMaxGroups groups per tile row;
-// a split with more groups takes them from a pass before the product instead
-// (group_rowsums_kernel, aq_prep.hip).
+// cores in fp32.  The S_g come from a pass before the product (group_rowsums_kernel,
+// aq_prep.hip): summed in the k-loop they cost every wave of a row band the same work,
+// about a sixth of the kernel's time.
 //
 // Pipeline: GM x GN waves, wave tile (32*WM) x (32*WN), workgroup tile (32*WM*GM) x (32*WN*GN),
 // BK = 64.  Operands travel global -> LDS by direct-to-LDS buffer loads
@@ -59,9 +58,7 @@ constexpr int kArow = 128;                 // bytes per x1 row in a stage (64 x 
 // XT: the weights are stored transposed, (n, k) (int4: (n, k/2) bytes packed along k).
 // PK: the weights are in the packed layout (wq_prepack_weight): 64 k x 32 column blocks in
 // MFMA B-fragment order.
-// SG: per-group row sums S_g summed in the k loop into an LDS region after the stages.
-template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false, bool PK = false,
-          bool SG = false>
+template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false, bool PK = false>
 struct Tile {
   static constexpr int Waves = GM * GN;              // wave grid GM x GN
   static constexpr int Threads = 64 * Waves;
@@ -96,18 +93,14 @@ struct Tile {
   // one 8-byte (int4: 4-byte) read per block from transposed weights
   static constexpr int Reads = (W4 && !XT && !PK) ? WN / 2 : WN;
   // LDS layout: stages (x1 | weights | group scale / offset rows) | per-channel S rows
-  // (BM fp32) or, with SG, the per-group S_g ([kSgMaxGroups][BM] fp32).  As many stages as
-  // fit (3 to 6): a deeper pipeline hides more load latency where a stage is small.
-  static constexpr bool SGsum = GROUPED && SG;
-  static constexpr int Extra = SGsum ? kSgMaxGroups * BM * 4 : BM * 4;
+  // (BM fp32).  As many stages as fit (3 to 6): a deeper pipeline hides more load
+  // latency where a stage is small.
+  static constexpr int Extra = BM * 4;
   static constexpr int FitStages = (160 * 1024 - Extra) / Stage;
   static constexpr int Stages = FitStages > 6 ? 6 : FitStages;
   static constexpr int SOff = Stages * Stage;
-  static constexpr int Total = SOff + Extra;
+  static constexpr int Total = SOff + BM * 4;
   static_assert(Stages >= 3, "at least three stages");
-  static_assert(Waves * 32 * (32 * WN + 8) * 4 <= SOff, "the epilogue's staging rows fit in the stages");
-  static_assert(!SG || GROUPED, "S_g are per-group row sums");
-  static_assert(!SG || GM * WM <= GN, "one S_g row block per wave at most");
   static_assert(BM == 64 || BM == 128 || BM == 256, "x1 stage holds 64, 128 or 256 rows");
   static_assert(Ablocks % Waves == 0, "x1 DMA blocks split evenly over the waves");
   static_assert(Bblocks % Waves == 0 || Bblocks < Waves, "weight DMA blocks split");
@@ -171,10 +164,10 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
 
 // The kernel body, specialised on the wave's column index WNI in the GM x GN wave grid:
 // column offsets and the per-channel row-sum block become compile-time constants.
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT, bool PK, bool SG, int WNI>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT, bool PK, int WNI>
 __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int wave) {
   constexpr bool W4 = WF == kWInt4;
-  using T = Tile<W4, GM, GN, WM, WN, GROUPED, XT, PK, SG>;
+  using T = Tile<W4, GM, GN, WM, WN, GROUPED, XT, PK>;
   constexpr int BN = T::BN, RB = T::RB, WC = T::WCols;
   const int lane = threadIdx.x & 63;
   const int wm = wave / GN;
@@ -245,14 +238,8 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
     rsc = make_rsrc((const uint8_t*)a.scale + 2 * (int64_t)n0, pbytes);
     rof = has_offset ? make_rsrc((const uint8_t*)a.offset + 2 * (int64_t)n0, pbytes) : rsc;
   }
-  // per-group: the S_g, read after the k loop, from the pass's (groups, m) fp32 workspace
-  // or (SG) from the tile's LDS region [group of the split][BM], which the wave of column
-  // wn fills for row block wn % WM of row band wn / WM (one summing wave per SIMD)
+  // per-group: the precomputed S_g, (groups, m) fp32, read after the k loop
   const float* gsum = a.gsum;
-  float* const sg_lds = (float*)(smem + T::SOff);
-  constexpr int sg_blk = WNI % WM;
-  const bool sg_wave = T::SGsum && wm == WNI / WM;
-  float sg = 0.f;
   // loads this wave issues per stage (the parameter wave: 2 parameter-row loads)
   constexpr int kOwnA = T::Aper, kOwnB = T::Bper, kOwnP = GROUPED ? 2 : 0;
   const bool has_b = wave < T::Bwaves, has_p = GROUPED && wave == T::Pwave;
@@ -404,10 +391,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
         const bool gv = gl < g1;
         float av[WM], bv[WN];
 #pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          if constexpr (T::SGsum) av[i] = gv ? sg_lds[(gl - g0) * T::BM + wm * (32 * WM) + 32 * i + (lane & 31)] : 0.f;
-          else av[i] = (gv && rows[i] < M) ? gsum[(int64_t)gl * M + rows[i]] : 0.f;
-        }
+        for (int i = 0; i < WM; ++i) av[i] = (gv && rows[i] < M) ? gsum[(int64_t)gl * M + rows[i]] : 0.f;
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           float q = 0.f;
@@ -497,12 +481,6 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
             }
           }
         }
-        if constexpr (GROUPED && RS) {
-          if (sg_wave) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sg = dot2_ones<BF16>(cur.a[sg_blk][q], sg);
-          }
-        }
         u32x4_t bfr[WN];
 #pragma unroll
         for (int j = 0; j < T::Reads; ++j) {
@@ -532,27 +510,17 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
         issue_step(nr, kk);  // behind this step's matrix-core work
 
         if constexpr (GROUPED) {
-          if (kk & 1) {  // groups end on multiples of 32 (k is one too)
+          if (kk & 1) {  // groups end on multiples of 32
             const int kdone = ks * kBK + kk * 16 + 16;
-            if (kdone <= klen && (kdone % a.group == 0 || kdone == klen)) {
+            if (kdone <= klen && (kdone % a.group == 0 || kdone == klen))
               rescale((const uint16_t*)(Bs + T::Bbytes), kk >> 1);
-              if constexpr (RS) {
-                if (sg_wave) {  // the group's row sums: the two lane halves hold k halves
-                  const float v = sg + __shfl_xor(sg, 32, 64);
-                  const int gi = (kdone - 1) / a.group;  // group of the split
-                  if (lane < 32) sg_lds[gi * T::BM + wm * (32 * WM) + 32 * sg_blk + lane] = v;
-                  sg = 0.f;
-                }
-              }
-            }
           }
         }
       }
     }
   };
   if constexpr (GROUPED) {
-    k_loop(std::integral_constant<bool, T::SGsum>{});
-    if constexpr (T::SGsum) __syncthreads();  // every wave's S_g are in LDS
+    k_loop(std::false_type{});
   } else {
     if (a.offset != nullptr || cbias != 0.f) k_loop(std::true_type{});
     else k_loop(std::false_type{});  // the row sums stay zero: the term they feed is zero
@@ -661,7 +629,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
   }
 }
 
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT, bool PK, bool SG>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT, bool PK>
 __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
@@ -669,7 +637,7 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #define WQ_WAVE_COLUMN(c)                                                      \
   if constexpr (GN > c) {                                                     \
     if (wn == c) {                                                            \
-      aq_gemm_body<BF16, WF, GM, GN, WM, WN, GROUPED, XT, PK, SG, c>(a, smem, wave); \
+      aq_gemm_body<BF16, WF, GM, GN, WM, WN, GROUPED, XT, PK, c>(a, smem, wave); \
       return;                                                                 \
     }                                                                         \
   }
@@ -678,21 +646,18 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void aq_gemm_kernel(const AqArgs a
 #undef WQ_WAVE_COLUMN
 }
 
-template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false, bool PK = false,
-          bool SG = false>
+template <bool BF16, int WF, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false, bool PK = false>
 hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   static_assert(GN <= 8, "wave grids have at most 8 columns");
-  using T = Tile<WF == kWInt4, GM, GN, WM, WN, GROUPED, XT, PK, SG>;
+  using T = Tile<WF == kWInt4, GM, GN, WM, WN, GROUPED, XT, PK>;
   AqArgs a = a0;
-  // the S_g region holds kSgMaxGroups groups of a split (the planner's rule)
-  if (SG && (a.kchunk + a.group - 1) / a.group > kSgMaxGroups) return hipErrorInvalidValue;
   a.tiles_m = (int)((a.m + T::BM - 1) / T::BM);
   a.tiles_n = (a.n + T::BN - 1) / T::BN;
   // operand bytes per tile row (x1) and per tile column (weights) over the k range
   a.xcd_rm = xcd_region_rows(a.tiles_m, a.tiles_n, (double)T::BM * a.kchunk * 2.0,
                              (double)T::BN * a.kchunk * (WF == kWInt4 ? 0.5 : 1.0));
   const size_t lds = (size_t)T::Total;
-  auto kern = aq_gemm_kernel<BF16, WF, GM, GN, WM, WN, GROUPED, XT, PK, SG>;
+  auto kern = aq_gemm_kernel<BF16, WF, GM, GN, WM, WN, GROUPED, XT, PK>;
   hipError_t e = raise_lds_limit((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
@@ -700,14 +665,6 @@ hipError_t launch_one(const AqArgs& a0, hipStream_t stream) {
   e = launch_main((const void*)kern, dim3((unsigned)blocks, (unsigned)splits), dim3(T::Threads), lds, stream, &a);
   if (e != hipSuccess) return e;
   return splits > 1 ? launch_aq_splitk_finish(a, stream) : hipSuccess;
-}
-
-// Per-group tiles (2x4 waves of (32 WM) x 64), with the S_g summed in the kernel (a.sg_lds)
-// or read from the pass's workspace.
-template <bool BF16, int WF, int WM, bool XT, bool PK>
-hipError_t launch_grouped(const AqArgs& a, hipStream_t stream) {
-  if (a.sg_lds) return launch_one<BF16, WF, 2, 4, WM, 2, true, XT, PK, true>(a, stream);
-  return launch_one<BF16, WF, 2, 4, WM, 2, true, XT, PK, false>(a, stream);
 }
 
 // Tile configurations (wave grid GM x GN, blocks per wave WM x WN).  The matrix cores and
@@ -728,8 +685,8 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   if (a.x2p) {  // packed weights
     if constexpr (kGroupedOk) {
       if (a.grouped) {
-        if (tiny_m) return launch_grouped<BF16, WF, 1, false, true>(a, stream);
-        return launch_grouped<BF16, WF, 2, false, true>(a, stream);
+        if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true, false, true>(a, stream);
+        return launch_one<BF16, WF, 2, 4, 2, 2, true, false, true>(a, stream);
       }
     }
     if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, false, false, true>(a, stream);
@@ -739,8 +696,8 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   if (a.x2t) {  // transposed weights
     if constexpr (kGroupedOk) {
       if (a.grouped) {
-        if (tiny_m) return launch_grouped<BF16, WF, 1, true, false>(a, stream);
-        return launch_grouped<BF16, WF, 2, true, false>(a, stream);
+        if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true, true>(a, stream);
+        return launch_one<BF16, WF, 2, 4, 2, 2, true, true>(a, stream);
       }
     }
     if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, false, true>(a, stream);
@@ -749,8 +706,8 @@ hipError_t launch_mode(const AqArgs& a, hipStream_t stream) {
   }
   if constexpr (kGroupedOk) {
     if (a.grouped) {
-      if (tiny_m) return launch_grouped<BF16, WF, 1, false, false>(a, stream);
-      return launch_grouped<BF16, WF, 2, false, false>(a, stream);
+      if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, true>(a, stream);
+      return launch_one<BF16, WF, 2, 4, 2, 2, true>(a, stream);
     }
   }
   if (tiny_m) return launch_one<BF16, WF, 2, 4, 1, 2, false>(a, stream);

@@ -104,7 +104,6 @@ int wq_antiquant_matmul(const wq_tensor* x1, const wq_tensor* x2, const wq_tenso
   a.splits = pl.split.splits;
   a.kchunk = pl.split.kchunk;
   a.bm = pl.bm;
-  a.sg_lds = pl.sg_in_kernel;
 
   hipError_t e;
   if (pl.param_bytes) {

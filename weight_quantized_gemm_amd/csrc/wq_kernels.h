@@ -18,7 +18,7 @@ struct AqArgs {
   void* out;             // (m, n)
   float* partial;        // split k: partial products [splits][m][n] (per-group: folded)
   float* rowsum_part;    // split k, per-tensor / per-channel: row sums of x1 [splits][m]
-  float* gsum;           // large-m per-group path without sg_lds: row sums of x1 per group, (groups, m)
+  float* gsum;           // large-m per-group path: row sums of x1 per group, (groups, m)
   int64_t m;
   int32_t k, n;
   int32_t group;         // group size along k (per-group); k otherwise
@@ -32,7 +32,6 @@ struct AqArgs {
   bool bf16, w4, f8, grouped, per_tensor;  // f8: FLOAT8_E4M3FN weights
   bool x2t;              // x2 stored transposed: (n, k) (int4: (n, k/2) bytes along k)
   bool x2p;              // x2 in the packed layout (wq_prepack_weight)
-  bool sg_lds;           // large-m per-group: the tiled kernel sums S_g itself (AqPlan::sg_in_kernel)
 };
 
 // W8A8 matmul.

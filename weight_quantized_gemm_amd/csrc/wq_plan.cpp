@@ -130,13 +130,9 @@ AqPlan plan_antiquant(const AntiquantProblem& p, int cus) {
   }
   if (p.params_t) pl.param_bytes = align_up(p.groups * p.n * 2);
   // per-group row sums S_g feed only the offset term s * (off - C) * S_g: none without an
-  // offset and with exact images.  The tiled kernel sums them itself where a split's groups
-  // fit its LDS region; otherwise a pass computes them into the workspace.
-  if (!pl.small_m && grouped && (p.has_offset || code_bias(p) != 0.f)) {
-    const int64_t split_groups = (pl.split.kchunk + p.group - 1) / p.group;
-    if (split_groups <= kSgMaxGroups) pl.sg_in_kernel = true;
-    else pl.gsum_bytes = align_up(p.groups * p.m * 4);
-  }
+  // offset and with exact images
+  if (!pl.small_m && p.mode == QuantMode::kGroup && (p.has_offset || code_bias(p) != 0.f))
+    pl.gsum_bytes = align_up(p.groups * p.m * 4);
   pl.workspace = pl.partial_bytes + pl.rowsum_bytes + 2 * pl.param_bytes + pl.gsum_bytes;
   return pl;
 }

@@ -20,10 +20,6 @@ constexpr int kSmWaves = 8;       // small-m kernel: waves per workgroup
 constexpr int kSmSlab = 128;      // small-m kernel: columns per workgroup
 constexpr int kSmRows = 64;       // small-m kernel: k rows per block (a wave's unit of work)
 constexpr int64_t kSmallM = 32;   // the small-m kernel serves m <= 32
-// Large m, per-group: the tiled kernel sums the per-group row sums S_g of x1 itself, into
-// LDS, when one k split holds at most this many groups; with more, a pass before the
-// product computes them into the workspace.
-constexpr int kSgMaxGroups = 64;
 
 struct SplitPlan {
   int kchunk = 64;   // k rows per split (a multiple of 64)
@@ -53,8 +49,7 @@ struct AqPlan {
   int64_t partial_bytes = 0;
   int64_t rowsum_bytes = 0;
   int64_t param_bytes = 0;   // per-group scale / offset given transposed: row-major copies
-  bool sg_in_kernel = false; // large m, per-group: S_g summed by the tiled kernel (kSgMaxGroups)
-  int64_t gsum_bytes = 0;    // large m, per-group, S_g from the pass: (groups, m) fp32
+  int64_t gsum_bytes = 0;    // large m, per-group: row sums of x1 per group, (groups, m) fp32
   int64_t workspace = 0;
 };
 AqPlan plan_antiquant(const AntiquantProblem& p, int cus);
