@@ -180,9 +180,11 @@ int wq_antiquant_matmul_noalloc(const wq_tensor* x1, const wq_tensor* x2, const 
  *   the (k, n) weight is cut into blocks of 64 k x 32 columns, stored block row by block row
  *   (k blocks outer, n blocks inner); a block holds, for each of its four 16-k steps s, the
  *   64 lanes of an MFMA B fragment in lane order: lane l is column l % 32 and k
- *   16 s + 8 (l / 32) + 0 .. 7, i.e. 8 codes, k ascending -- 8 bytes (int8, FLOAT8_E4M3FN)
- *   or 4 bytes (int4: two nibbles a byte, the even k in bits 0-3).  Blocks are 2048 bytes
- *   (1024 for int4); codes of k >= k (a final half block) are zero.
+ *   16 s + 8 (l / 32) + 0 .. 7, i.e. 8 codes, k ascending, one byte each (int8,
+ *   FLOAT8_E4M3FN): 2048-byte blocks.  int4 blocks are stored in pairs (2p, 2p + 1) as one
+ *   2048-byte unit of the same order, each byte holding both blocks' codes at its lane's
+ *   column and k, block 2p's in bits 0-3 (n is a multiple of 64).  Codes of k >= k (a final
+ *   half block) are zero.
  * Every B fragment the kernels need is then one contiguous run of bytes.
  *
  * wq_prepack_weight_get_size: the packed size in bytes of x2 (WQ_I8, WQ_I4 or WQ_F8E4M3,

@@ -3,8 +3,9 @@
 A (k, n) weight is cut into 64 k x 32 column blocks, k blocks outer, n blocks inner.  A block
 holds, for each 16-k step s (0..3), the codes of 64 lanes in lane order: lane l is column
 l % 32 and k 16 s + 8 (l // 32) + e for e = 0..7.  One-byte codes (int8, FLOAT8_E4M3FN) take
-8 bytes per lane (e ascending); int4 codes take 4 bytes per lane, two nibbles a byte, the
-even e in bits 0-3.  Codes at k past the end are zero.  This layout is the library's own
+8 bytes per lane (e ascending).  int4 blocks go in pairs (2p, 2p + 1), stored as one 2048-byte
+unit of the same lane order: byte e of a lane holds the codes of both blocks at that lane's
+column and k, block 2p in bits 0-3.  Codes at k past the end are zero.  This layout is the library's own
 (include/wqgemm.h describes it); these helpers are test infrastructure.
 """
 import numpy as np
@@ -38,16 +39,15 @@ def pack_reference(codes, int4):
     t = c.reshape(kb, 4, 2, 8, nb, 32).transpose(0, 4, 1, 2, 5, 3)
     if not int4:
         return (t & 0xFF).astype(np.uint8).reshape(-1)
+    # column blocks 2p and 2p + 1 share the bytes of pair p: [kb][p][s][h][col][e]
     nib = (t & 0xF).astype(np.uint8)
-    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8).reshape(-1)
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8).reshape(-1)
 
 
 def unpack_reference(packed, k, n, int4):
     """The inverse, element by element (a loop over the layout's definition, for small
     shapes)."""
     packed = np.asarray(packed, dtype=np.uint8)
-    lane_bytes = 4 if int4 else 8
-    block = 64 * 4 * lane_bytes
     out = np.zeros((k, n), dtype=np.int64)
     for kk in range(k):
         for col in range(n):
@@ -55,11 +55,11 @@ def unpack_reference(packed, k, n, int4):
             s, r = divmod(kr, 16)
             h, e = divmod(r, 8)
             lane = 32 * h + col % 32
-            base = (kb * (n // 32) + col // 32) * block + (s * 64 + lane) * lane_bytes
-            if int4:
-                byte = int(packed[base + e // 2])
-                v = (byte >> (4 * (e % 2))) & 0xF
+            if int4:   # 2048-byte units of two column blocks, n // 64 per k block
+                base = (kb * (n // 64) + col // 64) * 2048 + (s * 64 + lane) * 8
+                v = (int(packed[base + e]) >> (4 * ((col // 32) % 2))) & 0xF
                 out[kk, col] = v - 16 if v >= 8 else v
             else:
+                base = (kb * (n // 32) + col // 32) * 2048 + (s * 64 + lane) * 8
                 out[kk, col] = int(packed[base + e])
     return out

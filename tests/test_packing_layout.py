@@ -48,12 +48,21 @@ def test_pack_hand_positions():
 
 
 def test_pack_int4_nibble_order():
-    """int4: the even k of a lane's pair of codes sits in bits 0-3 of its byte."""
-    codes = np.zeros((64, 64), dtype=np.int64)
-    codes[0, 0], codes[1, 0], codes[2, 0] = 3, -2, 7     # lane 0, step 0, e = 0, 1, 2
+    """int4: a byte holds one k of a lane's column in both blocks of a pair, the even block's
+    code in bits 0-3; one byte per k, k ascending (positions worked out by hand)."""
+    codes = np.zeros((64, 128), dtype=np.int64)
+    codes[0, 0], codes[0, 32], codes[1, 0] = 3, -2, 7     # lane 0, step 0: e = 0 (both blocks), e = 1
+    codes[8, 1], codes[8, 33] = 5, -8                     # lane 33 (column 1, k 8..15), e = 0
+    codes[63, 31] = -1                                    # step 3, lane 63 (column 31, k 56..63), e = 7
+    codes[0, 64], codes[2, 96] = 6, 1                     # the second pair (columns 64..127) at 2048
     p = pack_reference(codes, True)
+    assert p.size == 4096
     assert p[0] == (3 | ((-2 & 0xF) << 4))
     assert p[1] == 7
+    assert p[33 * 8] == (5 | (8 << 4))
+    assert p[(3 * 64 + 63) * 8 + 7] == 0xF
+    assert p[2048] == 6 and p[2048 + 2] == (1 << 4)
+    assert int(np.count_nonzero(p)) == 6                   # columns 0 and 32 share byte 0
 
 
 def test_logical_codes_int4_layouts():

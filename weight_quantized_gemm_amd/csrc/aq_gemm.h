@@ -57,7 +57,7 @@ constexpr int kArow = 128;                 // bytes per x1 row in a stage (64 x 
 
 // XT: the weights are stored transposed, (n, k) (int4: (n, k/2) bytes packed along k).
 // PK: the weights are in the packed layout (wq_prepack_weight): 64 k x 32 column blocks in
-// MFMA B-fragment order.
+// MFMA B-fragment order, int4 blocks in pairs that share each byte.
 template <bool W4, int GM, int GN, int WM, int WN, bool GROUPED, bool XT = false, bool PK = false>
 struct Tile {
   static constexpr int Waves = GM * GN;              // wave grid GM x GN
@@ -86,12 +86,12 @@ struct Tile {
   static constexpr int WCols = 32 * WN;              // logical columns per wave
   static constexpr bool XTile = XT;
   static constexpr bool PKed = PK;
-  // packed weights: bytes of a 64 k x 32 column block, and of one lane's codes of a 16-k step
+  // packed weights: bytes of a 64 k x 32 column block; a B fragment read takes 8 bytes per
+  // lane from a 2048-byte unit (a block of one-byte codes, a pair of int4 blocks)
   static constexpr int PkBlock = W4 ? 1024 : 2048;
-  static constexpr int PkLane = W4 ? 4 : 8;
-  // B fragment reads per wave per 16-k step: tr8 reads (an int4 one feeds two blocks), or
-  // one 8-byte (int4: 4-byte) read per block from transposed weights
-  static constexpr int Reads = (W4 && !XT && !PK) ? WN / 2 : WN;
+  // B fragment reads per wave per 16-k step: int4 row-major (tr8) and packed reads feed two
+  // blocks each; one-byte codes and transposed int4 (4-byte reads) one block each
+  static constexpr int Reads = (W4 && !XT) ? WN / 2 : WN;
   // LDS layout: stages (x1 | weights | group scale / offset rows) | per-channel S rows
   // (BM fp32).  As many stages as fit (3 to 6): a deeper pipeline hides more load
   // latency where a stage is small.
@@ -105,7 +105,7 @@ struct Tile {
   static_assert(Ablocks % Waves == 0, "x1 DMA blocks split evenly over the waves");
   static_assert(Bblocks % Waves == 0 || Bblocks < Waves, "weight DMA blocks split");
   static_assert(Win >= 1 && Win <= 4, "weight row bytes 64..256");
-  static_assert(!W4 || XT || PK || WN % 2 == 0, "an int4 tr8 read feeds an even and an odd block");
+  static_assert(!W4 || XT || WN % 2 == 0, "an int4 read feeds an even and an odd block");
   static_assert(!(XT && PK), "one weight layout");
 };
 
@@ -127,14 +127,11 @@ __device__ __forceinline__ void load_frag(const uint8_t* As, const uint8_t* Bs, 
     f.a[i] = *(const u32x4_t*)(As + r * kArow + 16 * row_slot<kArow>(r, c));
   }
   if constexpr (T::PKed) {
-    // the stage holds the tile's 32-column blocks of one 64-k block side by side; the codes
-    // of 16-k step kk of block b are lane-ordered at b * PkBlock + kk * 64 * PkLane
+    // the stage holds the tile's 2048-byte units of one 64-k block side by side; the codes
+    // of 16-k step kk of unit u are lane-ordered, 8 bytes a lane, at u * 2048 + kk * 512
 #pragma unroll
-    for (int j = 0; j < T::Reads; ++j) {
-      const uint8_t* p = Bs + (wn * T::Reads + j) * T::PkBlock + kk * 64 * T::PkLane + T::PkLane * lane;
-      if constexpr (T::PkLane == 8) f.raw[j] = *(const u32x2_t*)p;
-      else f.raw[j] = u32x2_t{*(const uint32_t*)p, 0u};
-    }
+    for (int j = 0; j < T::Reads; ++j)
+      f.raw[j] = *(const u32x2_t*)(Bs + (wn * T::Reads + j) * 2048 + kk * 512 + 8 * lane);
     return;
   }
   if constexpr (T::XTile) {
@@ -484,7 +481,7 @@ __device__ __forceinline__ void aq_gemm_body(const AqArgs& a, uint8_t* smem, int
         u32x4_t bfr[WN];
 #pragma unroll
         for (int j = 0; j < T::Reads; ++j) {
-          if constexpr (W4 && (XT || PK)) bfr[j] = i4x8_k_to_act<BF16>(cur.raw[j][0]);
+          if constexpr (W4 && XT) bfr[j] = i4x8_k_to_act<BF16>(cur.raw[j][0]);
           else if constexpr (W4) i4_kpairs<BF16>(cur.raw[j], bfr[2 * j], bfr[2 * j + 1]);
           else bfr[j] = w8x8_to_act<BF16, WF>(cur.raw[j]);
         }

@@ -107,17 +107,20 @@ __global__ __launch_bounds__(256) void group_rowsums_kernel(const uint16_t* __re
   }
 }
 
-// One 64 k x 32 column block of the packed layout per workgroup (grid x: column block, y: k
-// block).  The block's codes are gathered into LDS as one byte each (int4: the nibble's
-// value), then written in fragment order: for 16-k step s and lane l, the codes of column
-// l % 32 at k 16 s + 8 (l / 32) + 0 .. 7.  Codes past k are zero.
+// One 2048-byte unit of the packed layout per workgroup (grid x: unit along n, y: k block):
+// a 64 k x 32 column block of one-byte codes, or two adjacent such blocks of int4 codes.  The
+// codes are gathered into LDS as one byte each (int4: the nibble's value), then written in
+// fragment order: for 16-k step s and lane l, the codes of column l % 32 at k
+// 16 s + 8 (l / 32) + 0 .. 7, one byte per k (int4: the unit's first block in bits 0-3, its
+// second in bits 4-7).  Codes past k are zero.
 template <bool W4, bool XT>
 __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict__ x2, uint8_t* __restrict__ packed,
                                                       int K, int N) {
-  __shared__ uint8_t tile[64][33];  // [k][column], padded
+  constexpr int kCols = W4 ? 64 : 32;   // columns of a unit
+  __shared__ uint8_t tile[64][kCols + 1];  // [k][column], padded
   const int t = threadIdx.x;
   const int nb = blockIdx.x, kb = blockIdx.y;
-  const int n0 = nb * 32, k0 = kb * 64;
+  const int n0 = nb * kCols, k0 = kb * 64;
   typedef uint8_t u8x16 __attribute__((ext_vector_type(16)));
   if constexpr (!W4 && !XT) {         // rows of k: 32 bytes of the block per row
     if (t < 128) {
@@ -135,19 +138,19 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int e = 0; e < 16; ++e) tile[16 * q + e][c] = v[e];
     }
-  } else if constexpr (!XT) {         // int4 rows of k: 16 bytes (32 columns) per row
-    if (t < 64) {
-      const int r = t;
+  } else if constexpr (!XT) {         // int4 rows of k: 32 bytes (64 columns) per row
+    if (t < 128) {
+      const int r = t >> 1, h = t & 1;
       u8x16 v = {};
-      if (k0 + r < K) v = *(const u8x16*)(x2 + (int64_t)(k0 + r) * (N / 2) + n0 / 2);
+      if (k0 + r < K) v = *(const u8x16*)(x2 + (int64_t)(k0 + r) * (N / 2) + n0 / 2 + 16 * h);
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
-        tile[r][2 * b] = v[b] & 15;
-        tile[r][2 * b + 1] = v[b] >> 4;
+        tile[r][32 * h + 2 * b] = v[b] & 15;
+        tile[r][32 * h + 2 * b + 1] = v[b] >> 4;
       }
     }
   } else {                            // int4 rows of columns: 32 bytes (64 k) per column
-    if (t < 64) {
+    if (t < 128) {
       const int c = t >> 1, h = t & 1;
       u8x16 v = {};
       if (k0 + 32 * h < K) v = *(const u8x16*)(x2 + (int64_t)(n0 + c) * (K / 2) + k0 / 2 + 16 * h);
@@ -161,27 +164,25 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
   __syncthreads();
   const int s = t >> 6, l = t & 63;           // 16-k step and lane of this thread's codes
   const int c = l & 31, kr = 16 * s + 8 * (l >> 5);
-  const int64_t block = (int64_t)kb * (N / 32) + nb;
-  if constexpr (!W4) {
-    uint32_t lo = 0, hi = 0;
+  const int64_t unit = (int64_t)kb * (N / kCols) + nb;
+  // the byte of k kr + e: the code of column c, and with int4 that of column c + 32 on top
+  auto code = [&](int e) -> uint32_t {
+    if constexpr (W4) return (uint32_t)(tile[kr + e][c] & 15) | ((uint32_t)(tile[kr + e][32 + c] & 15) << 4);
+    else return tile[kr + e][c];
+  };
+  uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lo |= (uint32_t)tile[kr + e][c] << (8 * e);
-      hi |= (uint32_t)tile[kr + 4 + e][c] << (8 * e);
-    }
-    *(u32x2_t*)(packed + block * 2048 + 8 * t) = u32x2_t{lo, hi};
-  } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w |= (uint32_t)(tile[kr + e][c] & 15) << (4 * e);
-    *(uint32_t*)(packed + block * 1024 + 4 * t) = w;
+  for (int e = 0; e < 4; ++e) {
+    lo |= code(e) << (8 * e);
+    hi |= code(4 + e) << (8 * e);
   }
+  *(u32x2_t*)(packed + unit * 2048 + 8 * t) = u32x2_t{lo, hi};
 }
 
 }  // namespace
 
 hipError_t launch_prepack(const PrepackProblem& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.n / 32), (unsigned)((p.k + 63) / 64));
+  const dim3 grid((unsigned)(p.n / (p.w4 ? 64 : 32)), (unsigned)((p.k + 63) / 64));
   auto kern = p.w4 ? (p.x2t ? prepack_kernel<true, true> : prepack_kernel<true, false>)
                    : (p.x2t ? prepack_kernel<false, true> : prepack_kernel<false, false>);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const uint8_t*)p.x2, (uint8_t*)p.packed, (int)p.k,

@@ -53,8 +53,9 @@ struct SmTile {
 
 // XT: the weights are stored transposed, (n, k) (int4: (n, k/2) bytes packed along k).
 // PK: the weights are in the packed layout (wq_prepack_weight): a block's four 32-column
-// pieces are adjacent 2 KiB (int4: 1 KiB) runs of B fragments in lane order, so the whole
-// block is one contiguous DMA and each fragment one contiguous LDS read.
+// pieces are adjacent 2 KiB runs of B fragments in lane order (int4: two 2 KiB runs, each
+// holding two pieces in the low and high nibbles), so the whole block is one contiguous DMA
+// and each fragment read one contiguous 8-byte LDS read.
 template <bool BF16, int WF, bool GROUPED, bool XT, bool PK = false>
 __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) {
   constexpr bool W4 = WF == kWInt4;
@@ -81,7 +82,6 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
   uint32_t w_off[T::WDma];
   int w_k[T::WDma];  // transposed weights: first k (within the block) of this lane's chunk
   constexpr int kPkBlock = W4 ? 1024 : 2048;     // packed: bytes of a 64 k x 32 column block
-  constexpr int kPkLane = W4 ? 4 : 8;            // packed: bytes of a lane's codes of a 16-k step
 #pragma unroll
   for (int j = 0; j < T::WDma; ++j) {
     if constexpr (PK) {
@@ -204,9 +204,9 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
     wave_wait<0>();
     const uint8_t* W = st;
     const uint8_t* X = st + T::Wbytes;
-    // B fragment reads per 16-k step: tr8 reads (an int4 one feeds two column blocks), or
-    // one 8-byte (int4: 4-byte) read per block from transposed weights
-    constexpr int kP = (W4 && !XT && !PK) ? 2 : 4;
+    // B fragment reads per 16-k step: int4 row-major (tr8) and packed reads feed two column
+    // blocks each; one-byte codes and transposed int4 (4-byte reads) one block each
+    constexpr int kP = (W4 && !XT) ? 2 : 4;
     u32x4_t af[kRows / 16];
     u32x2_t braw[kRows / 16][kP];
 #pragma unroll
@@ -215,11 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
       af[kk] = *(const u32x4_t*)(X + r * 128 + 16 * row_slot<128>(r, 2 * kk + (lane >> 5)));
       if constexpr (PK) {
 #pragma unroll
-        for (int p = 0; p < kP; ++p) {
-          const uint8_t* q = W + p * kPkBlock + kk * 64 * kPkLane + kPkLane * lane;
-          if constexpr (W4) braw[kk][p] = u32x2_t{*(const uint32_t*)q, 0u};
-          else braw[kk][p] = *(const u32x2_t*)q;
-        }
+        for (int p = 0; p < kP; ++p) braw[kk][p] = *(const u32x2_t*)(W + p * 2048 + kk * 512 + 8 * lane);
       } else if constexpr (XT) {
         constexpr int RowT = T::RowT;
         const int c = 2 * kk + (lane >> 5);  // 8-k piece within the column row
@@ -263,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void aq_smallm_kernel(const AqArgs a) 
       auto step = [&](bool zero) {
 #pragma unroll
         for (int p = 0; p < kP; ++p) {
-          if constexpr (W4 && (XT || PK)) {
+          if constexpr (W4 && XT) {
             acc[p] = mfma32x32x16<BF16>(af[kk], i4x8_k_to_act<BF16>(braw[kk][p][0]), zero ? f32x16_t{} : acc[p]);
           } else if constexpr (W4) {
             u32x4_t ev, od;
